@@ -1,0 +1,244 @@
+"""Benchmark of the BSA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config ns128] [--no-cpu-baseline]
+
+One step = one mosaic_bsa_forward call (pool -> compressed + top-n selection
+-> fused selected/local fine attention with the gated sum) over one batch of
+synthetic HEALPix-NESTED fields already resident in HBM.  The default
+workload is Nside = 128 (24 ensemble members x 8 heads x head_dim 64, block
+64, top-n 16, window 512); the Nside = 256 workload (2 x 16 heads, block 256,
+top-n 8, window 1024) is measured in the same run and reported under
+"secondary".  Prints one JSON line.
+
+Roofline of the dominant kernel (the fine-attention kernel, bf16 MFMA):
+algorithmic FLOPs per launch = sum over queries of 4*d*(n*block + |window(t)|)
+(edge windows clipped), divided by the kernel's mean duration measured with
+HIP events on the stream it runs on.  The oracle (float64 numpy) is timed on
+host cores on a bounded sample of (batch, head) slices of the same inputs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from spherical_block_sparse_amd import CONFIGS, BSAConfig, make_inputs  # noqa: E402
+from spherical_block_sparse_amd import _lib  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP64_TFLOPS = 78.6
+PEAK_HBM_GBS = 8000.0
+
+
+def window_keys_total(n_tok: int, window: int) -> int:
+    t = np.arange(n_tok, dtype=np.int64)
+    lo = np.maximum(t - window // 2, 0)
+    hi = np.minimum(t + (window + 1) // 2, n_tok)
+    return int((hi - lo).sum())
+
+
+def fine_flops(cfg: BSAConfig) -> float:
+    """Algorithmic FLOPs of one fine-kernel launch: QK^T and PV of both branches."""
+    d = cfg.head_dim
+    per_slice = 4 * d * (cfg.n_tokens * cfg.topn * cfg.block + window_keys_total(cfg.n_tokens, cfg.window))
+    return float(per_slice) * cfg.slices
+
+
+def compress_flops(cfg: BSAConfig) -> float:
+    m, d = cfg.n_blocks, cfg.head_dim
+    return 4.0 * m * m * d * cfg.slices          # logits (float64) + ā·v̄ (float32)
+
+
+def pool_bytes(cfg: BSAConfig) -> float:
+    e_in = cfg.slices * cfg.n_tokens * cfg.head_dim
+    e_out = cfg.slices * cfg.n_blocks * cfg.head_dim
+    return 3.0 * e_in * 2 + e_out * (8 + 8 + 4)
+
+
+def time_stream(fn, steps: int) -> float:
+    """Mean milliseconds of fn() over `steps` calls, HIP events on the current stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def measure(cfg: BSAConfig, steps: int, warmup: int) -> dict:
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v, g = make_inputs(cfg, device="cuda", dtype=torch.bfloat16)
+    b, h, n, d = cfg.batch, cfg.heads, cfg.n_tokens, cfg.head_dim
+    m = cfg.n_blocks
+    dev = q.device
+    out = torch.empty((b, h, n, d), dtype=torch.float32, device=dev)
+    sel = torch.empty((b, h, m, cfg.topn), dtype=torch.int32, device=dev)
+    ws = torch.empty(_lib.mosaic_bsa_workspace_bytes(b, h, d, cfg.nside, cfg.block, cfg.topn),
+                     dtype=torch.uint8, device=dev)
+    fwd = lambda: _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                          out=out, sel_idx=sel, workspace=ws)
+    print(f"[bench] {cfg.name}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    ms = time_stream(fwd, steps)
+
+    # per-kernel durations through the stage entry points (same kernels)
+    qbar = torch.empty((b, h, m, d), dtype=torch.float64, device=dev)
+    kbar = torch.empty_like(qbar)
+    vbar = torch.empty((b, h, m, d), dtype=torch.float32, device=dev)
+    o_cg = torch.empty_like(vbar)
+    sel2 = torch.empty_like(sel)
+    out2 = torch.empty_like(out)
+    pool = lambda: _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar)
+    cs = lambda: _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel2)
+    fine = lambda: _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel2, cfg.nside, cfg.block, cfg.topn, cfg.window, out2)
+    pool(); cs(); fine()
+    kt = max(3, steps // 2)
+    pool_ms = time_stream(pool, kt)
+    cs_ms = time_stream(cs, kt)
+    fine_ms = time_stream(fine, kt)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(sel, sel2) and torch.equal(out, out2))
+
+    ff = fine_flops(cfg)
+    res = dict(
+        cfg=cfg, ms=ms, tokens_per_s=cfg.tokens / (ms * 1e-3),
+        pool_ms=pool_ms, cs_ms=cs_ms, fine_ms=fine_ms, stages_match_forward=same,
+        fine_tflops=ff / (fine_ms * 1e-3) / 1e12, fine_flops=ff,
+        pool_gbs=pool_bytes(cfg) / (pool_ms * 1e-3) / 1e9, pool_bytes=pool_bytes(cfg),
+        cs_tflops=compress_flops(cfg) / (cs_ms * 1e-3) / 1e12,
+        inputs=(q, k, v, g, sel),
+    )
+    return res
+
+
+def cpu_baseline(cfg: BSAConfig, inputs, budget_s: float) -> dict:
+    """The float64 oracle as it stands, on whole (batch, head) slices of the
+    same inputs, until `budget_s` seconds of work are done (at least one)."""
+    import oracle
+    from spherical_block_sparse_amd.synth import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:   # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    q, k, v, g, _ = inputs
+    done, t_total = 0, 0.0
+    rng = np.random.default_rng(0)
+    order = rng.permutation(cfg.slices)
+    for s in order:
+        b, h = divmod(int(s), cfg.heads)
+        args = [to_f64(x[b, h]) for x in (q, k, v, g)]
+        t0 = time.perf_counter()
+        oracle.bsa_slice_ref(*args, cfg.block, cfg.topn, cfg.window)
+        t_total += time.perf_counter() - t0
+        done += 1
+        print(f"[bench] oracle slice ({b},{h}) done, {t_total:.1f} s", file=sys.stderr, flush=True)
+        if t_total >= budget_s:
+            break
+    # tokens/s in the metric's unit: one token = one pixel of one member across all heads
+    tok_s = done * cfg.n_tokens / cfg.heads / t_total
+    return {"value": tok_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.slices} (batch, head) slices of the {cfg.name} inputs, "
+                      f"{t_total:.1f} s, scaled by 1/heads to whole tokens",
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="ns128", choices=sorted(CONFIGS))
+    ap.add_argument("--secondary", default="ns256", help="second workload reported alongside ('' for none)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the BSA slices are independent and this build has no "
+              "multi-GPU path (batch/head slices would shard across GPUs with no communication). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    _lib.lib()
+
+    cfg = CONFIGS[args.config]
+    r = measure(cfg, args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, r["inputs"], args.cpu_budget)
+    del r["inputs"]
+    torch.cuda.empty_cache()
+
+    secondary = None
+    if args.secondary and args.secondary != args.config:
+        s = measure(CONFIGS[args.secondary], max(5, args.steps // 2), max(2, args.warmup // 2))
+        del s["inputs"]
+        secondary = {
+            "workload": s["cfg"].name, "value": s["tokens_per_s"], "unit": "tokens/s", "ms_per_step": s["ms"],
+            "kernels_ms": {"pool": s["pool_ms"], "compress_select": s["cs_ms"], "fine": s["fine_ms"]},
+            "fine_mfma_frac": s["fine_tflops"] / PEAK_BF16_TFLOPS,
+            "pool_hbm_frac": s["pool_gbs"] / PEAK_HBM_GBS,
+        }
+
+    c = r["cfg"]
+    line = {
+        "metric": "BSA fwd tokens/s at Nside=128 & 256; % bf16 MFMA peak, % HBM peak",
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{c.name}: HEALPix Nside={c.nside} NESTED, N={c.n_tokens}, batch {c.batch}, "
+                        f"{c.heads} heads x {c.head_dim}, block {c.block} ({c.n_blocks} blocks), "
+                        f"top-n {c.topn}, window {c.window}, {c.field} field",
+            "global_batch": c.batch, "seq_len": c.n_tokens, "heads": c.heads, "head_dim": c.head_dim,
+            "block": c.block, "topn": c.topn, "window": c.window, "tokens_per_step": c.tokens,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "bsa_fine (fine_kernel<64>)",
+            "achieved": r["fine_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": r["fine_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+            "flops_per_launch": r["fine_flops"], "ms_per_launch": r["fine_ms"],
+        },
+        "kernels": {
+            "pool": {"ms": r["pool_ms"], "bound": "hbm", "achieved_GBs": r["pool_gbs"],
+                     "frac": r["pool_gbs"] / PEAK_HBM_GBS, "bytes_per_launch": r["pool_bytes"]},
+            "compress_select": {"ms": r["cs_ms"], "bound": "fp64 matrix",
+                                "achieved_TFLOPs": r["cs_tflops"], "frac_fp64_peak": r["cs_tflops"] / PEAK_FP64_TFLOPS},
+            "fine": {"ms": r["fine_ms"], "frac_bf16_peak": r["fine_tflops"] / PEAK_BF16_TFLOPS},
+            "stages_match_forward": r["stages_match_forward"],
+        },
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,126 @@
+/*
+ * mosaic_bsa.h — C ABI of the MI355X (gfx950) forward pass of MOSAIC's
+ * mesh-aligned block-sparse attention (BSA) over HEALPix NESTED tokens.
+ *
+ * Operation (papernotes.org ICML2026 notes on "(Sparse) Attention to the
+ * Details", section 关键设计 › "Mesh-aligned Block-Sparse Attention (BSA)"):
+ * for every (batch, head) slice, the N = 12*nside^2 tokens in NESTED order
+ * are cut into m = N/block contiguous blocks (each one coarse HEALPix pixel,
+ * by the 4p..4p+3 children rule of the "HEALPix + NESTED" item);
+ *   q̄, k̄, v̄   = block means of q, k, v                       (pooling)
+ *   s_ij       = q̄_i·k̄_j / sqrt(d)
+ *   o_CG_i     = sum_j softmax_j(s_ij) v̄_j                     (compressed)
+ *   sel_i      = the topn j with largest s_ij, ties to lower j  (selection,
+ *                shared by every query of block i)
+ *   o_FG_t     = softmax attention of q_t over all tokens of the blocks sel_i
+ *   o_L_t      = softmax attention of q_t over keys [t-floor(W/2), t+ceil(W/2))
+ *                clipped to [0, N)                              (local)
+ *   out_t      = g_t0·o_CG_{t/block} + g_t1·o_FG_t + g_t2·o_L_t
+ * Scale 1/sqrt(d) everywhere, no causal mask, every slice independent.
+ *
+ * Conventions for every entry point
+ *   - Buffers are device pointers owned by the caller; the library allocates
+ *     nothing and keeps no state.  Inputs are never written.
+ *   - Layouts are dense row-major: q, k, v, out [batch][heads][N][head_dim];
+ *     gates [batch][heads][N][3] = (g_CG, g_FG, g_L); sel_idx
+ *     [batch][heads][m][topn]; pooled / per-block tensors [batch][heads][m][head_dim].
+ *   - q, k, v are bfloat16 bit patterns (uint16, round-to-nearest-even
+ *     conversion done by the caller); gates, out and pooled v̄ / o_CG are
+ *     float32; pooled q̄, k̄ are float64 (exact block means of bf16 data).
+ *   - stream is a hipStream_t (NULL = the legacy default stream).  Every call
+ *     only enqueues work and returns; faults inside a kernel surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated before any HIP call.  On error nothing is
+ *     launched, outputs are untouched, and the status is returned; the text
+ *     of the last error of the calling thread is mosaic_last_error().
+ *   - Supported: nside a power of two with N < 2^31; block = 4^k with
+ *     16 <= block <= nside^2 (so a block never straddles two base pixels);
+ *     1 <= topn <= min(m, 64); window >= 1; head_dim in {32, 64};
+ *     batch, heads >= 1.  Blocks of 1 or 4 tokens and topn > 64 return
+ *     MOSAIC_ERR_UNSUPPORTED.
+ *   - Alignment: q, k, v, out, o_cg, pooled buffers and sel_idx rows of 16
+ *     bytes; gates 4 bytes; workspace 256 bytes.
+ */
+#ifndef MOSAIC_BSA_H
+#define MOSAIC_BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOSAIC_BSA_ABI_VERSION 1
+
+typedef enum mosaic_status {
+  MOSAIC_OK = 0,
+  MOSAIC_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  MOSAIC_ERR_BAD_SHAPE = 2,    /* sizes violate the definition (nside, block, topn, window) */
+  MOSAIC_ERR_UNSUPPORTED = 3,  /* valid BSA, but outside what the kernels implement */
+  MOSAIC_ERR_MISALIGNED = 4,   /* a pointer is not aligned as required */
+  MOSAIC_ERR_WORKSPACE = 5,    /* workspace smaller than mosaic_bsa_workspace_bytes() */
+  MOSAIC_ERR_HIP = 6           /* the HIP runtime refused a launch (no device, bad stream, ...) */
+} mosaic_status;
+
+/* Returns MOSAIC_BSA_ABI_VERSION of the built library. */
+int mosaic_bsa_abi_version(void);
+
+/* Static name of a status code ("MOSAIC_OK", ...). */
+const char* mosaic_status_string(int status);
+
+/* Text of the last failed call on the calling thread ("" if none). */
+const char* mosaic_last_error(void);
+
+/* Bytes of device workspace mosaic_bsa_forward needs: pooled q̄, k̄ (float64),
+ * pooled v̄ and o_CG (float32), each [batch][heads][m][head_dim], 256-byte
+ * aligned sections.  Returns 0 if the shape is invalid or unsupported. */
+size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn);
+
+/* The whole BSA forward pass (pool -> compressed + selection -> selected and
+ * local fine attention with the gated sum), three kernels on `stream`.
+ *   q, k, v   in : bf16 bits [batch][heads][N][head_dim]
+ *   gates     in : float32 [batch][heads][N][3]
+ *   out       out: float32 [batch][heads][N][head_dim]
+ *   sel_idx   out: int32 [batch][heads][m][topn], block indices in ascending order
+ *   workspace in/out scratch of at least mosaic_bsa_workspace_bytes(...) bytes
+ * (papernotes.org ICML2026 notes, 关键设计 › Mesh-aligned Block-Sparse Attention) */
+mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, const float* gates,
+                                 int batch, int heads, int head_dim, int nside, int block, int topn,
+                                 int window, float* out, int32_t* sel_idx, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Pooling only: q̄, k̄ (float64) and v̄ (float32), [batch][heads][m][head_dim],
+ * the mean of each block's `block` consecutive NESTED tokens (the block
+ * summaries of the BSA item; the mean is this library's reading of the
+ * unspecified pooling). */
+mosaic_status mosaic_bsa_pool(const void* q, const void* k, const void* v, int batch, int heads,
+                              int head_dim, int nside, int block, double* qbar, double* kbar,
+                              float* vbar, void* stream);
+
+/* Compressed branch and top-n selection from pooled tensors: o_cg
+ * [batch][heads][m][head_dim] float32 = sum_j softmax_j(q̄_i·k̄_j/sqrt(d)) v̄_j,
+ * and sel_idx [batch][heads][m][topn] = the topn largest logits of each row,
+ * ties to the lower block index, listed in ascending order.  Logits are
+ * formed in float64, so the selection matches a float64 evaluation except on
+ * rows whose n-th and (n+1)-th logits differ by a few float64 ulps. */
+mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar, const float* vbar,
+                                         int batch, int heads, int head_dim, int nside, int block,
+                                         int topn, float* o_cg, int32_t* sel_idx, void* stream);
+
+/* Selected-block and sliding-window fine attention plus the gated sum, from
+ * q, k, v (bf16), gates, o_cg (per block, float32) and sel_idx (any topn
+ * valid block indices per row, each in [0, m); order is irrelevant):
+ * out = g_CG·o_cg[t/block] + g_FG·o_FG + g_L·o_L.  bf16 products with
+ * float32 accumulation; attention weights are rounded to bf16 before they
+ * multiply v. */
+mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const float* gates,
+                              const float* o_cg, const int32_t* sel_idx, int batch, int heads,
+                              int head_dim, int nside, int block, int topn, int window, float* out,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOSAIC_BSA_H */

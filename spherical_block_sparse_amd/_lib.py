@@ -1,0 +1,177 @@
+"""ctypes binding of libmosaic_bsa (include/mosaic_bsa.h): argument marshalling only.
+
+Every step of the BSA forward pass runs in the library's HIP kernels; this
+module checks that the torch tensors have the layout the C ABI documents,
+passes their device pointers and torch's current HIP stream, and turns a
+non-OK status into MosaicError.  There is no fallback: without the built
+library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmosaic_bsa.so")
+
+MOSAIC_OK = 0
+STATUS_NAMES = {
+    0: "MOSAIC_OK", 1: "MOSAIC_ERR_NULL_POINTER", 2: "MOSAIC_ERR_BAD_SHAPE",
+    3: "MOSAIC_ERR_UNSUPPORTED", 4: "MOSAIC_ERR_MISALIGNED", 5: "MOSAIC_ERR_WORKSPACE",
+    6: "MOSAIC_ERR_HIP",
+}
+
+EXPORTED = (
+    "mosaic_bsa_abi_version", "mosaic_status_string", "mosaic_last_error",
+    "mosaic_bsa_workspace_bytes", "mosaic_bsa_forward", "mosaic_bsa_pool",
+    "mosaic_bsa_compress_select", "mosaic_bsa_fine",
+)
+
+
+class MosaicError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmosaic_bsa.so from the package directory (no search path, no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m spherical_block_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.mosaic_bsa_abi_version.restype = I
+        L.mosaic_bsa_abi_version.argtypes = []
+        L.mosaic_status_string.restype = ctypes.c_char_p
+        L.mosaic_status_string.argtypes = [I]
+        L.mosaic_last_error.restype = ctypes.c_char_p
+        L.mosaic_last_error.argtypes = []
+        L.mosaic_bsa_workspace_bytes.restype = S
+        L.mosaic_bsa_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.mosaic_bsa_forward.restype = I
+        L.mosaic_bsa_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, P, S, P]
+        L.mosaic_bsa_pool.restype = I
+        L.mosaic_bsa_pool.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P]
+        L.mosaic_bsa_compress_select.restype = I
+        L.mosaic_bsa_compress_select.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
+        L.mosaic_bsa_fine.restype = I
+        L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != MOSAIC_OK:
+        raise MosaicError(status, lib().mosaic_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def _ptr(t: torch.Tensor, dtype: torch.dtype, shape: tuple, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _dims(q: torch.Tensor, nside: int):
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, N, head_dim]")
+    b, h, n, d = q.shape
+    if n != 12 * nside * nside:
+        raise ValueError(f"N = {n} but 12*nside^2 = {12 * nside * nside}")
+    return b, h, n, d
+
+
+def mosaic_bsa_abi_version() -> int:
+    return lib().mosaic_bsa_abi_version()
+
+
+def mosaic_bsa_workspace_bytes(batch, heads, head_dim, nside, block, topn) -> int:
+    return lib().mosaic_bsa_workspace_bytes(batch, heads, head_dim, nside, block, topn)
+
+
+def mosaic_bsa_forward(q, k, v, gates, nside, block, topn, window, out=None, sel_idx=None,
+                       workspace=None, stream=None):
+    """out [b,H,N,d] fp32 and sel_idx [b,H,m,topn] int32 from bf16 q, k, v and fp32 gates."""
+    b, h, n, d = _dims(q, nside)
+    m = n // block
+    if out is None:
+        out = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((b, h, m, topn), dtype=torch.int32, device=q.device)
+    need = mosaic_bsa_workspace_bytes(b, h, d, nside, block, topn)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or workspace.device.type != "cuda":
+        raise ValueError("workspace must be a 1-D uint8 device tensor")
+    _check(lib().mosaic_bsa_forward(
+        _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
+        _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
+        b, h, d, nside, block, topn, window,
+        _ptr(out, torch.float32, (b, h, n, d), "out"),
+        _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, sel_idx
+
+
+def mosaic_bsa_pool(q, k, v, nside, block, qbar=None, kbar=None, vbar=None, stream=None):
+    """q̄, k̄ (float64) and v̄ (float32), [b,H,m,d]: block means."""
+    b, h, n, d = _dims(q, nside)
+    m = n // block
+    qbar = torch.empty((b, h, m, d), dtype=torch.float64, device=q.device) if qbar is None else qbar
+    kbar = torch.empty((b, h, m, d), dtype=torch.float64, device=q.device) if kbar is None else kbar
+    vbar = torch.empty((b, h, m, d), dtype=torch.float32, device=q.device) if vbar is None else vbar
+    _check(lib().mosaic_bsa_pool(
+        _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
+        _ptr(v, torch.bfloat16, (b, h, n, d), "v"), b, h, d, nside, block,
+        _ptr(qbar, torch.float64, (b, h, m, d), "qbar"), _ptr(kbar, torch.float64, (b, h, m, d), "kbar"),
+        _ptr(vbar, torch.float32, (b, h, m, d), "vbar"), _stream(stream)))
+    return qbar, kbar, vbar
+
+
+def mosaic_bsa_compress_select(qbar, kbar, vbar, nside, block, topn, o_cg=None, sel_idx=None, stream=None):
+    """o_cg [b,H,m,d] fp32 and sel_idx [b,H,m,topn] int32 from the pooled tensors."""
+    b, h, m, d = qbar.shape
+    if m * block != 12 * nside * nside:
+        raise ValueError("m * block must equal 12*nside^2")
+    o_cg = torch.empty((b, h, m, d), dtype=torch.float32, device=qbar.device) if o_cg is None else o_cg
+    sel_idx = torch.empty((b, h, m, topn), dtype=torch.int32, device=qbar.device) if sel_idx is None else sel_idx
+    _check(lib().mosaic_bsa_compress_select(
+        _ptr(qbar, torch.float64, (b, h, m, d), "qbar"), _ptr(kbar, torch.float64, (b, h, m, d), "kbar"),
+        _ptr(vbar, torch.float32, (b, h, m, d), "vbar"), b, h, d, nside, block, topn,
+        _ptr(o_cg, torch.float32, (b, h, m, d), "o_cg"),
+        _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"), _stream(stream)))
+    return o_cg, sel_idx
+
+
+def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, out=None, stream=None):
+    """out [b,H,N,d] fp32: gated sum of o_cg with the selected and local fine branches."""
+    b, h, n, d = _dims(q, nside)
+    m = n // block
+    out = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device) if out is None else out
+    _check(lib().mosaic_bsa_fine(
+        _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
+        _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
+        _ptr(o_cg, torch.float32, (b, h, m, d), "o_cg"), _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"),
+        b, h, d, nside, block, topn, window, _ptr(out, torch.float32, (b, h, n, d), "out"), _stream(stream)))
+    return out

@@ -1,0 +1,106 @@
+// Block pooling: mean of every `block` consecutive NESTED tokens of q, k, v.
+//
+// Source: papernotes.org ICML2026 notes, 关键设计 › Mesh-aligned Block-Sparse
+// Attention (block summaries q̄, k̄, v̄ by a pooling phi; the mean is the
+// reading taken here) and › HEALPix + NESTED (a block is a contiguous index
+// range, so it is read in one coalesced sweep).
+//
+// Layout: x [slices][N][D] bf16 -> xbar [slices][m][D]; q̄, k̄ in float64, v̄
+// in float32.  A block is block*D*2 contiguous bytes.
+//
+// Mapping: D/8 lanes cover one token row (16 bytes = 8 bf16 each), so a
+// 256-thread workgroup streams 256/(D/8) blocks side by side, every lane
+// walking its 16-byte column slice down all rows of its block.  Each wave
+// instruction touches 64/(D/8) full 128-byte (D=64) row segments; no
+// cross-lane reduction is needed.  Sums are float64: exact for bf16 inputs
+// (8-bit significands, at most a few thousand terms), and block = 4^k makes
+// the final scaling exact.  HBM-bound: 6*D bytes read per token.
+#include "bsa_common.h"
+
+namespace mosaic {
+namespace {
+
+struct PoolArgs {
+  const uint16_t* src[3];
+  double* dst64[2];   // q̄, k̄
+  float* dst32;       // v̄
+  long long total_blocks;   // slices * m
+  long long wgs_per_tensor;
+  int block;
+  double inv_block;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
+  constexpr int TPR = D / 8;              // lanes per token row
+  constexpr int BPW = 256 / TPR;          // blocks per workgroup
+  const int tensor = (int)(blockIdx.x / a.wgs_per_tensor);
+  const long long wg = blockIdx.x - (long long)tensor * a.wgs_per_tensor;
+  const int lb = threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  const long long gb = wg * BPW + lb;
+  if (gb >= a.total_blocks) return;
+
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* p = reinterpret_cast<const u32x4*>(a.src[tensor] + (size_t)gb * a.block * D) + c;
+  double acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+
+  const int rows = a.block;
+  for (int r0 = 0; r0 < rows; r0 += 8) {
+    u32x4 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = __builtin_nontemporal_load(p + (size_t)(r0 + u) * TPR);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t x[4] = {w[u][0], w[u][1], w[u][2], w[u][3]};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc[2 * h] += (double)__uint_as_float(x[h] << 16);
+        acc[2 * h + 1] += (double)__uint_as_float(x[h] & 0xffff0000u);
+      }
+    }
+  }
+
+  const size_t o = (size_t)gb * D + c * 8;
+  if (tensor < 2) {
+    double* dst = a.dst64[tensor] + o;
+    double2* d2 = reinterpret_cast<double2*>(dst);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d2[j] = make_double2(acc[2 * j] * a.inv_block, acc[2 * j + 1] * a.inv_block);
+  } else {
+    float4* d4 = reinterpret_cast<float4*>(a.dst32 + o);
+    d4[0] = make_float4((float)(acc[0] * a.inv_block), (float)(acc[1] * a.inv_block),
+                        (float)(acc[2] * a.inv_block), (float)(acc[3] * a.inv_block));
+    d4[1] = make_float4((float)(acc[4] * a.inv_block), (float)(acc[5] * a.inv_block),
+                        (float)(acc[6] * a.inv_block), (float)(acc[7] * a.inv_block));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* qbar,
+                       double* kbar, float* vbar, long long slices, int n_tok, int head_dim,
+                       int block, hipStream_t stream) {
+  PoolArgs a;
+  a.src[0] = q;
+  a.src[1] = k;
+  a.src[2] = v;
+  a.dst64[0] = qbar;
+  a.dst64[1] = kbar;
+  a.dst32 = vbar;
+  a.total_blocks = slices * (long long)(n_tok / block);
+  a.block = block;
+  a.inv_block = 1.0 / (double)block;
+  const int bpw = 256 / (head_dim / 8);
+  a.wgs_per_tensor = (a.total_blocks + bpw - 1) / bpw;
+  dim3 grid((unsigned)(3 * a.wgs_per_tensor));
+  if (head_dim == 64)
+    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(pool_kernel<32>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mosaic

@@ -1,0 +1,217 @@
+// C-ABI entry points of libmosaic_bsa (declared in include/mosaic_bsa.h).
+//
+// Every entry point validates all arguments before the first HIP call, so an
+// invalid call launches nothing and leaves the outputs untouched; errors are
+// returned as mosaic_status with a thread-local message.
+#include "../../include/mosaic_bsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "bsa_common.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+mosaic_status fail(mosaic_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mosaic_status ok() {
+  g_last_error[0] = '\0';
+  return MOSAIC_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Shape {
+  long long slices;
+  int n_tok;
+  int m;
+  int d;
+  int block;
+  int topn;
+  int window;   // clipped to 2N (a wider window sees the same keys)
+};
+
+enum : unsigned { kUsesTopn = 1, kUsesWindow = 2 };
+
+// Checks the sizes shared by every entry point; `uses` says whether this
+// entry point takes topn and window.
+mosaic_status check_shape(int batch, int heads, int head_dim, int nside, int block, int topn,
+                          int window, unsigned uses, Shape* s) {
+  if (batch < 1 || heads < 1) return fail(MOSAIC_ERR_BAD_SHAPE, "batch (%d) and heads (%d) must be >= 1", batch, heads);
+  if (nside < 1 || (nside & (nside - 1)))
+    return fail(MOSAIC_ERR_BAD_SHAPE, "nside (%d) must be a power of two >= 1", nside);
+  if (nside > 8192) return fail(MOSAIC_ERR_UNSUPPORTED, "nside %d: N = 12*nside^2 must fit in int32", nside);
+  const long long n_tok = 12LL * nside * nside;
+  if (block < 1 || (block & (block - 1)) || (__builtin_ctz((unsigned)block) & 1))
+    return fail(MOSAIC_ERR_BAD_SHAPE, "block (%d) must be a power of four", block);
+  if ((long long)block > (long long)nside * nside)
+    return fail(MOSAIC_ERR_BAD_SHAPE, "block (%d) must be <= nside^2 (%lld) so it is one coarse pixel", block,
+                (long long)nside * nside);
+  if (block < 16) return fail(MOSAIC_ERR_UNSUPPORTED, "block %d: the kernels need block >= 16", block);
+  const long long m = n_tok / block;
+  if (uses & kUsesTopn) {
+    if (topn < 1 || topn > m) return fail(MOSAIC_ERR_BAD_SHAPE, "topn (%d) must lie in [1, m=%lld]", topn, m);
+    if (topn > 64) return fail(MOSAIC_ERR_UNSUPPORTED, "topn %d: the selection keeps at most 64 blocks", topn);
+  }
+  if ((uses & kUsesWindow) && window < 1) return fail(MOSAIC_ERR_BAD_SHAPE, "window (%d) must be >= 1", window);
+  if (head_dim != 32 && head_dim != 64)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "head_dim %d: supported head_dim is 32 or 64", head_dim);
+  const long long slices = (long long)batch * heads;
+  // one-dimensional grids: the largest is the pooling grid, 3 * slices*m/(256/(d/8)) groups of 256 lanes
+  if (slices * (n_tok / 64) > 0x7fffffffLL || slices * m * 3 * 8 > 0x7fffffffLL)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "batch*heads*N too large for one launch");
+  s->slices = slices;
+  s->n_tok = (int)n_tok;
+  s->m = (int)m;
+  s->d = head_dim;
+  s->block = block;
+  s->topn = (uses & kUsesTopn) ? topn : 0;
+  s->window = (uses & kUsesWindow) ? (int)((long long)window > 2 * n_tok ? 2 * n_tok : window) : 0;
+  return MOSAIC_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+  size_t qbar, kbar, vbar, ocg, total;
+};
+
+Workspace layout(const Shape& s) {
+  const size_t e = (size_t)s.slices * s.m * s.d;
+  Workspace w;
+  w.qbar = 0;
+  w.kbar = w.qbar + align256(e * sizeof(double));
+  w.vbar = w.kbar + align256(e * sizeof(double));
+  w.ocg = w.vbar + align256(e * sizeof(float));
+  w.total = w.ocg + align256(e * sizeof(float));
+  return w;
+}
+
+mosaic_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOSAIC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define REQUIRE_PTR(p) \
+  if (!(p)) return fail(MOSAIC_ERR_NULL_POINTER, "%s is NULL", #p)
+#define REQUIRE_ALIGN(p, a) \
+  if (!aligned((p), (a))) return fail(MOSAIC_ERR_MISALIGNED, "%s is not %d-byte aligned", #p, (int)(a))
+
+}  // namespace
+
+extern "C" {
+
+int mosaic_bsa_abi_version(void) { return MOSAIC_BSA_ABI_VERSION; }
+
+const char* mosaic_status_string(int status) {
+  switch (status) {
+    case MOSAIC_OK: return "MOSAIC_OK";
+    case MOSAIC_ERR_NULL_POINTER: return "MOSAIC_ERR_NULL_POINTER";
+    case MOSAIC_ERR_BAD_SHAPE: return "MOSAIC_ERR_BAD_SHAPE";
+    case MOSAIC_ERR_UNSUPPORTED: return "MOSAIC_ERR_UNSUPPORTED";
+    case MOSAIC_ERR_MISALIGNED: return "MOSAIC_ERR_MISALIGNED";
+    case MOSAIC_ERR_WORKSPACE: return "MOSAIC_ERR_WORKSPACE";
+    case MOSAIC_ERR_HIP: return "MOSAIC_ERR_HIP";
+    default: return "MOSAIC_ERR_UNKNOWN";
+  }
+}
+
+const char* mosaic_last_error(void) { return g_last_error; }
+
+size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn) {
+  Shape s;
+  if (check_shape(batch, heads, head_dim, nside, block, topn, 0, kUsesTopn, &s) != MOSAIC_OK) return 0;
+  return layout(s).total;
+}
+
+mosaic_status mosaic_bsa_pool(const void* q, const void* k, const void* v, int batch, int heads,
+                              int head_dim, int nside, int block, double* qbar, double* kbar,
+                              float* vbar, void* stream) {
+  REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v);
+  REQUIRE_PTR(qbar); REQUIRE_PTR(kbar); REQUIRE_PTR(vbar);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16);
+  REQUIRE_ALIGN(qbar, 16); REQUIRE_ALIGN(kbar, 16); REQUIRE_ALIGN(vbar, 16);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, 0, 0, 0, &s);
+  if (st != MOSAIC_OK) return st;
+  return hip_status(mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                        static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices,
+                                        s.n_tok, s.d, s.block, static_cast<hipStream_t>(stream)),
+                    "bsa_pool launch");
+}
+
+mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar, const float* vbar,
+                                         int batch, int heads, int head_dim, int nside, int block,
+                                         int topn, float* o_cg, int32_t* sel_idx, void* stream) {
+  REQUIRE_PTR(qbar); REQUIRE_PTR(kbar); REQUIRE_PTR(vbar); REQUIRE_PTR(o_cg); REQUIRE_PTR(sel_idx);
+  REQUIRE_ALIGN(qbar, 16); REQUIRE_ALIGN(kbar, 16); REQUIRE_ALIGN(vbar, 16); REQUIRE_ALIGN(o_cg, 16);
+  REQUIRE_ALIGN(sel_idx, 4);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, 0, kUsesTopn, &s);
+  if (st != MOSAIC_OK) return st;
+  return hip_status(mosaic::launch_compress_select(qbar, kbar, vbar, o_cg, sel_idx, s.slices, s.m, s.d,
+                                                   s.topn, static_cast<hipStream_t>(stream)),
+                    "bsa_compress_select launch");
+}
+
+mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const float* gates,
+                              const float* o_cg, const int32_t* sel_idx, int batch, int heads,
+                              int head_dim, int nside, int block, int topn, int window, float* out,
+                              void* stream) {
+  REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(o_cg);
+  REQUIRE_PTR(sel_idx); REQUIRE_PTR(out);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
+  REQUIRE_ALIGN(o_cg, 16); REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(out, 16);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
+  if (st != MOSAIC_OK) return st;
+  return hip_status(mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                        static_cast<const uint16_t*>(v), gates, o_cg, sel_idx, out,
+                                        s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
+                                        static_cast<hipStream_t>(stream)),
+                    "bsa_fine launch");
+}
+
+mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, const float* gates,
+                                 int batch, int heads, int head_dim, int nside, int block, int topn,
+                                 int window, float* out, int32_t* sel_idx, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(out);
+  REQUIRE_PTR(sel_idx); REQUIRE_PTR(workspace);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
+  REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(workspace, 256);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
+  if (st != MOSAIC_OK) return st;
+  const Workspace w = layout(s);
+  if (workspace_bytes < w.total)
+    return fail(MOSAIC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+  char* ws = static_cast<char*>(workspace);
+  double* qbar = reinterpret_cast<double*>(ws + w.qbar);
+  double* kbar = reinterpret_cast<double*>(ws + w.kbar);
+  float* vbar = reinterpret_cast<float*>(ws + w.vbar);
+  float* ocg = reinterpret_cast<float*>(ws + w.ocg);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
+                                     s.d, s.block, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
+                          s.block, s.topn, s.window, hs);
+  return hip_status(e, "bsa_fine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI (include/mosaic_bsa.h): no GPU needed.
+
+Only argument sets that the library rejects during validation are passed, so
+no call here reaches the HIP runtime (validation completes before any HIP
+call; the fake pointers below are never dereferenced).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from spherical_block_sparse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mosaic_bsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmosaic_bsa.so not built")
+
+FAKE = 0x10000          # 256-byte aligned, never dereferenced
+OK, NULL, SHAPE, UNSUP, MISAL, WS, HIP = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(mosaic_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_and_library_exports_the_same_symbols():
+    declared = declared_functions()
+    assert set(declared) == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (mosaic_[a-z_]+)\b", out))
+    assert set(declared) <= exported, set(declared) - exported
+    L = _lib.lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings():
+    L = _lib.lib()
+    assert L.mosaic_bsa_abi_version() == 1
+    for code, name in _lib.STATUS_NAMES.items():
+        assert L.mosaic_status_string(code).decode() == name
+    assert L.mosaic_status_string(99).decode() == "MOSAIC_ERR_UNKNOWN"
+
+
+def test_workspace_bytes_layout():
+    L = _lib.lib()
+    # ns128: S = 192, m = 3072, d = 64 -> two float64 and two float32 [S][m][d] sections
+    e = 192 * 3072 * 64
+    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) == e * (8 + 8 + 4 + 4)
+    # tiny: S = 2, m = 48, d = 32 -> sections rounded up to 256 bytes
+    e = 2 * 48 * 32
+    r = lambda x: (x + 255) // 256 * 256
+    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 4) == 2 * r(8 * e) + 2 * r(4 * e)
+    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 0) == 0      # invalid -> 0
+    assert L.mosaic_bsa_workspace_bytes(1, 2, 48, 8, 16, 4) == 0      # unsupported -> 0
+
+
+def fwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=32, nside=8, block=16, topn=4,
+        window=32, out=FAKE, sel=FAKE, ws=FAKE, ws_bytes=None):
+    L = _lib.lib()
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return L.mosaic_bsa_forward(q, k, v, gates, batch, heads, d, nside, block, topn, window, out, sel,
+                                ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(gates=None), NULL),
+    (dict(out=None), NULL), (dict(sel=None), NULL), (dict(ws=None), NULL),
+    (dict(q=FAKE + 8), MISAL), (dict(out=FAKE + 4), MISAL), (dict(ws=FAKE + 16), MISAL),
+    (dict(gates=FAKE + 2), MISAL),
+    (dict(batch=0), SHAPE), (dict(heads=-1), SHAPE),
+    (dict(nside=3), SHAPE), (dict(nside=0), SHAPE),
+    (dict(block=8), SHAPE), (dict(block=32), SHAPE), (dict(block=256), SHAPE),   # 256 > nside^2 = 64
+    (dict(topn=0), SHAPE), (dict(topn=49), SHAPE), (dict(window=0), SHAPE),
+    (dict(block=4), UNSUP), (dict(block=1), UNSUP), (dict(d=48), UNSUP), (dict(d=128), UNSUP),
+    (dict(nside=16, block=16, topn=65), UNSUP), (dict(nside=16384), UNSUP),
+    (dict(ws_bytes=100), WS),
+])
+def test_forward_validation(kw, code):
+    assert fwd(**kw) == code
+    assert _lib.lib().mosaic_last_error().decode() != ""
+
+
+def test_stage_entry_points_validate():
+    L = _lib.lib()
+    assert L.mosaic_bsa_pool(FAKE, FAKE, None, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None) == NULL
+    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 12, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, FAKE + 8, FAKE, FAKE, None) == MISAL
+    assert L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 0, FAKE, FAKE, None) == SHAPE
+    assert L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 4, None, FAKE, None) == NULL
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 4, 0, FAKE, None) == SHAPE
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 32, 8, 16, 4, 32, FAKE, None) == NULL
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 4, 4, 32, FAKE, None) == UNSUP
+
+
+def test_python_binding_rejects_bad_tensors_without_launch():
+    import torch
+    q = torch.zeros(1, 2, 768, 32, dtype=torch.float32)
+    with pytest.raises((TypeError, ValueError)):
+        _lib.mosaic_bsa_forward(q, q, q, torch.zeros(1, 2, 768, 3), 8, 16, 4, 32,
+                                out=torch.zeros(1), sel_idx=torch.zeros(1), workspace=torch.zeros(1, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        _lib.mosaic_bsa_forward(q[:, :, :700], q, q, q, 8, 16, 4, 32)
