@@ -9,16 +9,20 @@
 //
 // Design (gfx950):
 //   * one workgroup = 64 query-block rows of one slice, 4 waves x 16 rows;
-//     the key blocks stream through LDS 64 at a time (k̄ in float64, v̄ in
-//     float32).
-//   * logits: v_mfma_f64_16x16x4_f64 on the exact float64 block means, so
-//     the ranking equals a float64 evaluation up to summation order (a few
-//     ulps), far below any gap that decides a selection.
-//   * softmax numerator/denominator: online (running max), p = 2^((s-max)
-//     log2 e) in float32; o_CG += P·V̄ with v_mfma_f32_16x16x4_f32.
-//   * top-n: per row a sorted list held one entry per lane (n <= 64);
-//     each 64-key chunk is filtered against the current n-th entry with one
-//     ballot, and only the survivors are inserted (shift by one lane).
+//     key blocks stream through LDS 64 at a time (k̄ float64, v̄ float32).
+//   * logits transposed, S^T = K̄ Q̄^T, with v_mfma_f64_16x16x4_f64 on the
+//     exact float64 block means: in that layout lane l owns 16 logits of row
+//     l%16, which is also the B operand layout of O^T += V̄^T P^T
+//     (v_mfma_f32_16x16x4_f32), so the online softmax (running max, exp2 in
+//     float32) needs no LDS round trip and only two cross-lane steps.
+//   * ranking uses the float64 dot products themselves (dividing by sqrt(d)
+//     is monotone), so the selection equals a float64 evaluation up to the
+//     summation order of 64 products.
+//   * top-n: each row keeps its current n-th best (value, index) key; the
+//     logits that beat it are appended to the row's LDS buffer with an LDS
+//     atomic, and when a buffer passes 64 entries one wave compacts it to its
+//     best n with a 128-element bitonic network (DPP / swizzle exchanges),
+//     which raises the key.  A final compaction orders the n survivors.
 // Roofline: float64 matrix work 2*m^2*d per slice for the logits plus
 // float32 matrix work 2*m^2*d for ā·v̄; HBM traffic is only the pooled
 // tensors, o_CG and the indices.
@@ -38,37 +42,97 @@ struct CSArgs {
   int m;
   int topn;
   int row_tiles;
-  double sqrt_d;
+  double c_exp2;   // log2(e) / sqrt(d): exp(s) = 2^(dot * c_exp2)
 };
 
-constexpr double kLog2e = 1.4426950408889634;
+constexpr int kCap = 128;   // candidate buffer per row
 
+// (value, index) order of the selection: larger value first, then lower index
 __device__ __forceinline__ bool beats(double av, int ai, double bv, int bi) {
   return av > bv || (av == bv && ai < bi);
+}
+
+// x from lane (lane ^ J)
+template <int J>
+__device__ __forceinline__ int xor_lane(int x) {
+  if constexpr (J == 1) return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  else if constexpr (J == 2) return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  else if constexpr (J <= 16) return __builtin_amdgcn_ds_swizzle(x, (J << 10) | 0x1F);   // bit mode, xor J
+  else return __builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ J) << 2, x);
+}
+
+// compare-exchange of position p with p ^ J inside a bitonic block of size K
+template <int J, int K>
+__device__ __forceinline__ void bitonic_step(double& v, int& i, int p) {
+  const long long b = __double_as_longlong(v);
+  const int plo = xor_lane<J>((int)(b & 0xffffffffLL));
+  const int phi = xor_lane<J>((int)(b >> 32));
+  const int pi = xor_lane<J>(i);
+  const double pv = __longlong_as_double(((long long)phi << 32) | (unsigned)plo);
+  const bool lower = (p & J) == 0;
+  const bool desc = (p & K) == 0;
+  const bool mine = beats(v, i, pv, pi);
+  if (!((lower == desc) ? mine : !mine)) {
+    v = pv;
+    i = pi;
+  }
+}
+
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge(double& v0, int& i0, double& v1, int& i1, int lane) {
+  if constexpr (J == 64) {   // positions lane and lane+64 sit in the same lane
+    if (!beats(v0, i0, v1, i1)) {
+      const double tv = v0; const int ti = i0;
+      v0 = v1; i0 = i1; v1 = tv; i1 = ti;
+    }
+  } else {
+    bitonic_step<J, K>(v0, i0, lane);
+    bitonic_step<J, K>(v1, i1, lane + 64);
+  }
+  if constexpr (J > 1) bitonic_merge<K, J / 2>(v0, i0, v1, i1, lane);
+}
+
+// Sort the 128 entries (position p = lane + 64*h) best first.
+template <int K = 128>
+__device__ __forceinline__ void bitonic_sort(double& v0, int& i0, double& v1, int& i1, int lane) {
+  if constexpr (K > 2) bitonic_sort<K / 2>(v0, i0, v1, i1, lane);
+  bitonic_merge<K, K / 2>(v0, i0, v1, i1, lane);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
   constexpr int KS = D / 4;    // f64 MFMA k-steps over the head dimension
-  constexpr int DT = D / 16;   // 16-wide output tiles over the head dimension
+  constexpr int DT = D / 16;   // 16-row tiles of O^T over the head dimension
   __shared__ double Ks[64][D + 1];
   __shared__ float Vs[64][D + 16];
-  __shared__ double Ss[4][16][65];
+  __shared__ double BufV[64][kCap];
+  __shared__ int BufI[64][kCap];
+  __shared__ int Cnt[64];
+  __shared__ double ThrV[64];
+  __shared__ int ThrI[64];
 
   const int m = a.m;
+  const int n = a.topn;
   const long long slice = blockIdx.x / a.row_tiles;
   const int tile = blockIdx.x % a.row_tiles;
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int lr = lane % 16;   // row (A operand) / column (B operand) within a tile
+  const int lr = lane % 16;   // this lane's row within the wave
   const int lg = lane / 16;   // lane group 0..3
-  const int rw = tile * 64 + w * 16;   // first row of this wave
+  const int rw = tile * 64 + w * 16;
+  const int brow = w * 16 + lr;   // this lane's row in the workgroup buffers
 
   const double* qb = a.qbar + (size_t)slice * m * D;
   const double* kb = a.kbar + (size_t)slice * m * D;
   const float* vb = a.vbar + (size_t)slice * m * D;
 
-  // A operand of the logit MFMA: q̄[rw + lr][4*ks + lg]
+  if (threadIdx.x < 64) {
+    Cnt[threadIdx.x] = 0;
+    ThrV[threadIdx.x] = -INFINITY;
+    ThrI[threadIdx.x] = 0x7fffffff;
+  }
+
+  // B operand of S^T = K̄ Q̄^T: q̄[rw + lr][4*ks + lg]
   double qa[KS];
   {
     const int row = rw + lr;
@@ -79,18 +143,10 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
   floatx4 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  double m_run = -INFINITY;   // running max of row lr
-  float l_run = 0.f;          // this lane's part of the running denominator of row lr
-
-  // top-n lists: row r of this wave, entry `lane`, sorted best first
-  double lv[16];
-  int li[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    lv[r] = -INFINITY;
-    li[r] = 0x7fffffff;
-  }
-  const int n = a.topn;
+  double m_run = -INFINITY;   // running max of row lr (dot products)
+  float l_run = 0.f;          // this lane's part of the running denominator
+  double thr_v = -INFINITY;   // current n-th best key of row lr
+  int thr_i = 0x7fffffff;
 
   for (int c0 = 0; c0 < m; c0 += 64) {
     __syncthreads();
@@ -109,98 +165,119 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
     }
     __syncthreads();
 
-    // logits of this wave's 16 rows x 64 key blocks
+    // dot products: acc[ct][i] = q̄[row lr] · k̄[c0 + 16*ct + 4*i + lg]
+    doublex4 acc[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = doublex4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], Ks[ct * 16 + lr][4 * ks + lg], acc, 0, 0, 0);
-      const int col = ct * 16 + lr;
-      const bool ok = c0 + col < m;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ss[w][4 * i + lg][col] = ok ? acc[i] / a.sqrt_d : -INFINITY;
-    }
-    __syncthreads();
+      for (int ct = 0; ct < 4; ++ct)
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ks[ct * 16 + lr][4 * ks + lg], qa[ks], acc[ct], 0, 0, 0);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (c0 + 16 * ct + 4 * i + lg >= m) acc[ct][i] = -INFINITY;
 
-    // online softmax over this chunk, row lr
-    double cmax = -INFINITY;
+    // online softmax of row lr and O^T += V̄^T P^T
+    double cmax = acc[0][0];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) cmax = fmax(cmax, Ss[w][lr][4 * kk + lg]);
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cmax = fmax(cmax, acc[ct][i]);
     cmax = fmax(cmax, __shfl_xor(cmax, 16));
     cmax = fmax(cmax, __shfl_xor(cmax, 32));
     const double m_new = fmax(m_run, cmax);
-    const float alpha = __builtin_amdgcn_exp2f((float)((m_run - m_new) * kLog2e));
+    const float alpha = __builtin_amdgcn_exp2f((float)((m_run - m_new) * a.c_exp2));
     l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ar = __shfl(alpha, 4 * lg + i);
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt][i] *= ar;
-    }
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float p = __builtin_amdgcn_exp2f((float)((Ss[w][lr][4 * kk + lg] - m_new) * kLog2e));
-      l_run += p;
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f((float)((acc[ct][i] - m_new) * a.c_exp2));
+        l_run += p;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, Vs[4 * kk + lg][dt * 16 + lr], oacc[dt], 0, 0, 0);
-    }
+        for (int dt = 0; dt < DT; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Vs[16 * ct + 4 * i + lg][dt * 16 + lr], p, oacc[dt], 0, 0, 0);
+      }
     m_run = m_new;
 
-    // top-n: merge this chunk into each row's list
-    const int col = c0 + lane;
-    const bool valid_col = col < m;
+    // selection: append the logits that beat the row's current n-th key
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (rw + r >= m) break;   // uniform across the wave
-      const double sv = Ss[w][r][lane];
-      double wv = __shfl(lv[r], n - 1);
-      int wi = __shfl(li[r], n - 1);
-      unsigned long long mask = __ballot(valid_col && beats(sv, col, wv, wi));
-      while (mask) {
-        const int b = __ffsll((long long)mask) - 1;
-        mask &= mask - 1;
-        const double cv = __shfl(sv, b);
-        const int ci = c0 + b;
-        if (!beats(cv, ci, wv, wi)) continue;
-        const int pos = __popcll(__ballot(lane < n && beats(lv[r], li[r], cv, ci)));
-        const double upv = __shfl_up(lv[r], 1);
-        const int upi = __shfl_up(li[r], 1);
-        if (lane == pos) {
-          lv[r] = cv;
-          li[r] = ci;
-        } else if (lane > pos && lane < n) {
-          lv[r] = upv;
-          li[r] = upi;
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = c0 + 16 * ct + 4 * i + lg;
+        const bool cand = col < m && beats(acc[ct][i], col, thr_v, thr_i);
+        if (__ballot(cand)) {
+          if (cand) {
+            const int pos = atomicAdd(&Cnt[brow], 1);
+            BufV[brow][pos] = acc[ct][i];
+            BufI[brow][pos] = col;
+          }
         }
-        wv = __shfl(lv[r], n - 1);
-        wi = __shfl(li[r], n - 1);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // compact rows whose buffer passed 64 entries (the next chunk adds <= 64)
+    for (int r = 0; r < 16; ++r) {
+      const int R = w * 16 + r;
+      const int c = Cnt[R];
+      if (c <= 64) continue;
+      double v0 = lane < c ? BufV[R][lane] : -INFINITY;
+      int i0 = lane < c ? BufI[R][lane] : 0x7fffffff;
+      double v1 = lane + 64 < c ? BufV[R][lane + 64] : -INFINITY;
+      int i1 = lane + 64 < c ? BufI[R][lane + 64] : 0x7fffffff;
+      bitonic_sort(v0, i0, v1, i1, lane);
+      const double tv = __shfl(v0, n - 1);
+      const int ti = __shfl(i0, n - 1);
+      if (lane < n) {
+        BufV[R][lane] = v0;
+        BufI[R][lane] = i0;
+      }
+      if (lane == 0) {
+        ThrV[R] = tv;
+        ThrI[R] = ti;
+        Cnt[R] = n;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    thr_v = ThrV[brow];
+    thr_i = ThrI[brow];
   }
 
-  // finalize o_CG = O / l
+  // o_CG = O / l; lane l holds rows lr, head-dim entries dt*16 + 4*lg + i
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  if (rw + lr < m) {
+    const float inv = 1.0f / l_run;
+    float* dst = a.o_cg + ((size_t)slice * m + rw + lr) * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = rw + 4 * lg + i;
-    const float inv = 1.0f / __shfl(l_run, 4 * lg + i);
-    if (row < m) {
-      float* dst = a.o_cg + ((size_t)slice * m + row) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dst[dt * 16 + lr] = oacc[dt][i] * inv;
-    }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(dst + dt * 16 + 4 * lg) =
+          make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
   }
 
-  // selected indices, ascending
-#pragma unroll
+  // final top-n of every row, written in ascending block order
   for (int r = 0; r < 16; ++r) {
     if (rw + r >= m) break;
+    const int R = w * 16 + r;
+    const int c = Cnt[R];
+    double v0 = lane < c ? BufV[R][lane] : -INFINITY;
+    int i0 = lane < c ? BufI[R][lane] : 0x7fffffff;
+    double v1 = lane + 64 < c ? BufV[R][lane + 64] : -INFINITY;
+    int i1 = lane + 64 < c ? BufI[R][lane + 64] : 0x7fffffff;
+    bitonic_sort(v0, i0, v1, i1, lane);
     int rank = 0;
-    for (int j = 0; j < n; ++j) rank += __shfl(li[r], j) < li[r] ? 1 : 0;
-    if (lane < n) a.sel[((size_t)slice * m + rw + r) * n + rank] = li[r];
+    for (int j = 0; j < n; ++j) rank += __shfl(i0, j) < i0 ? 1 : 0;
+    if (lane < n) a.sel[((size_t)slice * m + rw + r) * n + rank] = i0;
   }
 }
 
@@ -218,7 +295,7 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
   a.m = m;
   a.topn = topn;
   a.row_tiles = (m + 63) / 64;
-  a.sqrt_d = sqrt((double)head_dim);
+  a.c_exp2 = 1.4426950408889634 / sqrt((double)head_dim);
   dim3 grid((unsigned)(slices * a.row_tiles));
   if (head_dim == 64)
     hipLaunchKernelGGL(compress_select_kernel<64>, grid, dim3(256), 0, stream, a);

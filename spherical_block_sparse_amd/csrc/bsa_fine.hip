@@ -12,9 +12,14 @@
 // Design (gfx950, wave64):
 //   * one workgroup = 64 consecutive queries of one slice, 4 waves x 16
 //     queries; each wave keeps its 16 queries' q in registers.
-//   * keys stream through LDS 64 at a time: K row-major [key][d], V transposed
-//     [d][key] (keys permuted so each lane's MFMA operand is one 16-byte read).
-//     All four waves share each staged chunk.
+//   * keys stream through LDS 64 at a time, K and V both row-major [key][d]
+//     (16-byte writes).  The V^T operand of the P·V MFMA is read with the
+//     gfx950 transposing LDS load ds_read_b64_tr_b16: within each group of 16
+//     lanes, output lane i receives element i%4 of the 8-byte rows addressed by
+//     source lanes 4j + i/4 (j = 0..3), so a source lane r of group g points
+//     at key 32*jj + 16*h + 4*g + r/4, column 16*dt + 4*(r%4), and every lane
+//     ends up with 4 keys of one head-dim column.  All four waves share each
+//     staged chunk.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (16 keys x 16 queries per
 //     tile); in that layout each lane owns 16 scores of one query, so the
 //     online softmax (running max, exp2 with log2(e)/sqrt(d) folded in)
@@ -55,30 +60,30 @@ struct FineArgs {
   float scale_log2;   // log2(e) / sqrt(d)
 };
 
-constexpr int kVtRow = 72;   // transposed-V row: 64 keys + 8 pad (bf16 elements)
 
 struct SoftmaxState {
   float m;      // running max of raw scores (this lane's query)
   floatx4 l;    // running denominator of this lane's query (all four entries equal)
 };
 
-// position of chunk key `kappa` inside a transposed-V row, so that the B
-// operand of the P·V MFMA (lane group g, elements 0..7) reads one 16-byte run
-__device__ __forceinline__ int vt_pos(int kappa) {
-  const int kt = kappa >> 4, g = (kappa >> 2) & 3, i = kappa & 3;
-  return 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + i;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// transposing 8-byte LDS read (ds_read_b64_tr_b16)
+__device__ __forceinline__ shortx4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
 }
 
 template <int D>
 struct Tile {
   static constexpr int KK = D / 32;   // bf16 k-steps over d for S = K Q^T
   static constexpr int DT = D / 16;   // 16-row tiles of O^T over d
-  static constexpr int KROW = D + 8;  // padded K row (bf16 elements)
+  static constexpr int KROW = D + 8;  // padded K / V row (bf16 elements)
 };
 
 // Stage 64 keys into LDS.  token_of(kappa) returns the token index or -1.
 template <int D, typename F>
-__device__ __forceinline__ void stage_chunk(uint16_t* Ks, uint16_t* Vt, const uint16_t* kslice,
+__device__ __forceinline__ void stage_chunk(uint16_t* Ks, uint16_t* Vs, const uint16_t* kslice,
                                             const uint16_t* vslice, F token_of) {
   constexpr int KROW = Tile<D>::KROW;
   for (int p = threadIdx.x; p < 64 * (D / 8); p += 256) {
@@ -90,20 +95,14 @@ __device__ __forceinline__ void stage_chunk(uint16_t* Ks, uint16_t* Vt, const ui
       vx = *reinterpret_cast<const uint4*>(vslice + (size_t)tok * D + 8 * e8);
     }
     *reinterpret_cast<uint4*>(Ks + kappa * KROW + 8 * e8) = kx;
-    const int pos = vt_pos(kappa);
-    const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      Vt[(8 * e8 + 2 * h) * kVtRow + pos] = (uint16_t)(vw[h] & 0xffffu);
-      Vt[(8 * e8 + 2 * h + 1) * kVtRow + pos] = (uint16_t)(vw[h] >> 16);
-    }
+    *reinterpret_cast<uint4*>(Vs + kappa * KROW + 8 * e8) = vx;
   }
 }
 
 // One 64-key chunk for this wave's 16 queries.  valid(kappa_index) decides
 // per score when `masked`.
 template <int D, typename V>
-__device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t* Vt,
+__device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t* Vs,
                                              const bf16x8 (&qf)[Tile<D>::KK],
                                              floatx4 (&o)[Tile<D>::DT], SoftmaxState& st,
                                              float c, bool masked, V valid) {
@@ -163,7 +162,12 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t*
     st.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[j], st.l, 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + (dt * 16 + lr) * kVtRow + 32 * j + 8 * lg);
+      // A operand V^T[d = 16*dt + lr][k-slots 8*lg + e]: key of slot e is
+      // 32*j + 16*(e/4) + 4*lg + e%4, matching the score layout of pb[j]
+      const uint16_t* src = Vs + (32 * j + 4 * lg + (lr >> 2)) * KROW + dt * 16 + 4 * (lr & 3);
+      const shortx4 lo = lds_read_tr16(src);
+      const shortx4 hi = lds_read_tr16(src + 16 * KROW);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[j], o[dt], 0, 0, 0);
     }
   }
@@ -173,7 +177,7 @@ template <int D>
 __global__ __launch_bounds__(256) void fine_kernel(FineArgs a) {
   constexpr int KK = Tile<D>::KK, DT = Tile<D>::DT, KROW = Tile<D>::KROW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kVtRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * KROW];
 
   const int N = a.n_tok, B = a.block, n = a.topn, m = a.m;
   const long long slice = blockIdx.x / a.tiles;
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256) void fine_kernel(FineArgs a) {
     const int32_t* selrow = a.sel + ((size_t)slice * m + blk) * n;
     for (int vc0 = 0; vc0 < nB; vc0 += 64) {
       __syncthreads();
-      stage_chunk<D>(Ks, Vt, ks, vs, [&](int kappa) {
+      stage_chunk<D>(Ks, Vs, ks, vs, [&](int kappa) {
         const int vk = vc0 + kappa;
         if (vk >= nB) return -1;
         int j = selrow[vk / B];
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(256) void fine_kernel(FineArgs a) {
       });
       __syncthreads();
       if (active)
-        attend_chunk<D>(Ks, Vt, qf, ofg, sfg, c, nB - vc0 < 64, [&](int kappa) { return vc0 + kappa < nB; });
+        attend_chunk<D>(Ks, Vs, qf, ofg, sfg, c, nB - vc0 < 64, [&](int kappa) { return vc0 + kappa < nB; });
     }
   }
 
@@ -235,11 +239,11 @@ __global__ __launch_bounds__(256) void fine_kernel(FineArgs a) {
   const int ihi = (int)min((long long)N, (long long)tw + hi_off);
   for (int u0 = wlo; u0 < whi; u0 += 64) {
     __syncthreads();
-    stage_chunk<D>(Ks, Vt, ks, vs, [&](int kappa) { return u0 + kappa < whi ? u0 + kappa : -1; });
+    stage_chunk<D>(Ks, Vs, ks, vs, [&](int kappa) { return u0 + kappa < whi ? u0 + kappa : -1; });
     __syncthreads();
     if (u0 < uhi && u0 + 64 > ulo) {
       const bool full = u0 >= ilo && u0 + 64 <= ihi;
-      attend_chunk<D>(Ks, Vt, qf, ol, sl, c, !full, [&](int kappa) {
+      attend_chunk<D>(Ks, Vs, qf, ol, sl, c, !full, [&](int kappa) {
         const int u = u0 + kappa;
         return u >= tq - lo_off && u < tq + hi_off && u < N;
       });

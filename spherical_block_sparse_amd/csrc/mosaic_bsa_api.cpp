@@ -3,7 +3,7 @@
 // Every entry point validates all arguments before the first HIP call, so an
 // invalid call launches nothing and leaves the outputs untouched; errors are
 // returned as mosaic_status with a thread-local message.
-#include "../../include/mosaic_bsa.h"
+#include "mosaic_bsa.h"
 
 #include <hip/hip_runtime.h>
 
