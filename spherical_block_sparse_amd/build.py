@@ -37,9 +37,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmosaic_bsa)")
 
 
+# per-source extra flags: the fine-attention kernel never relies on NaN
+# semantics (masked scores are -inf, which stays honoured), and without this
+# every fmaxf of an MFMA result is preceded by a NaN-quieting instruction
+EXTRA = {"bsa_fine.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
   const int n = a.topn;
   const long long slice = blockIdx.x / a.row_tiles;
   const int tile = blockIdx.x % a.row_tiles;
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // scalar: uniform branches
   const int lane = threadIdx.x % kWave;
   const int lr = lane % 16;   // this lane's row within the wave
   const int lg = lane / 16;   // lane group 0..3

@@ -10,29 +10,40 @@
 // selected branch is one softmax over the union of the selected tokens.
 //
 // Design (gfx950, wave64):
-//   * one workgroup = 64 consecutive queries of one slice, 4 waves x 16
-//     queries; each wave keeps its 16 queries' q in registers.
-//   * keys stream through LDS 64 at a time, K and V both row-major [key][d]
-//     (16-byte writes).  The V^T operand of the P·V MFMA is read with the
-//     gfx950 transposing LDS load ds_read_b64_tr_b16: within each group of 16
-//     lanes, output lane i receives element i%4 of the 8-byte rows addressed by
-//     source lanes 4j + i/4 (j = 0..3), so a source lane r of group g points
-//     at key 32*jj + 16*h + 4*g + r/4, column 16*dt + 4*(r%4), and every lane
-//     ends up with 4 keys of one head-dim column.  All four waves share each
-//     staged chunk.
+//   * a workgroup owns T = 32*WAVES consecutive queries of one slice (T = 64
+//     for blocks of 64 tokens, 128 when a block holds >= 128 tokens so that
+//     more queries share one gathered key set); each wave owns 32 queries as
+//     two 16-query sub-tiles whose MFMAs share every K / V operand read.
+//   * keys stream into LDS 64 at a time with gfx950 direct global->LDS loads
+//     (global_load_lds_dwordx4: lane l of a wave's load writes bytes
+//     16*l..16*l+15 of a 1 KB span), K and V row-major [key][d] with the
+//     16-byte chunks of each row XOR-swizzled; double-buffered in two
+//     separate LDS objects so the loads of chunk c+1 are in flight while
+//     chunk c is computed, one barrier per chunk, no staging registers.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (16 keys x 16 queries per
 //     tile); in that layout each lane owns 16 scores of one query, so the
-//     online softmax (running max, exp2 with log2(e)/sqrt(d) folded in)
-//     needs only two cross-lane steps per chunk, and the bf16-rounded weights
-//     are already the B operand of O^T += V^T P^T; the denominator is the
-//     same MFMA with an all-ones A operand (sum of the rounded weights).
-//   * selected branch: the chunk gathers n*block tokens by the selection
-//     indices (virtual key v -> token sel[v/block]*block + v%block); for
-//     blocks smaller than 64 the tile's 64/block query blocks are taken in
-//     turn, each by the wave(s) whose queries it holds.
+//     online softmax needs two cross-lane steps per chunk and the
+//     bf16-rounded weights are already the B operand of O^T += V^T P^T.
+//   * the V^T operand is read with the gfx950 transposing LDS load
+//     ds_read_b64_tr_b16: within each group of 16 lanes, output lane i
+//     receives element i%4 of the 8-byte rows addressed by source lanes
+//     4j + i/4 (j = 0..3), so source lane r of group g points at key
+//     32*jj + 16*h + 4*g + r/4, column 16*dt + 4*(r%4).
+//   * softmax in base 2 with log2(e)/sqrt(d) folded into the scores; the
+//     running reference max only moves when a score exceeds it by more than
+//     2^8 (weights stay <= 256), so O is rescaled on few chunks; the
+//     denominator is the same MFMA with an all-ones A operand (sum of the
+//     rounded weights, so each output is an exact convex combination of the
+//     weights actually applied).
+//   * selected branch: virtual key v of a group -> token sel[v/block]*block +
+//     v%block; for blocks smaller than T the tile's T/block query blocks are
+//     taken in turn by the sub-tiles they contain.
 //   * local branch: the union of the tile's windows is streamed; chunks
-//     inside every window of a wave's 16 queries run unmasked, chunks outside
-//     them are skipped, the rest are masked per score.
+//     inside every window of a sub-tile run unmasked, chunks outside it are
+//     skipped, the rest are masked per score.
+//   * workgroup ids are remapped so each XCD (dispatched round-robin) gets a
+//     contiguous run of tiles: neighbouring tiles share window keys and
+//     largely the same selected blocks, and they now share an L2.
 //   * epilogue: out = g0·o_CG[t/block] + g1·o_FG + g2·o_L, float32.
 // Roofline: bf16 matrix work 4*d*(n*block + W) per query, HBM traffic at
 // least q, k, v once plus gates, o_CG and out.
@@ -56,18 +67,15 @@ struct FineArgs {
   int topn;
   int window;
   int m;
-  int tiles;
+  int tiles;          // query tiles per slice
+  long long groups;   // total workgroups
   float scale_log2;   // log2(e) / sqrt(d)
-};
-
-
-struct SoftmaxState {
-  float m;      // running max of raw scores (this lane's query)
-  floatx4 l;    // running denominator of this lane's query (all four entries equal)
 };
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+constexpr float kLazy = 8.0f;   // rescale only when the scaled max grows by > 8 (a factor 2^8)
 
 // transposing 8-byte LDS read (ds_read_b64_tr_b16)
 __device__ __forceinline__ shortx4 lds_read_tr16(const uint16_t* p) {
@@ -78,115 +86,214 @@ template <int D>
 struct Tile {
   static constexpr int KK = D / 32;   // bf16 k-steps over d for S = K Q^T
   static constexpr int DT = D / 16;   // 16-row tiles of O^T over d
-  static constexpr int KROW = D + 8;  // padded K / V row (bf16 elements)
 };
 
-// Stage 64 keys into LDS.  token_of(kappa) returns the token index or -1.
-template <int D, typename F>
-__device__ __forceinline__ void stage_chunk(uint16_t* Ks, uint16_t* Vs, const uint16_t* kslice,
-                                            const uint16_t* vslice, F token_of) {
-  constexpr int KROW = Tile<D>::KROW;
-  for (int p = threadIdx.x; p < 64 * (D / 8); p += 256) {
-    const int kappa = p / (D / 8), e8 = p % (D / 8);
-    const int tok = token_of(kappa);
-    uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-    if (tok >= 0) {
-      kx = *reinterpret_cast<const uint4*>(kslice + (size_t)tok * D + 8 * e8);
-      vx = *reinterpret_cast<const uint4*>(vslice + (size_t)tok * D + 8 * e8);
-    }
-    *reinterpret_cast<uint4*>(Ks + kappa * KROW + 8 * e8) = kx;
-    *reinterpret_cast<uint4*>(Vs + kappa * KROW + 8 * e8) = vx;
-  }
+// XOR swizzle of the 16-byte chunks of an LDS row (rows are D*2 bytes, no
+// padding, so a 1 KB direct load fills whole rows).  For D = 64 it keeps both
+// the 16-row K operand reads and the transposing V reads free of bank
+// conflicts; for D = 32 the K reads.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 64) return 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
+  else return (row >> 2) & 3;
 }
 
-// One 64-key chunk for this wave's 16 queries.  valid(kappa_index) decides
-// per score when `masked`.
-template <int D, typename V>
-__device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t* Vs,
-                                             const bf16x8 (&qf)[Tile<D>::KK],
-                                             floatx4 (&o)[Tile<D>::DT], SoftmaxState& st,
-                                             float c, bool masked, V valid) {
-  constexpr int KK = Tile<D>::KK, DT = Tile<D>::DT, KROW = Tile<D>::KROW;
+template <int D>
+struct Branch {               // online-softmax state of one 16-query sub-tile
+  floatx4 o[Tile<D>::DT];     // O^T: lane holds d = 16*dt + 4*lg + i of query lr
+  floatx4 l;                  // denominator (all four entries equal)
+  float m;                    // reference max, log2 units
+};
+
+template <int D>
+__device__ __forceinline__ void branch_init(Branch<D>& b) {
+#pragma unroll
+  for (int dt = 0; dt < Tile<D>::DT; ++dt) b.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  b.l = floatx4{0.f, 0.f, 0.f, 0.f};
+  b.m = -INFINITY;
+}
+
+// P·V for both sub-tiles (and the denominators, as an all-ones A operand);
+// act[s] false skips sub-tile s.
+template <int D, bool ALL>
+__device__ __forceinline__ void pv_chunk(const uint16_t* Vs, const bf16x8 (&pb)[2][2], Branch<D> (&br)[2],
+                                         const bool (&act)[2]) {
+  constexpr int DT = Tile<D>::DT;
   const int lane = threadIdx.x % kWave;
   const int lr = lane % 16, lg = lane / 16;
-
-  float s[4][4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (kt * 16 + lr) * KROW + 32 * kk + 8 * lg);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[kt][i] = acc[i];
-  }
-  if (masked) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!valid(16 * kt + 4 * lg + i)) s[kt][i] = -INFINITY;
-  }
-
-  float mx = s[0][0];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float msc = m_new == -INFINITY ? 0.f : m_new * c;
-  const float alpha = __builtin_amdgcn_exp2f(st.m * c - msc);
-
-  bf16x8 pb[2];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pb[kt >> 1][4 * (kt & 1) + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -msc)));
-  st.m = m_new;
-  st.l *= alpha;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-  // The denominator is the sum of the same bf16-rounded weights that multiply
-  // V (an all-ones A operand), so each output is an exact convex combination
-  // of the weights actually used; every row of that tile holds the sum.
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    st.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[j], st.l, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (ALL || act[s]) br[s].l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[s][j], br[s].l, 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      // A operand V^T[d = 16*dt + lr][k-slots 8*lg + e]: key of slot e is
-      // 32*j + 16*(e/4) + 4*lg + e%4, matching the score layout of pb[j]
-      const uint16_t* src = Vs + (32 * j + 4 * lg + (lr >> 2)) * KROW + dt * 16 + 4 * (lr & 3);
+      // A operand V^T[d = 16*dt + lr][k-slots 8*lg + e]; slot e holds key
+      // 32*j + 16*(e/4) + 4*lg + e%4, the order of the scores in pb[s][j]
+      // (swz(row + 16) == swz(row), so the second half is 16 rows further)
+      const int row = 32 * j + 4 * lg + (lr >> 2);
+      const int col = dt * 16 + 4 * (lr & 3);
+      const uint16_t* src = Vs + row * D + 8 * ((col >> 3) ^ swz<D>(row)) + (col & 7);
       const shortx4 lo = lds_read_tr16(src);
-      const shortx4 hi = lds_read_tr16(src + 16 * KROW);
+      const shortx4 hi = lds_read_tr16(src + 16 * D);
       const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[j], o[dt], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (ALL || act[s]) br[s].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[s][j], br[s].o[dt], 0, 0, 0);
     }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void fine_kernel(FineArgs a) {
-  constexpr int KK = Tile<D>::KK, DT = Tile<D>::DT, KROW = Tile<D>::KROW;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * KROW];
-
-  const int N = a.n_tok, B = a.block, n = a.topn, m = a.m;
-  const long long slice = blockIdx.x / a.tiles;
-  const int t0 = (blockIdx.x % a.tiles) * 64;
-  const int w = threadIdx.x / kWave;
+// S^T tiles of both sub-tiles: acc[s][kt][i] = q_(lr) . k_(16*kt + 4*lg + i)
+template <int D, bool ALL>
+__device__ __forceinline__ void qk_chunk(const uint16_t* Ks, const bf16x8 (&qf)[2][Tile<D>::KK],
+                                         floatx4 (&acc)[2][4], const bool (&act)[2]) {
+  constexpr int KK = Tile<D>::KK;
   const int lane = threadIdx.x % kWave;
   const int lr = lane % 16, lg = lane / 16;
-  const int tw = t0 + 16 * w;   // first query of this wave
-  const int tq = tw + lr;       // this lane's query
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) acc[s][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int row = kt * 16 + lr;
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + row * D + 8 * ((4 * kk + lg) ^ swz<D>(row)));
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (ALL || act[s]) acc[s][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[s][kk], acc[s][kt], 0, 0, 0);
+    }
+}
+
+// Online-softmax update of the sub-tiles in `act` from raw scores acc (the
+// scale c = log2(e)/sqrt(d) is applied inside the exp2 argument).  The
+// reference max moves only when a score exceeds it by more than 2^8 after
+// scaling; that decision is taken for the whole wave, so it is a scalar
+// branch (any lane may move its reference: alpha <= 1 is always exact).
+template <int D, bool ALL>
+__device__ __forceinline__ void softmax_chunk(floatx4 (&acc)[2][4], Branch<D> (&br)[2], bf16x8 (&pb)[2][2],
+                                              const bool (&act)[2], float c, float lazy_raw) {
+  constexpr int DT = Tile<D>::DT;
+  float mx[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float a = fmaxf(acc[s][0][0], acc[s][0][1]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = (kt == 0 ? 2 : 0); i < 4; i += 2) a = fmaxf(a, fmaxf(acc[s][kt][i], acc[s][kt][i + 1]));
+    a = fmaxf(a, __shfl_xor(a, 16));
+    mx[s] = fmaxf(a, __shfl_xor(a, 32));
+  }
+  const bool grow = (ALL || act[0]) && mx[0] > br[0].m + lazy_raw;
+  const bool grow1 = (ALL || act[1]) && mx[1] > br[1].m + lazy_raw;
+  if (__ballot(grow || grow1)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (!(ALL || act[s])) continue;
+      const float mnew = fmaxf(br[s].m, mx[s]);
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((br[s].m - mnew) * c);
+      br[s].m = mnew;
+      br[s].l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) br[s].o[dt] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (!(ALL || act[s])) continue;
+    const float nmc = br[s].m == -INFINITY ? 0.f : -br[s].m * c;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pb[s][kt >> 1][4 * (kt & 1) + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(acc[s][kt][i], c, nmc)));
+  }
+}
+
+// One staged 64-key chunk, every key valid for both sub-tiles (the common case).
+template <int D>
+__device__ __forceinline__ void attend_full(const uint16_t* Ks, const uint16_t* Vs,
+                                            const bf16x8 (&qf)[2][Tile<D>::KK], Branch<D> (&br)[2],
+                                            float c, float lazy_raw) {
+  const bool act[2] = {true, true};
+  floatx4 acc[2][4];
+  bf16x8 pb[2][2];
+  qk_chunk<D, true>(Ks, qf, acc, act);
+  softmax_chunk<D, true>(acc, br, pb, act, c, lazy_raw);
+  pv_chunk<D, true>(Vs, pb, br, act);
+}
+
+// One staged 64-key chunk in general form: act[s] says whether sub-tile s
+// takes part, msk[s] whether its scores need valid(s, kappa).
+template <int D, typename V>
+__device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t* Vs,
+                                             const bf16x8 (&qf)[2][Tile<D>::KK], Branch<D> (&br)[2],
+                                             const bool (&act)[2], const bool (&msk)[2], float c,
+                                             float lazy_raw, V valid) {
+  if (!act[0] && !act[1]) return;
+  const int lg = (threadIdx.x % kWave) / 16;
+  floatx4 acc[2][4];
+  bf16x8 pb[2][2];
+  qk_chunk<D, false>(Ks, qf, acc, act);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    if (act[s] && msk[s]) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!valid(s, 16 * kt + 4 * lg + i)) acc[s][kt][i] = -INFINITY;
+    }
+  softmax_chunk<D, false>(acc, br, pb, act, c, lazy_raw);
+  pv_chunk<D, false>(Vs, pb, br, act);
+}
+
+// 16 zero bytes: the DMA source of key slots that hold no token (masked keys
+// then read exact zeros, as a zero-filled chunk would hold)
+__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void fine_kernel(FineArgs a) {
+  constexpr int KK = Tile<D>::KK, DT = Tile<D>::DT;
+  constexpr int T = 32 * WAVES;           // queries per workgroup
+  constexpr int CPR = D / 8;              // 16-byte chunks per key row
+  constexpr int RPG = 64 / CPR;           // key rows per 1 KB load (one wave instruction)
+  constexpr int GPC = 64 / RPG;           // 1 KB loads per tensor per 64-key chunk
+  static_assert(GPC % WAVES == 0, "loads split evenly over the waves");
+  // two LDS buffers as separate objects, so the compiler can tell the chunk
+  // being read from the one the DMA is filling
+  __shared__ __attribute__((aligned(16))) uint16_t Kb0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Kb1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb1[64 * D];
+  __shared__ int SelT[4 * 64];   // selection rows of the tile's query blocks (<= T/16 rows of <= 64)
+
+  // contiguous run of tiles per XCD (workgroups are dispatched round-robin)
+  long long logical;
+  {
+    const long long G = a.groups, b = blockIdx.x;
+    const long long q8 = G / 8, r8 = G % 8, xcd = b % 8, k = b / 8;
+    logical = xcd < r8 ? xcd * (q8 + 1) + k : r8 * (q8 + 1) + (xcd - r8) * q8 + k;
+  }
+  const int N = a.n_tok, B = a.block, n = a.topn, m = a.m;
+  const long long slice = logical / a.tiles;
+  const int t0 = (int)(logical % a.tiles) * T;
+  // wave index as a scalar: every per-wave decision below (which sub-tiles
+  // take part in a chunk, masking) is then a scalar branch, so no MFMA ever
+  // sits under an EXEC-masked region
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int lr = lane % 16, lg = lane / 16;
+  const int tw = t0 + 32 * w;   // first query of this wave
 
   const size_t sbase = (size_t)slice * N * D;
   const uint16_t* qs = a.q + sbase;
@@ -194,79 +301,218 @@ __global__ __launch_bounds__(256) void fine_kernel(FineArgs a) {
   const uint16_t* vs = a.v + sbase;
   const float c = a.scale_log2;
 
-  // B operand of S^T = K Q^T: Q[query lr][32*kk + 8*lg + e]
-  bf16x8 qf[KK];
+  // B operands of S^T = K Q^T: Q[query ts + lr][32*kk + 8*lg + e]
+  bf16x8 qf[2][KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qs + (size_t)tq * D + 32 * kk + 8 * lg);
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[s][kk] = *reinterpret_cast<const bf16x8*>(qs + (size_t)(tw + 16 * s + lr) * D + 32 * kk + 8 * lg);
 
-  // ---- selected branch ------------------------------------------------
-  floatx4 ofg[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) ofg[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState sfg = {-INFINITY, floatx4{0.f, 0.f, 0.f, 0.f}};
+  // chunk plan: selected-branch chunks (per query-block group), then window chunks
   const int nB = n * B;
-  const int groups = B >= 64 ? 1 : 64 / B;
-  for (int gi = 0; gi < groups; ++gi) {
-    const int blk = t0 / B + gi;
-    const bool active = B >= 64 || tw / B == blk;
-    const int32_t* selrow = a.sel + ((size_t)slice * m + blk) * n;
-    for (int vc0 = 0; vc0 < nB; vc0 += 64) {
-      __syncthreads();
-      stage_chunk<D>(Ks, Vs, ks, vs, [&](int kappa) {
-        const int vk = vc0 + kappa;
-        if (vk >= nB) return -1;
-        int j = selrow[vk / B];
-        j = j < 0 ? 0 : (j >= m ? m - 1 : j);   // never read outside the slice
-        return j * B + vk % B;
-      });
-      __syncthreads();
-      if (active)
-        attend_chunk<D>(Ks, Vs, qf, ofg, sfg, c, nB - vc0 < 64, [&](int kappa) { return vc0 + kappa < nB; });
-    }
-  }
-
-  // ---- local branch -----------------------------------------------------
-  floatx4 ol[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) ol[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState sl = {-INFINITY, floatx4{0.f, 0.f, 0.f, 0.f}};
+  const int groups = B >= T ? 1 : T / B;
+  const int cpg = (nB + 63) / 64;
+  const int c_sel = groups * cpg;
   const int lo_off = a.window / 2, hi_off = a.window - a.window / 2;
   const int wlo = max(0, t0 - lo_off);
-  const int whi = (int)min((long long)N, (long long)t0 + 63 + hi_off);
-  const int ulo = max(0, tw - lo_off);                                 // union of this wave's windows
-  const int uhi = (int)min((long long)N, (long long)tw + 15 + hi_off);
-  const int ilo = max(0, tw + 15 - lo_off);                            // intersection of them
-  const int ihi = (int)min((long long)N, (long long)tw + hi_off);
-  for (int u0 = wlo; u0 < whi; u0 += 64) {
-    __syncthreads();
-    stage_chunk<D>(Ks, Vs, ks, vs, [&](int kappa) { return u0 + kappa < whi ? u0 + kappa : -1; });
-    __syncthreads();
-    if (u0 < uhi && u0 + 64 > ulo) {
-      const bool full = u0 >= ilo && u0 + 64 <= ihi;
-      attend_chunk<D>(Ks, Vs, qf, ol, sl, c, !full, [&](int kappa) {
-        const int u = u0 + kappa;
-        return u >= tq - lo_off && u < tq + hi_off && u < N;
-      });
+  const int whi = (int)min((long long)N, (long long)t0 + T - 1 + hi_off);
+  const int c_all = c_sel + (whi - wlo + 63) / 64;
+  const int blk0 = t0 / B;
+  {
+    // the selection rows of this tile's query blocks, clamped so that a bad
+    // index can never address outside the slice
+    const int32_t* selbase = a.sel + ((size_t)slice * m + blk0) * n;
+    for (int e = threadIdx.x; e < groups * n; e += 64 * WAVES) {
+      const int j = selbase[e];
+      SelT[e] = j < 0 ? 0 : (j >= m ? m - 1 : j);
     }
+    __syncthreads();
   }
 
-  // ---- gated sum ----------------------------------------------------------
-  const float lfg = sfg.l[0], ll = sl.l[0];
-  const float* g = a.gates + ((size_t)slice * N + tq) * 3;
-  const float g0 = g[0], g1 = g[1] / lfg, g2 = g[2] / ll;
-  const float* ocg = a.o_cg + ((size_t)slice * m + tq / B) * D;
-  float* dst = a.out + ((size_t)slice * N + tq) * D;
+  auto token_of = [&](int ci, int kappa) __attribute__((always_inline)) -> int {
+    if (ci < c_sel) {
+      const int gi = ci / cpg;
+      const int vk = (ci - gi * cpg) * 64 + kappa;
+      if (vk >= nB) return -1;
+      return SelT[gi * n + vk / B] * B + vk % B;
+    }
+    const int u = wlo + (ci - c_sel) * 64 + kappa;
+    return u < whi ? u : -1;
+  };
+
+  // Direct global -> LDS loads of chunk ci: lane l of a 1 KB load writes
+  // physical chunk l % CPR of row RPG*grp + l / CPR, which holds logical
+  // chunk (l % CPR) ^ swz(row) of that key row.  When the chunk's keys are
+  // consecutive tokens tok0 .. tok0+valid-1 (every window chunk, and every
+  // selected chunk when a key block holds >= 64 tokens) the per-lane offsets
+  // are fixed; otherwise each row looks its token up.
+  constexpr int LPW = GPC / WAVES;   // 1 KB loads per tensor per wave
+  int lane_off[LPW], lane_row[LPW];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int d0 = dt * 16 + 4 * lg;
-    const float4 cg = *reinterpret_cast<const float4*>(ocg + d0);
-    float4 r;
-    r.x = g0 * cg.x + g1 * ofg[dt][0] + g2 * ol[dt][0];
-    r.y = g0 * cg.y + g1 * ofg[dt][1] + g2 * ol[dt][1];
-    r.z = g0 * cg.z + g1 * ofg[dt][2] + g2 * ol[dt][2];
-    r.w = g0 * cg.w + g1 * ofg[dt][3] + g2 * ol[dt][3];
-    *reinterpret_cast<float4*>(dst + d0) = r;
+  for (int gg = 0; gg < LPW; ++gg) {
+    const int grp = w + WAVES * gg;
+    lane_row[gg] = RPG * grp + lane / CPR;
+    lane_off[gg] = lane_row[gg] * D + 8 * ((lane % CPR) ^ swz<D>(lane_row[gg]));
   }
+  auto issue_rows = [&](int tok0, int valid, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
+    const char* kbase = reinterpret_cast<const char*>(ks + (size_t)tok0 * D);   // uniform
+    const char* vbase = reinterpret_cast<const char*>(vs + (size_t)tok0 * D);
+    if (valid >= 64) {   // whole chunk of consecutive tokens: no per-lane checks
+#pragma unroll
+      for (int gg = 0; gg < LPW; ++gg) {
+        const int grp = w + WAVES * gg;
+        const unsigned off = 2u * (unsigned)lane_off[gg];
+        __builtin_amdgcn_global_load_lds((global_void*)(kbase + off), (lds_void*)(kb + grp * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_void*)(vbase + off), (lds_void*)(vb + grp * 512), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < LPW; ++gg) {
+        const int grp = w + WAVES * gg;
+        const bool ok = lane_row[gg] < valid;
+        const unsigned off = 2u * (unsigned)lane_off[gg];
+        const void* ksrc = ok ? (const void*)(kbase + off) : (const void*)&kZero16;
+        const void* vsrc = ok ? (const void*)(vbase + off) : (const void*)&kZero16;
+        __builtin_amdgcn_global_load_lds((global_void*)ksrc, (lds_void*)(kb + grp * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_void*)vsrc, (lds_void*)(vb + grp * 512), 16, 0, 0);
+      }
+    }
+  };
+  auto issue_gather = [&](int ci, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int gg = 0; gg < LPW; ++gg) {
+      const int grp = w + WAVES * gg;
+      const int row = lane_row[gg];
+      const int lc = (lane % CPR) ^ swz<D>(row);
+      const int tok = token_of(ci, row);
+      const void* ksrc = tok >= 0 ? (const void*)(ks + (size_t)tok * D + 8 * lc) : (const void*)&kZero16;
+      const void* vsrc = tok >= 0 ? (const void*)(vs + (size_t)tok * D + 8 * lc) : (const void*)&kZero16;
+      __builtin_amdgcn_global_load_lds((global_void*)ksrc, (lds_void*)(kb + grp * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)vsrc, (lds_void*)(vb + grp * 512), 16, 0, 0);
+    }
+  };
+  auto issue = [&](int ci, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
+    if (ci >= c_sel) {
+      const int u0 = wlo + (ci - c_sel) * 64;
+      issue_rows(u0, whi - u0, kb, vb);
+    } else if (B >= 64) {
+      const int gi = ci / cpg;
+      const int vk0 = (ci - gi * cpg) * 64;   // a multiple of 64 inside one key block
+      issue_rows(SelT[gi * n + vk0 / B] * B + vk0 % B, nB - vk0, kb, vb);
+    } else {
+      issue_gather(ci, kb, vb);
+    }
+  };
+
+  Branch<D> br[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) branch_init(br[s]);
+  float4 pre[2][DT];   // g_CG*o_CG + g_FG*o_FG, formed when the selected branch ends
+
+  auto finish_selected = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int tq = tw + 16 * s + lr;
+      const float* g = a.gates + ((size_t)slice * N + tq) * 3;
+      const float g0 = g[0], g1 = g[1] / br[s].l[0];
+      const float* ocg = a.o_cg + ((size_t)slice * m + tq / B) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float4 cg = *reinterpret_cast<const float4*>(ocg + dt * 16 + 4 * lg);
+        pre[s][dt] = make_float4(g0 * cg.x + g1 * br[s].o[dt][0], g0 * cg.y + g1 * br[s].o[dt][1],
+                                 g0 * cg.z + g1 * br[s].o[dt][2], g0 * cg.w + g1 * br[s].o[dt][3]);
+      }
+      branch_init(br[s]);
+    }
+  };
+
+  const float lazy_raw = kLazy / c;
+  auto step_selected = [&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
+    const int gi = ci / cpg;
+    const int vc0 = (ci - gi * cpg) * 64;
+    if (B >= T && nB - vc0 >= 64) {
+      attend_full<D>(kb, vb, qf, br, c, lazy_raw);
+      return;
+    }
+    bool act[2], msk[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      act[s] = B >= T || (tw + 16 * s) / B == blk0 + gi;
+      msk[s] = nB - vc0 < 64;
+    }
+    attend_chunk<D>(kb, vb, qf, br, act, msk, c, lazy_raw, [&](int, int kappa) { return vc0 + kappa < nB; });
+  };
+  auto step_local = [&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
+    const int u0 = wlo + (ci - c_sel) * 64;
+    bool act[2], msk[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int ts = tw + 16 * s;
+      const int ulo = max(0, ts - lo_off);                                  // union of the windows
+      const int uhi = (int)min((long long)N, (long long)ts + 15 + hi_off);
+      const int ilo = max(0, ts + 15 - lo_off);                             // their intersection
+      const int ihi = (int)min((long long)N, (long long)ts + hi_off);
+      act[s] = u0 < uhi && u0 + 64 > ulo;
+      msk[s] = !(u0 >= ilo && u0 + 64 <= ihi);
+    }
+    if (act[0] && act[1] && !msk[0] && !msk[1]) {
+      attend_full<D>(kb, vb, qf, br, c, lazy_raw);
+      return;
+    }
+    attend_chunk<D>(kb, vb, qf, br, act, msk, c, lazy_raw, [&](int s, int kappa) {
+      const int u = u0 + kappa, t = tw + 16 * s + lr;
+      return u >= t - lo_off && u < t + hi_off && u < N;
+    });
+  };
+
+  // Chunks [c0, c1) double-buffered: the loads of chunk ci+1 run while chunk
+  // ci is computed; each barrier follows the wave's wait for its own loads.
+  auto run = [&](int c0, int c1, auto step) __attribute__((always_inline)) {
+    if (c0 >= c1) return;
+    issue(c0, Kb0, Vb0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    for (int ci = c0; ci < c1; ci += 2) {
+      if (ci + 1 < c1) issue(ci + 1, Kb1, Vb1);
+      step(ci, Kb0, Vb0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (ci + 1 >= c1) break;
+      if (ci + 2 < c1) issue(ci + 2, Kb0, Vb0);
+      step(ci + 1, Kb1, Vb1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+  };
+  run(0, c_sel, step_selected);
+  finish_selected();
+  run(c_sel, c_all, step_local);
+
+  // gated sum: pre + g_L * o_L
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int tq = tw + 16 * s + lr;
+    const float g2 = a.gates[((size_t)slice * N + tq) * 3 + 2] / br[s].l[0];
+    float* dst = a.out + ((size_t)slice * N + tq) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      float4 r = pre[s][dt];
+      r.x += g2 * br[s].o[dt][0];
+      r.y += g2 * br[s].o[dt][1];
+      r.z += g2 * br[s].o[dt][2];
+      r.w += g2 * br[s].o[dt][3];
+      *reinterpret_cast<float4*>(dst + dt * 16 + 4 * lg) = r;
+    }
+  }
+}
+
+template <int D, int WAVES>
+hipError_t launch(FineArgs a, hipStream_t stream) {
+  a.tiles = a.n_tok / (32 * WAVES);
+  dim3 grid((unsigned)a.groups);
+  hipLaunchKernelGGL((fine_kernel<D, WAVES>), grid, dim3(64 * WAVES), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -288,14 +534,12 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.topn = topn;
   a.window = window;
   a.m = n_tok / block;
-  a.tiles = n_tok / 64;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
-  dim3 grid((unsigned)(slices * a.tiles));
-  if (head_dim == 64)
-    hipLaunchKernelGGL(fine_kernel<64>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(fine_kernel<32>, grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  // 128-query tiles when a block holds >= 128 tokens (N is then a multiple of 128)
+  const bool wide = block >= 128 && n_tok % 128 == 0;
+  a.groups = slices * (n_tok / (wide ? 128 : 64));
+  if (head_dim == 64) return wide ? launch<64, 4>(a, stream) : launch<64, 2>(a, stream);
+  return wide ? launch<32, 4>(a, stream) : launch<32, 2>(a, stream);
 }
 
 }  // namespace mosaic
