@@ -18,8 +18,7 @@ by gates g_CG, g_FG, g_L:
   (c) local: standard attention of each query over a sliding window;
   out_t = g_CG·o_CG + g_FG·o_FG + g_L·o_L.
 
-Readings taken where the pages are silent or ambiguous (the same list is kept
-in DESIGN.md):
+Readings taken where the pages are silent or ambiguous:
 
   c1  pooling phi = arithmetic mean over the block's tokens, no weights.
   c2  the compressed branch uses block-level q̄_i; its output for block i,

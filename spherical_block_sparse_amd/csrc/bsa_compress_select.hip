@@ -19,10 +19,13 @@
 //     is monotone), so the selection equals a float64 evaluation up to the
 //     summation order of 64 products.
 //   * top-n: each row keeps its current n-th best (value, index) key; the
-//     logits that beat it are appended to the row's LDS buffer with an LDS
-//     atomic, and when a buffer passes 64 entries one wave compacts it to its
-//     best n with a 128-element bitonic network (DPP / swizzle exchanges),
-//     which raises the key.  A final compaction orders the n survivors.
+//     logits that beat it are appended to the row's LDS candidate buffer at
+//     slots given by a prefix count over the lanes that hold the row (no
+//     atomics).  When a buffer could overflow on the next chunk, the wave
+//     compacts four rows at once (one per 16-lane group, 8 entries per lane)
+//     to their best n with a 128-entry bitonic network (register and DPP /
+//     swizzle exchanges), which raises the row's key.  A final compaction
+//     ranks the n survivors and writes them in ascending block order.
 // Roofline: float64 matrix work 2*m^2*d per slice for the logits plus
 // float32 matrix work 2*m^2*d for ā·v̄; HBM traffic is only the pooled
 // tensors, o_CG and the indices.
@@ -61,52 +64,94 @@ __device__ __forceinline__ int xor_lane(int x) {
   else return __builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ J) << 2, x);
 }
 
-// compare-exchange of position p with p ^ J inside a bitonic block of size K
-template <int J, int K>
-__device__ __forceinline__ void bitonic_step(double& v, int& i, int p) {
-  const long long b = __double_as_longlong(v);
-  const int plo = xor_lane<J>((int)(b & 0xffffffffLL));
-  const int phi = xor_lane<J>((int)(b >> 32));
-  const int pi = xor_lane<J>(i);
-  const double pv = __longlong_as_double(((long long)phi << 32) | (unsigned)plo);
-  const bool lower = (p & J) == 0;
-  const bool desc = (p & K) == 0;
-  const bool mine = beats(v, i, pv, pi);
-  if (!((lower == desc) ? mine : !mine)) {
-    v = pv;
-    i = pi;
-  }
-}
-
-template <int K, int J>
-__device__ __forceinline__ void bitonic_merge(double& v0, int& i0, double& v1, int& i1, int lane) {
-  if constexpr (J == 64) {   // positions lane and lane+64 sit in the same lane
-    if (!beats(v0, i0, v1, i1)) {
-      const double tv = v0; const int ti = i0;
-      v0 = v1; i0 = i1; v1 = tv; i1 = ti;
+// Four rows at once, one per 16-lane group: lane l of a group holds
+// positions 8*l .. 8*l+7 of its row's 128-entry buffer in v[e], ix[e].
+// Bitonic sort, best first.  Exchanges at distances 1, 2, 4 stay inside a
+// lane (register compare-exchanges); distances 8 .. 64 are lane distances
+// 1 .. 8 inside the 16-lane group (DPP / swizzle).
+template <int J>
+__device__ __forceinline__ void sort_lane_stage(double (&v)[8], int (&ix)[8], int l, int k) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e & J) continue;
+    const int p = 8 * l + e;
+    const bool desc = (p & k) == 0;
+    const bool b = beats(v[e], ix[e], v[e | J], ix[e | J]);
+    if (desc ? !b : b) {
+      const double tv = v[e]; const int ti = ix[e];
+      v[e] = v[e | J]; ix[e] = ix[e | J];
+      v[e | J] = tv; ix[e | J] = ti;
     }
-  } else {
-    bitonic_step<J, K>(v0, i0, lane);
-    bitonic_step<J, K>(v1, i1, lane + 64);
   }
-  if constexpr (J > 1) bitonic_merge<K, J / 2>(v0, i0, v1, i1, lane);
 }
 
-// Sort the 128 entries (position p = lane + 64*h) best first.
-template <int K = 128>
-__device__ __forceinline__ void bitonic_sort(double& v0, int& i0, double& v1, int& i1, int lane) {
-  if constexpr (K > 2) bitonic_sort<K / 2>(v0, i0, v1, i1, lane);
-  bitonic_merge<K, K / 2>(v0, i0, v1, i1, lane);
+template <int LD>   // lane distance
+__device__ __forceinline__ void sort_cross_stage(double (&v)[8], int (&ix)[8], int l, int k) {
+  const bool lower = (l & LD) == 0;
+  const bool desc = ((8 * l) & k) == 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const long long b = __double_as_longlong(v[e]);
+    const int plo = xor_lane<LD>((int)(b & 0xffffffffLL));
+    const int phi = xor_lane<LD>((int)(b >> 32));
+    const int pi = xor_lane<LD>(ix[e]);
+    const double pv = __longlong_as_double(((long long)phi << 32) | (unsigned)plo);
+    const bool mine = beats(v[e], ix[e], pv, pi);
+    if (!((lower == desc) ? mine : !mine)) {
+      v[e] = pv;
+      ix[e] = pi;
+    }
+  }
 }
+
+__device__ __forceinline__ void sort_rows4(double (&v)[8], int (&ix)[8], int l) {
+#pragma unroll
+  for (int k = 2; k <= 128; k <<= 1) {
+    if (k >= 128) sort_cross_stage<8>(v, ix, l, k);
+    if (k >= 64) sort_cross_stage<4>(v, ix, l, k);
+    if (k >= 32) sort_cross_stage<2>(v, ix, l, k);
+    if (k >= 16) sort_cross_stage<1>(v, ix, l, k);
+    if (k >= 8) sort_lane_stage<4>(v, ix, l, k);
+    if (k >= 4) sort_lane_stage<2>(v, ix, l, k);
+    sort_lane_stage<1>(v, ix, l, k);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
+
+// 16 zero bytes: the direct-load source of rows past the last key block
+__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
+
+constexpr int kCols = 32;   // key blocks per streamed chunk
+
+// LDS layouts of one chunk (rows are key blocks, no padding, so a wave's
+// 1 KB direct load fills whole rows); 16-byte chunks XOR-swizzled per row:
+//   k̄: D float64 per row (D/2 chunks), chunk c of row r at c ^ (r & 15):
+//       the 16 rows read at one head-dim index by an f64 MFMA hit 16
+//       different chunks;
+//   v̄: D float32 per row (D/4 chunks), chunk c of row r at c ^ 4*(r & 3):
+//       the four rows read together by the P·V MFMA start in different banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return r & (D / 2 - 1) & 15; }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return (4 * (r & 3)) & (D / 4 - 1); }
 
 template <int D>
 __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
   constexpr int KS = D / 4;    // f64 MFMA k-steps over the head dimension
   constexpr int DT = D / 16;   // 16-row tiles of O^T over the head dimension
-  __shared__ double Ks[64][D + 1];
-  __shared__ float Vs[64][D + 16];
-  __shared__ double BufV[64][kCap];
-  __shared__ int BufI[64][kCap];
+  constexpr int KROW = D * 8, VROW = D * 4;   // bytes per LDS row
+  constexpr int KLOADS = kCols * KROW / 1024 / 4, VLOADS = kCols * VROW / 1024 / 4;   // 1 KB loads per wave
+  static_assert(KLOADS >= 1 && VLOADS >= 1, "chunk split");
+  __shared__ __attribute__((aligned(16))) double Kb0[kCols * D];
+  __shared__ __attribute__((aligned(16))) float Vb0[kCols * D];
+  __shared__ __attribute__((aligned(16))) double Kb1[kCols * D];
+  __shared__ __attribute__((aligned(16))) float Vb1[kCols * D];
+  // candidate buffers, rows padded by 16 entries so that neighbouring rows
+  // start in different LDS bank halves (a row is 1 KB unpadded)
+  __shared__ double BufV[64][kCap + 16];
+  __shared__ int BufI[64][kCap + 16];
   __shared__ int Cnt[64];
   __shared__ double ThrV[64];
   __shared__ int ThrI[64];
@@ -123,8 +168,8 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
   const int brow = w * 16 + lr;   // this lane's row in the workgroup buffers
 
   const double* qb = a.qbar + (size_t)slice * m * D;
-  const double* kb = a.kbar + (size_t)slice * m * D;
-  const float* vb = a.vbar + (size_t)slice * m * D;
+  const char* kbytes = reinterpret_cast<const char*>(a.kbar + (size_t)slice * m * D);
+  const char* vbytes = reinterpret_cast<const char*>(a.vbar + (size_t)slice * m * D);
 
   if (threadIdx.x < 64) {
     Cnt[threadIdx.x] = 0;
@@ -140,6 +185,31 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
     for (int ks = 0; ks < KS; ++ks) qa[ks] = row < m ? qb[(size_t)row * D + 4 * ks + lg] : 0.0;
   }
 
+  // Direct global -> LDS loads of the kCols key blocks starting at c0: lane
+  // l of a 1 KB load writes bytes 16*l.. of that span, i.e. physical chunk
+  // (1024*g + 16*l) % ROW / 16 of row (1024*g + 16*l) / ROW, which holds the
+  // logical chunk given by the row's swizzle.
+  auto issue = [&](int c0, double* kb, float* vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int gg = 0; gg < KLOADS; ++gg) {
+      const int g = w + 4 * gg;
+      const int byte = 1024 * g + 16 * lane;
+      const int r = byte / KROW, pc = (byte % KROW) / 16;
+      const int lc = pc ^ kswz<D>(r);
+      const void* src = c0 + r < m ? (const void*)(kbytes + (size_t)(c0 + r) * KROW + 16 * lc) : (const void*)&kZero16;
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(reinterpret_cast<char*>(kb) + 1024 * g), 16, 0, 0);
+    }
+#pragma unroll
+    for (int gg = 0; gg < VLOADS; ++gg) {
+      const int g = w + 4 * gg;
+      const int byte = 1024 * g + 16 * lane;
+      const int r = byte / VROW, pc = (byte % VROW) / 16;
+      const int lc = pc ^ vswz<D>(r);
+      const void* src = c0 + r < m ? (const void*)(vbytes + (size_t)(c0 + r) * VROW + 16 * lc) : (const void*)&kZero16;
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(reinterpret_cast<char*>(vb) + 1024 * g), 16, 0, 0);
+    }
+  };
+
   floatx4 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -148,34 +218,74 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
   double thr_v = -INFINITY;   // current n-th best key of row lr
   int thr_i = 0x7fffffff;
 
-  for (int c0 = 0; c0 < m; c0 += 64) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * D / 2; idx += 256) {
-      const int key = idx / (D / 2), pr = idx % (D / 2);
-      double2 x = make_double2(0.0, 0.0);
-      if (c0 + key < m) x = *reinterpret_cast<const double2*>(kb + (size_t)(c0 + key) * D + 2 * pr);
-      Ks[key][2 * pr] = x.x;
-      Ks[key][2 * pr + 1] = x.y;
-    }
-    for (int idx = threadIdx.x; idx < 64 * D / 4; idx += 256) {
-      const int key = idx / (D / 4), qd = idx % (D / 4);
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + key < m) x = *reinterpret_cast<const float4*>(vb + (size_t)(c0 + key) * D + 4 * qd);
-      *reinterpret_cast<float4*>(&Vs[key][4 * qd]) = x;
-    }
-    __syncthreads();
-
-    // dot products: acc[ct][i] = q̄[row lr] · k̄[c0 + 16*ct + 4*i + lg]
-    doublex4 acc[4];
+  // Sort the buffers of rows R0 .. R0+3 (16 lanes each) and keep each row's
+  // best n; with final set, write them out in ascending block order instead.
+  auto compact4 = [&](int R0, bool final) __attribute__((always_inline)) {
+    const int R = R0 + lg, l = lr;
+    const int c = Cnt[R];
+    double v[8];
+    int ix[8];
+    // unsorted input, so any placement will do: read buffer entry 16*e + l
+    // into slot e of lane l (16 lanes read 16 consecutive entries)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = doublex4{0.0, 0.0, 0.0, 0.0};
+    for (int e = 0; e < 8; ++e) {
+      const int pos = 16 * e + l;
+      v[e] = pos < c ? BufV[R][pos] : -INFINITY;
+      ix[e] = pos < c ? BufI[R][pos] : 0x7fffffff;
+    }
+    sort_rows4(v, ix, l);   // now position 8*l + e holds the (8*l+e)-th best
+    if (!final) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = 8 * l + e;
+        if (pos < n) {
+          BufV[R][pos] = v[e];
+          BufI[R][pos] = ix[e];
+        }
+        if (pos == n - 1) {
+          ThrV[R] = v[e];
+          ThrI[R] = ix[e];
+          Cnt[R] = n;
+        }
+      }
+    } else {
+      // the best n, by block index: rank among the kept n through LDS
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (8 * l + e < n) BufI[R][8 * l + e] = ix[e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int row = tile * 64 + R;
+      if (row < m) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pos = 8 * l + e;
+          if (pos < n) {
+            int rank = 0;
+            for (int j = 0; j < n; ++j) rank += BufI[R][j] < ix[e] ? 1 : 0;
+            a.sel[((size_t)slice * m + row) * n + rank] = ix[e];
+          }
+        }
+      }
+    }
+  };
+
+  auto chunk = [&](int c0, const double* kb, const float* vb) __attribute__((always_inline)) {
+    // dot products: acc[ct][i] = q̄[row lr] · k̄[c0 + 16*ct + 4*i + lg]
+    doublex4 acc[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc[ct] = doublex4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ks[ct * 16 + lr][4 * ks + lg], qa[ks], acc[ct], 0, 0, 0);
+      for (int ct = 0; ct < 2; ++ct) {
+        const int r = ct * 16 + lr, k = 4 * ks + lg;   // A operand k̄[r][k]
+        const double kv = kb[r * D + 2 * ((k >> 1) ^ kswz<D>(r)) + (k & 1)];
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qa[ks], acc[ct], 0, 0, 0);
+      }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (c0 + 16 * ct + 4 * i + lg >= m) acc[ct][i] = -INFINITY;
@@ -183,7 +293,7 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
     // online softmax of row lr and O^T += V̄^T P^T
     double cmax = acc[0][0];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) cmax = fmax(cmax, acc[ct][i]);
     cmax = fmax(cmax, __shfl_xor(cmax, 16));
@@ -194,63 +304,87 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = __builtin_amdgcn_exp2f((float)((acc[ct][i] - m_new) * a.c_exp2));
         l_run += p;
+        const int r = 16 * ct + 4 * i + lg;   // B operand v̄[r][16*dt + lr]
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Vs[16 * ct + 4 * i + lg][dt * 16 + lr], p, oacc[dt], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt) {
+          const int col = dt * 16 + lr;
+          const float vv = vb[r * D + 4 * ((col >> 2) ^ vswz<D>(r)) + (col & 3)];
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, p, oacc[dt], 0, 0, 0);
+        }
       }
     m_run = m_new;
 
-    // selection: append the logits that beat the row's current n-th key
+    // selection: append the logits that beat the row's current n-th key.
+    // The four lanes of a row (lanes lr, lr+16, lr+32, lr+48) take
+    // consecutive slots by a prefix count, so no atomics are needed.
+    unsigned cm = 0;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = c0 + 16 * ct + 4 * i + lg;
-        const bool cand = col < m && beats(acc[ct][i], col, thr_v, thr_i);
-        if (__ballot(cand)) {
-          if (cand) {
-            const int pos = atomicAdd(&Cnt[brow], 1);
-            BufV[brow][pos] = acc[ct][i];
-            BufI[brow][pos] = col;
-          }
-        }
+        if (col < m && beats(acc[ct][i], col, thr_v, thr_i)) cm |= 1u << (4 * ct + i);
       }
+    if (__ballot(cm != 0)) {
+      const int mine = __popc(cm);
+      const int up16 = __shfl_xor(mine, 16);
+      const int up32 = __shfl_xor(mine, 32);
+      const int up48 = __shfl_xor(up16, 32);
+      // counts of lane groups 0..3 of this row, in group order
+      const int c_g0 = lg == 0 ? mine : (lg == 1 ? up16 : (lg == 2 ? up32 : up48));
+      const int c_g1 = lg == 1 ? mine : (lg == 0 ? up16 : (lg == 3 ? up32 : up48));
+      const int c_g2 = lg == 2 ? mine : (lg == 3 ? up16 : (lg == 0 ? up32 : up48));
+      const int c_g3 = lg == 3 ? mine : (lg == 2 ? up16 : (lg == 1 ? up32 : up48));
+      int pos = Cnt[brow] + (lg > 0 ? c_g0 : 0) + (lg > 1 ? c_g1 : 0) + (lg > 2 ? c_g2 : 0);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (cm & (1u << (4 * ct + i))) {
+            BufV[brow][pos] = acc[ct][i];
+            BufI[brow][pos] = c0 + 16 * ct + 4 * i + lg;
+            ++pos;
+          }
+      __builtin_amdgcn_wave_barrier();
+      if (lg == 0) Cnt[brow] += c_g0 + c_g1 + c_g2 + c_g3;
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // compact rows whose buffer passed 64 entries (the next chunk adds <= 64)
-    for (int r = 0; r < 16; ++r) {
-      const int R = w * 16 + r;
-      const int c = Cnt[R];
-      if (c <= 64) continue;
-      double v0 = lane < c ? BufV[R][lane] : -INFINITY;
-      int i0 = lane < c ? BufI[R][lane] : 0x7fffffff;
-      double v1 = lane + 64 < c ? BufV[R][lane + 64] : -INFINITY;
-      int i1 = lane + 64 < c ? BufI[R][lane + 64] : 0x7fffffff;
-      bitonic_sort(v0, i0, v1, i1, lane);
-      const double tv = __shfl(v0, n - 1);
-      const int ti = __shfl(i0, n - 1);
-      if (lane < n) {
-        BufV[R][lane] = v0;
-        BufI[R][lane] = i0;
-      }
-      if (lane == 0) {
-        ThrV[R] = tv;
-        ThrI[R] = ti;
-        Cnt[R] = n;
-      }
-    }
+    // compact rows whose buffer passed kCap - kCols entries (the next chunk
+    // adds at most kCols): one read of the wave's 16 counts, a ballot, then
+    // each group of four rows holding such a row is sorted together
+    const unsigned long long full = __ballot(lane < 16 && Cnt[w * 16 + (lane & 15)] > kCap - kCols);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if ((full >> (4 * q)) & 0xF) compact4(w * 16 + 4 * q, false);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     thr_v = ThrV[brow];
     thr_i = ThrI[brow];
+  };
+
+  // double-buffered stream over the key blocks
+  issue(0, Kb0, Vb0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  for (int c0 = 0; c0 < m; c0 += 2 * kCols) {
+    if (c0 + kCols < m) issue(c0 + kCols, Kb1, Vb1);
+    chunk(c0, Kb0, Vb0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (c0 + kCols >= m) break;
+    if (c0 + 2 * kCols < m) issue(c0 + 2 * kCols, Kb0, Vb0);
+    chunk(c0 + kCols, Kb1, Vb1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   }
 
   // o_CG = O / l; lane l holds rows lr, head-dim entries dt*16 + 4*lg + i
@@ -266,19 +400,12 @@ __global__ __launch_bounds__(256) void compress_select_kernel(CSArgs a) {
   }
 
   // final top-n of every row, written in ascending block order
-  for (int r = 0; r < 16; ++r) {
-    if (rw + r >= m) break;
-    const int R = w * 16 + r;
-    const int c = Cnt[R];
-    double v0 = lane < c ? BufV[R][lane] : -INFINITY;
-    int i0 = lane < c ? BufI[R][lane] : 0x7fffffff;
-    double v1 = lane + 64 < c ? BufV[R][lane + 64] : -INFINITY;
-    int i1 = lane + 64 < c ? BufI[R][lane + 64] : 0x7fffffff;
-    bitonic_sort(v0, i0, v1, i1, lane);
-    int rank = 0;
-    for (int j = 0; j < n; ++j) rank += __shfl(i0, j) < i0 ? 1 : 0;
-    if (lane < n) a.sel[((size_t)slice * m + rw + r) * n + rank] = i0;
-  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (rw + 4 * q < m) compact4(w * 16 + 4 * q, true);
 }
 
 }  // namespace
