@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 from spherical_block_sparse_amd import CONFIGS, BSAConfig, make_inputs  # noqa: E402
 from spherical_block_sparse_amd import _lib  # noqa: E402
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP64_TFLOPS = 78.6
 PEAK_HBM_GBS = 8000.0
@@ -62,6 +64,21 @@ def pool_bytes(cfg: BSAConfig) -> float:
     e_in = cfg.slices * cfg.n_tokens * cfg.head_dim
     e_out = cfg.slices * cfg.n_blocks * cfg.head_dim
     return 3.0 * e_in * 2 + e_out * (8 + 8 + 4)
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (copy-calibrated), or None when they are
+    missing or the kernel source has changed since they were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_JSON))[key]
+        src = os.path.join(ROOT, rec["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["hbm_bytes"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def time_stream(fn, steps: int) -> float:
@@ -222,14 +239,16 @@ def main() -> int:
         "roofline": {
             "bound": "mfma", "kernel": "bsa_fine (fine_kernel<64>)",
             "achieved": r["fine_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": r["fine_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+            "frac": r["fine_tflops"] / PEAK_BF16_TFLOPS, "traffic": measured_traffic(f"fine_{c.name}"),
             "flops_per_launch": r["fine_flops"], "ms_per_launch": r["fine_ms"],
         },
         "kernels": {
             "pool": {"ms": r["pool_ms"], "bound": "hbm", "achieved_GBs": r["pool_gbs"],
-                     "frac": r["pool_gbs"] / PEAK_HBM_GBS, "bytes_per_launch": r["pool_bytes"]},
+                     "frac": r["pool_gbs"] / PEAK_HBM_GBS, "bytes_per_launch": r["pool_bytes"],
+                     "traffic": measured_traffic(f"pool_{c.name}")},
             "compress_select": {"ms": r["cs_ms"], "bound": "fp64 matrix",
-                                "achieved_TFLOPs": r["cs_tflops"], "frac_fp64_peak": r["cs_tflops"] / PEAK_FP64_TFLOPS},
+                                "achieved_TFLOPs": r["cs_tflops"], "frac_fp64_peak": r["cs_tflops"] / PEAK_FP64_TFLOPS,
+                                "traffic": measured_traffic(f"select_{c.name}")},
             "fine": {"ms": r["fine_ms"], "frac_bf16_peak": r["fine_tflops"] / PEAK_BF16_TFLOPS},
             "stages_match_forward": r["stages_match_forward"],
         },

@@ -1,0 +1,62 @@
+"""Run one BSA stage (or a plain copy) a few times, for rocprofv3 passes.
+
+    python -m spherical_block_sparse_amd.profile_run --config ns128 --stage fine --reps 2
+    python -m spherical_block_sparse_amd.profile_run --copy-mib 4096 --reps 2
+
+--stage pool | select | fine | forward runs that entry point `reps` times on
+the workload's synthetic inputs (the earlier stages run once beforehand to
+produce their inputs).  --copy-mib N copies an N MiB buffer with torch's
+elementwise copy kernel `reps` times: N MiB read and N MiB written per call,
+the calibration of the FETCH_SIZE / WRITE_SIZE counters.
+"""
+
+from __future__ import annotations
+
+import argparse
+import sys
+
+import torch
+
+from . import CONFIGS, make_inputs
+from . import _lib
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", default="ns128", choices=sorted(CONFIGS))
+    ap.add_argument("--stage", default="fine", choices=["pool", "select", "fine", "forward"])
+    ap.add_argument("--reps", type=int, default=2)
+    ap.add_argument("--copy-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {args.copy_mib} MiB x {args.reps}", flush=True)
+        return 0
+
+    cfg = CONFIGS[args.config]
+    q, k, v, g = make_inputs(cfg, device="cuda", dtype=torch.bfloat16)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
+    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        if args.stage == "pool":
+            _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar)
+        elif args.stage == "select":
+            _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel)
+        elif args.stage == "fine":
+            _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window)
+        else:
+            _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    torch.cuda.synchronize()
+    print(f"{args.stage} {cfg.name} x {args.reps} done", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
