@@ -37,10 +37,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmosaic_bsa)")
 
 
-# per-source extra flags: the fine-attention kernel never relies on NaN
+# per-source extra flags: the fine-attention and selection kernels never rely on NaN
 # semantics (masked scores are -inf, which stays honoured), and without this
 # every fmaxf of an MFMA result is preceded by a NaN-quieting instruction
-EXTRA = {"bsa_fine.hip": ["-fno-honor-nans"]}
+EXTRA = {"bsa_fine.hip": ["-fno-honor-nans"], "bsa_compress_select.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -81,6 +81,46 @@ def test_compress_select_stage(name):
     log(f"    indices: {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
 
 
+def _check_compress_select(cfg, q, k, v, topn=None):
+    topn = topn or cfg.topn
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
+    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, topn)
+    torch.cuda.synchronize()
+    near = 0
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            ref = selection_ref(_slice(q, b, h), _slice(k, b, h), _slice(v, b, h), cfg.block, topn)
+            near += check_indices(sel[b, h].cpu().numpy(), ref, topn)["near_ties"]
+            np.testing.assert_allclose(o_cg[b, h].cpu().numpy(), ref["o_cg"], rtol=0, atol=2e-5)
+    return near
+
+
+def test_compress_select_rows_crowded_into_one_lane_group():
+    """Key blocks j = 0 mod 4 carry a large common direction u, and the query
+    blocks i = 0 mod 3 carry it too: those rows' whole top-16 sits in blocks
+    congruent mod 4, i.e. in the share of the keys one lane of the selection
+    sees, so that lane's list must hold all of them."""
+    cfg = CONFIGS["ns32"]
+    q, k, v, _ = _gpu_inputs(cfg)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    u = torch.randn(cfg.head_dim, generator=gen, dtype=torch.float64)
+    u = (3.0 * u / u.norm()).to(DEV)
+    B, m = cfg.block, cfg.n_blocks
+    kb = (torch.arange(cfg.n_tokens, device=DEV) // B) % 4 == 0
+    qb = (torch.arange(cfg.n_tokens, device=DEV) // B) % 3 == 0
+    k = (k.double() + kb[:, None] * u).bfloat16()
+    q = (q.double() + qb[:, None] * u).bfloat16()
+    near = _check_compress_select(cfg, q, k, v)
+    log(f"    {cfg.slices * m} rows ({cfg.slices * ((m + 2) // 3)} crowded), {near} near-tie rows")
+
+
+@pytest.mark.parametrize("topn", [17, 32, 64])
+def test_compress_select_topn_above_sixteen(topn):
+    cfg = CONFIGS["ns32"]
+    q, k, v, _ = _gpu_inputs(cfg)
+    _check_compress_select(cfg, q, k, v, topn=topn)
+
+
 @pytest.mark.parametrize("name", ["tiny", "ns32"])
 def test_fine_stage_branches_one_hot(name):
     """mosaic_bsa_fine with one-hot gates isolates o_CG, o_FG and o_L."""
