@@ -75,7 +75,13 @@ struct FineArgs {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-constexpr float kLazy = 8.0f;   // rescale only when the scaled max grows by > 8 (a factor 2^8)
+// word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format,
+// no swizzle, stride 0 (offsets are plain byte offsets, range-checked
+// against the record count)
+constexpr int kRsrcWord3 = 0x00020000;
+
+constexpr float kLazy = 8.0f;
+
 
 // transposing 8-byte LDS read (ds_read_b64_tr_b16)
 __device__ __forceinline__ shortx4 lds_read_tr16(const uint16_t* p) {
@@ -261,6 +267,60 @@ __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void global_void;
 
+// Direct loads into LDS (lane l's 16 bytes land at M0 + 16*l), written as
+// inline assembly so that the compiler does not track them: it would
+// otherwise make every transposing LDS read wait for all loads in flight
+// (it cannot tell which buffer those reads touch), which serialises the
+// prefetch of the next chunk with the current one.  The loads have no
+// register results; their completion is awaited explicitly (s_waitcnt
+// vmcnt, then a barrier) before a buffer is read.  M0 is restored.
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of p as a scalar (the asm operands below must be SGPRs;
+// every caller passes a workgroup-uniform address)
+__device__ __forceinline__ int lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((int)(unsigned)(uintptr_t)(lds_void*)p);
+}
+
+__device__ __forceinline__ void dma_buffer(const void* lds, int voff, int32x4 rsrc, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
+}
+
+__device__ __forceinline__ void dma_global(const void* lds, const void* src) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds)), "v"(src)
+      : "memory");
+}
+
+// buffer resource of one slice's tensor: base, stride 0, byte range, word 3
+__device__ __forceinline__ int32x4 slice_rsrc(const void* base, int bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  int32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffull));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffull));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (lgkm and exp counters not waited on)
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
+
 template <int D, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void fine_kernel(FineArgs a) {
   constexpr int KK = Tile<D>::KK, DT = Tile<D>::DT;
@@ -319,6 +379,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   const int whi = (int)min((long long)N, (long long)t0 + T - 1 + hi_off);
   const int c_all = c_sel + (whi - wlo + 63) / 64;
   const int blk0 = t0 / B;
+  const int lb = 31 - __builtin_clz(B);   // block = 2^lb
   {
     // the selection rows of this tile's query blocks, clamped so that a bad
     // index can never address outside the slice
@@ -355,28 +416,35 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     lane_row[gg] = RPG * grp + lane / CPR;
     lane_off[gg] = lane_row[gg] * D + 8 * ((lane % CPR) ^ swz<D>(lane_row[gg]));
   }
+  // Whole chunks go through buffer loads of the slice's K and V: the
+  // per-lane byte offsets are fixed registers and the chunk start is a
+  // scalar offset, so issuing a chunk costs no vector instructions.  Byte
+  // offsets are 32-bit, hence only for slices under 2 GiB.
+  const bool use_rsrc = (long long)N * D * 2 < 0x7fffffffLL;
+  const int slice_bytes = use_rsrc ? N * D * 2 : 0;
+  const int32x4 rk = slice_rsrc(ks, slice_bytes);
+  const int32x4 rv = slice_rsrc(vs, slice_bytes);
   auto issue_rows = [&](int tok0, int valid, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
+    if (valid >= 64 && use_rsrc) {   // whole chunk of consecutive tokens: no per-lane checks
+      const int soff = __builtin_amdgcn_readfirstlane(tok0 * (D * 2));   // uniform by construction
+#pragma unroll
+      for (int gg = 0; gg < LPW; ++gg) {
+        const int grp = w + WAVES * gg;
+        const int off = 2 * lane_off[gg];
+        dma_buffer(kb + grp * 512, off, rk, soff);
+        dma_buffer(vb + grp * 512, off, rv, soff);
+      }
+      return;
+    }
     const char* kbase = reinterpret_cast<const char*>(ks + (size_t)tok0 * D);   // uniform
     const char* vbase = reinterpret_cast<const char*>(vs + (size_t)tok0 * D);
-    if (valid >= 64) {   // whole chunk of consecutive tokens: no per-lane checks
 #pragma unroll
-      for (int gg = 0; gg < LPW; ++gg) {
-        const int grp = w + WAVES * gg;
-        const unsigned off = 2u * (unsigned)lane_off[gg];
-        __builtin_amdgcn_global_load_lds((global_void*)(kbase + off), (lds_void*)(kb + grp * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((global_void*)(vbase + off), (lds_void*)(vb + grp * 512), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int gg = 0; gg < LPW; ++gg) {
-        const int grp = w + WAVES * gg;
-        const bool ok = lane_row[gg] < valid;
-        const unsigned off = 2u * (unsigned)lane_off[gg];
-        const void* ksrc = ok ? (const void*)(kbase + off) : (const void*)&kZero16;
-        const void* vsrc = ok ? (const void*)(vbase + off) : (const void*)&kZero16;
-        __builtin_amdgcn_global_load_lds((global_void*)ksrc, (lds_void*)(kb + grp * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((global_void*)vsrc, (lds_void*)(vb + grp * 512), 16, 0, 0);
-      }
+    for (int gg = 0; gg < LPW; ++gg) {
+      const int grp = w + WAVES * gg;
+      const bool ok = lane_row[gg] < valid;
+      const unsigned off = 2u * (unsigned)lane_off[gg];
+      dma_global(kb + grp * 512, ok ? (const void*)(kbase + off) : (const void*)&kZero16);
+      dma_global(vb + grp * 512, ok ? (const void*)(vbase + off) : (const void*)&kZero16);
     }
   };
   auto issue_gather = [&](int ci, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
@@ -386,20 +454,17 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       const int row = lane_row[gg];
       const int lc = (lane % CPR) ^ swz<D>(row);
       const int tok = token_of(ci, row);
-      const void* ksrc = tok >= 0 ? (const void*)(ks + (size_t)tok * D + 8 * lc) : (const void*)&kZero16;
-      const void* vsrc = tok >= 0 ? (const void*)(vs + (size_t)tok * D + 8 * lc) : (const void*)&kZero16;
-      __builtin_amdgcn_global_load_lds((global_void*)ksrc, (lds_void*)(kb + grp * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void*)vsrc, (lds_void*)(vb + grp * 512), 16, 0, 0);
+      dma_global(kb + grp * 512, tok >= 0 ? (const void*)(ks + (size_t)tok * D + 8 * lc) : (const void*)&kZero16);
+      dma_global(vb + grp * 512, tok >= 0 ? (const void*)(vs + (size_t)tok * D + 8 * lc) : (const void*)&kZero16);
     }
   };
   auto issue = [&](int ci, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
     if (ci >= c_sel) {
       const int u0 = wlo + (ci - c_sel) * 64;
       issue_rows(u0, whi - u0, kb, vb);
-    } else if (B >= 64) {
-      const int gi = ci / cpg;
-      const int vk0 = (ci - gi * cpg) * 64;   // a multiple of 64 inside one key block
-      issue_rows(SelT[gi * n + vk0 / B] * B + vk0 % B, nB - vk0, kb, vb);
+    } else if (B >= 64) {   // one group: 128-query tiles only come with blocks of >= 128
+      const int vk0 = ci * 64;   // a multiple of 64 inside one key block
+      issue_rows((SelT[vk0 >> lb] << lb) + (vk0 & (B - 1)), nB - vk0, kb, vb);
     } else {
       issue_gather(ci, kb, vb);
     }
@@ -429,12 +494,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
 
   const float lazy_raw = kLazy / c;
   auto step_selected = [&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
-    const int gi = ci / cpg;
-    const int vc0 = (ci - gi * cpg) * 64;
-    if (B >= T && nB - vc0 >= 64) {
+    if (B >= T && nB - ci * 64 >= 64) {   // one group: chunk ci starts at virtual key 64*ci
       attend_full<D>(kb, vb, qf, br, c, lazy_raw);
       return;
     }
+    const int gi = groups == 1 ? 0 : ci / cpg;
+    const int vc0 = (ci - gi * cpg) * 64;
     bool act[2], msk[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -471,17 +536,17 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   auto run = [&](int c0, int c1, auto step) __attribute__((always_inline)) {
     if (c0 >= c1) return;
     issue(c0, Kb0, Vb0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     for (int ci = c0; ci < c1; ci += 2) {
       if (ci + 1 < c1) issue(ci + 1, Kb1, Vb1);
       step(ci, Kb0, Vb0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
       __syncthreads();
       if (ci + 1 >= c1) break;
       if (ci + 2 < c1) issue(ci + 2, Kb0, Vb0);
       step(ci + 1, Kb1, Vb1);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
       __syncthreads();
     }
   };
