@@ -572,9 +572,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   }
 }
 
+// One workgroup per tile of 32*WAVES queries of every slice: the tile size
+// fixes the tile count and the grid together.
 template <int D, int WAVES>
-hipError_t launch(FineArgs a, hipStream_t stream) {
+hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
   a.tiles = a.n_tok / (32 * WAVES);
+  a.groups = slices * a.tiles;
   dim3 grid((unsigned)a.groups);
   hipLaunchKernelGGL((fine_kernel<D, WAVES>), grid, dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
@@ -600,11 +603,11 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.window = window;
   a.m = n_tok / block;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
-  // 128-query tiles when a block holds >= 128 tokens (N is then a multiple of 128)
+  // 128-query tiles when a block holds >= 128 tokens (N is then a multiple of
+  // 128), else 64 (N = 12*nside^2 with nside^2 >= block >= 16 is a multiple of 64)
   const bool wide = block >= 128 && n_tok % 128 == 0;
-  a.groups = slices * (n_tok / (wide ? 128 : 64));
-  if (head_dim == 64) return wide ? launch<64, 4>(a, stream) : launch<64, 2>(a, stream);
-  return wide ? launch<32, 4>(a, stream) : launch<32, 2>(a, stream);
+  if (head_dim == 64) return wide ? launch<64, 4>(a, slices, stream) : launch<64, 2>(a, slices, stream);
+  return wide ? launch<32, 4>(a, slices, stream) : launch<32, 2>(a, slices, stream);
 }
 
 }  // namespace mosaic

@@ -279,6 +279,11 @@ def test_edge_block_256_ragged_chunks():
     _edge(BSAConfig("n16-b256", 16, 1, 2, 64, 256, 3, 100, "iid", 16))
 
 
+def test_edge_head_dim_32_block_256():
+    # 128-query tiles with head_dim 32
+    _edge(BSAConfig("n16-b256-d32", 16, 1, 2, 32, 256, 3, 100, "iid", 17))
+
+
 def test_edge_block_64_small_m():
     # nside 8 with block 64: m = 12 (< one 64-row tile), window > N/2
     _edge(BSAConfig("n8-b64", 8, 2, 2, 32, 64, 5, 500, "iid", 9))
