@@ -14,7 +14,8 @@
 //   * logits transposed, S^T = K̄ Q̄^T, with v_mfma_f64_16x16x4_f64 on the
 //     exact float64 block means: in that layout lane l owns 8 logits of row
 //     l%16 per chunk (the keys congruent to l/16 mod 4), which is also the B
-//     operand layout of O^T += V̄^T P^T (v_mfma_f32_16x16x4_f32), so the
+//     operand layout of O^T += V̄^T P^T (v_mfma_f32_16x16x32_bf16 on
+//     bf16-rounded weights and v̄, with its k-slots permuted to match), so the
 //     online softmax needs no LDS round trip and only two cross-lane steps.
 //   * ranking uses the float64 dot products themselves (dividing by sqrt(d)
 //     is monotone), so the selection equals a float64 evaluation up to the
@@ -36,9 +37,9 @@
 //     candidate buffer at prefix-count slots, and a buffer that could
 //     overflow is compacted to its best n by a 128-entry bitonic network over
 //     four rows at once (register and DPP / swizzle exchanges).
-// Roofline: float64 matrix work 2*m^2*d per slice for the logits plus
-// float32 matrix work 2*m^2*d for ā·v̄; HBM traffic is only the pooled
-// tensors, o_CG and the indices.
+// Roofline: float64 matrix work 2*m^2*d per slice for the logits plus bf16
+// matrix work 2*m^2*d for ā·v̄; HBM traffic is only the pooled tensors, o_CG
+// and the indices.
 #include "bsa_common.h"
 
 #include <math.h>
@@ -201,6 +202,12 @@ __device__ __forceinline__ void chunk_logits(doublex4 (&acc)[2], const double* k
 
 // Online softmax of row lr over one chunk and O^T += V̄^T P^T.  m_run is the
 // running maximum dot product, l_run this lane's part of the denominator.
+// The weights are rounded to bf16 and multiply bf16-rounded v̄ in one
+// v_mfma_f32_16x16x32_bf16 per 16 head-dim rows: k-slot 8*g + e of that
+// product holds key 16*(e/4) + 4*(e%4) + g, which is exactly the key whose
+// logit lane lr + 16*g holds in acc[e/4][e%4], so the weights need no
+// exchange between lanes.  The denominator adds the rounded weights, so o_CG
+// is an exact convex combination of the v̄ rows as the product sees them.
 template <int D>
 __device__ __forceinline__ void chunk_softmax_pv(const doublex4 (&acc)[2], const float* vb, double c_exp2,
                                                  double& m_run, float& l_run, floatx4 (&oacc)[D / 16],
@@ -220,20 +227,23 @@ __device__ __forceinline__ void chunk_softmax_pv(const doublex4 (&acc)[2], const
     for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
   }
   const double nmc = -m_new * c_exp2;
+  bf16x8 pb;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int e = 0; e < 8; ++e) {
+    pb[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f((float)fma(acc[e / 4][e % 4], c_exp2, nmc)));
+    l_run += static_cast<float>(pb[e]);
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f((float)fma(acc[ct][i], c_exp2, nmc));
-      l_run += p;
-      const int r = 16 * ct + 4 * i + lg;   // B operand v̄[r][16*dt + lr]
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int col = dt * 16 + lr;   // A operand v̄^T[col][slot 8*lg + e]
+    bf16x8 va;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const int col = dt * 16 + lr;
-        const float vv = vb[r * D + 4 * ((col >> 2) ^ vswz<D>(r)) + (col & 3)];
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, p, oacc[dt], 0, 0, 0);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int r = 16 * (e / 4) + 4 * (e % 4) + lg;
+      va[e] = static_cast<__bf16>(vb[r * D + 4 * ((col >> 2) ^ vswz<D>(r)) + (col & 3)]);
     }
+    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
+  }
   m_run = m_new;
 }
 

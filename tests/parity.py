@@ -35,6 +35,15 @@ def selection_ref(q, k, v, block, topn):
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, s=s, o_cg=o_cg, idx=idx, gap=gap)
 
 
+def ocg_tolerance(vbar: np.ndarray) -> float:
+    """Bound on |o_CG(gpu) - o_CG(oracle)| elementwise.  The kernel rounds the
+    softmax weights and v̄ to bf16 (relative error <= 2^-9 each) and sums the
+    rounded weights for the denominator: the normalised weights then err by
+    at most 2 * 2^-9 relative and sum to one, so o_CG errs by at most
+    (2 + 1) * 2^-9 * max|v̄|, plus float32 accumulation."""
+    return 3.0 * 2.0 ** -9 * float(np.abs(vbar).max()) + 2e-5
+
+
 def check_indices(gpu_idx: np.ndarray, ref: dict, topn: int) -> dict:
     """Bit-exact on non-near-tie rows; top-n-within-slack on near-tie rows."""
     idx, gap, s = ref["idx"], ref["gap"], ref["s"]

@@ -18,7 +18,7 @@ from spherical_block_sparse_amd import CONFIGS, BSAConfig, make_inputs
 from spherical_block_sparse_amd import _lib
 from spherical_block_sparse_amd.synth import to_f64
 
-from parity import assert_close, check_indices, log, selection_ref
+from parity import assert_close, check_indices, log, ocg_tolerance, selection_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,7 @@ def test_compress_select_stage(name):
         for h in range(cfg.heads):
             ref = selection_ref(_slice(q, b, h), _slice(k, b, h), _slice(v, b, h), cfg.block, cfg.topn)
             near += check_indices(sel[b, h].cpu().numpy(), ref, cfg.topn)["near_ties"]
-            np.testing.assert_allclose(o_cg[b, h].cpu().numpy(), ref["o_cg"], rtol=0, atol=2e-5)
+            np.testing.assert_allclose(o_cg[b, h].cpu().numpy(), ref["o_cg"], rtol=0, atol=ocg_tolerance(ref["vbar"]))
     log(f"    indices: {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
 
 
@@ -91,7 +91,7 @@ def _check_compress_select(cfg, q, k, v, topn=None):
         for h in range(cfg.heads):
             ref = selection_ref(_slice(q, b, h), _slice(k, b, h), _slice(v, b, h), cfg.block, topn)
             near += check_indices(sel[b, h].cpu().numpy(), ref, topn)["near_ties"]
-            np.testing.assert_allclose(o_cg[b, h].cpu().numpy(), ref["o_cg"], rtol=0, atol=2e-5)
+            np.testing.assert_allclose(o_cg[b, h].cpu().numpy(), ref["o_cg"], rtol=0, atol=ocg_tolerance(ref["vbar"]))
     return near
 
 
