@@ -57,7 +57,14 @@ def fine_flops(cfg: BSAConfig) -> float:
 
 def compress_flops(cfg: BSAConfig) -> float:
     m, d = cfg.n_blocks, cfg.head_dim
-    return 4.0 * m * m * d * cfg.slices          # logits (float64) + ā·v̄ (float32)
+    return 4.0 * m * m * d * cfg.slices          # logits (float64) + ā·v̄ (bf16)
+
+
+def compress_bound_ms(cfg: BSAConfig) -> float:
+    """Matrix-core time of one compress+select launch at the published peaks:
+    2*m^2*d float64 FLOPs of logits plus 2*m^2*d bf16 FLOPs of ā·v̄ per slice."""
+    half = 2.0 * cfg.n_blocks ** 2 * cfg.head_dim * cfg.slices
+    return (half / (PEAK_FP64_TFLOPS * 1e12) + half / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
 
 
 def pool_bytes(cfg: BSAConfig) -> float:
@@ -211,6 +218,7 @@ def main() -> int:
             "workload": s["cfg"].name, "value": s["tokens_per_s"], "unit": "tokens/s", "ms_per_step": s["ms"],
             "kernels_ms": {"pool": s["pool_ms"], "compress_select": s["cs_ms"], "fine": s["fine_ms"]},
             "fine_mfma_frac": s["fine_tflops"] / PEAK_BF16_TFLOPS,
+            "compress_select_frac": compress_bound_ms(s["cfg"]) / s["cs_ms"],
             "pool_hbm_frac": s["pool_gbs"] / PEAK_HBM_GBS,
         }
 
@@ -246,8 +254,9 @@ def main() -> int:
             "pool": {"ms": r["pool_ms"], "bound": "hbm", "achieved_GBs": r["pool_gbs"],
                      "frac": r["pool_gbs"] / PEAK_HBM_GBS, "bytes_per_launch": r["pool_bytes"],
                      "traffic": measured_traffic(f"pool_{c.name}")},
-            "compress_select": {"ms": r["cs_ms"], "bound": "fp64 matrix",
-                                "achieved_TFLOPs": r["cs_tflops"], "frac_fp64_peak": r["cs_tflops"] / PEAK_FP64_TFLOPS,
+            "compress_select": {"ms": r["cs_ms"], "bound": "fp64 + bf16 matrix",
+                                "bound_ms": compress_bound_ms(c), "frac": compress_bound_ms(c) / r["cs_ms"],
+                                "achieved_TFLOPs": r["cs_tflops"],
                                 "traffic": measured_traffic(f"select_{c.name}")},
             "fine": {"ms": r["fine_ms"], "frac_bf16_peak": r["fine_tflops"] / PEAK_BF16_TFLOPS},
             "stages_match_forward": r["stages_match_forward"],

@@ -179,13 +179,16 @@ __device__ __forceinline__ void qk_chunk(const uint16_t* Ks, const bf16x8 (&qf)[
 // Online-softmax update of the sub-tiles in `act` from raw scores acc (the
 // scale c = log2(e)/sqrt(d) is applied inside the exp2 argument).  The
 // reference max moves only when a score exceeds it by more than 2^8 after
-// scaling; that decision is taken for the whole wave, so it is a scalar
-// branch (any lane may move its reference: alpha <= 1 is always exact).
+// scaling.  Each lane checks its own 16 scores of a query against the
+// query's reference and the wave votes, so the common case needs no
+// exchange between lanes; only when some score grew does the wave form the
+// queries' maxima across their four lanes and rescale (a scalar branch; any
+// query may move its reference: alpha <= 1 is always exact).
 template <int D, bool ALL>
 __device__ __forceinline__ void softmax_chunk(floatx4 (&acc)[2][4], Branch<D> (&br)[2], bf16x8 (&pb)[2][2],
                                               const bool (&act)[2], float c, float lazy_raw) {
   constexpr int DT = Tile<D>::DT;
-  float mx[2];
+  float mx[2];   // this lane's maximum of each sub-tile's scores
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     float a = fmaxf(acc[s][0][0], acc[s][0][1]);
@@ -193,8 +196,7 @@ __device__ __forceinline__ void softmax_chunk(floatx4 (&acc)[2][4], Branch<D> (&
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = (kt == 0 ? 2 : 0); i < 4; i += 2) a = fmaxf(a, fmaxf(acc[s][kt][i], acc[s][kt][i + 1]));
-    a = fmaxf(a, __shfl_xor(a, 16));
-    mx[s] = fmaxf(a, __shfl_xor(a, 32));
+    mx[s] = a;
   }
   const bool grow = (ALL || act[0]) && mx[0] > br[0].m + lazy_raw;
   const bool grow1 = (ALL || act[1]) && mx[1] > br[1].m + lazy_raw;
@@ -202,7 +204,9 @@ __device__ __forceinline__ void softmax_chunk(floatx4 (&acc)[2][4], Branch<D> (&
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (!(ALL || act[s])) continue;
-      const float mnew = fmaxf(br[s].m, mx[s]);
+      float row = fmaxf(mx[s], __shfl_xor(mx[s], 16));
+      row = fmaxf(row, __shfl_xor(row, 32));
+      const float mnew = fmaxf(br[s].m, row);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((br[s].m - mnew) * c);
       br[s].m = mnew;
       br[s].l *= alpha;
@@ -222,15 +226,28 @@ __device__ __forceinline__ void softmax_chunk(floatx4 (&acc)[2][4], Branch<D> (&
   }
 }
 
-// One staged 64-key chunk, every key valid for both sub-tiles (the common case).
-template <int D>
+// One staged 64-key chunk in which both sub-tiles take part (the common
+// case).  With MASK, chunk key kappa is valid for this lane's query of
+// sub-tile s iff lo[s] <= kappa < lo[s] + span[s] (span >= 0); otherwise
+// every key is valid.
+template <int D, bool MASK>
 __device__ __forceinline__ void attend_full(const uint16_t* Ks, const uint16_t* Vs,
                                             const bf16x8 (&qf)[2][Tile<D>::KK], Branch<D> (&br)[2],
-                                            float c, float lazy_raw) {
+                                            float c, float lazy_raw, const int (&lo)[2], const int (&span)[2]) {
   const bool act[2] = {true, true};
   floatx4 acc[2][4];
   bf16x8 pb[2][2];
   qk_chunk<D, true>(Ks, qf, acc, act);
+  if constexpr (MASK) {
+    const int lg = (threadIdx.x % kWave) / 16;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((unsigned)(16 * kt + 4 * lg + i - lo[s]) >= (unsigned)span[s]) acc[s][kt][i] = -INFINITY;
+  }
   softmax_chunk<D, true>(acc, br, pb, act, c, lazy_raw);
   pv_chunk<D, true>(Vs, pb, br, act);
 }
@@ -259,6 +276,8 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t*
   softmax_chunk<D, false>(acc, br, pb, act, c, lazy_raw);
   pv_chunk<D, false>(Vs, pb, br, act);
 }
+
+constexpr int kNoRange[2] = {0, 0};   // key range argument of unmasked chunks
 
 // 16 zero bytes: the DMA source of key slots that hold no token (masked keys
 // then read exact zeros, as a zero-filled chunk would hold)
@@ -495,7 +514,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   const float lazy_raw = kLazy / c;
   auto step_selected = [&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
     if (B >= T && nB - ci * 64 >= 64) {   // one group: chunk ci starts at virtual key 64*ci
-      attend_full<D>(kb, vb, qf, br, c, lazy_raw);
+      attend_full<D, false>(kb, vb, qf, br, c, lazy_raw, kNoRange, kNoRange);
       return;
     }
     const int gi = groups == 1 ? 0 : ci / cpg;
@@ -522,7 +541,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       msk[s] = !(u0 >= ilo && u0 + 64 <= ihi);
     }
     if (act[0] && act[1] && !msk[0] && !msk[1]) {
-      attend_full<D>(kb, vb, qf, br, c, lazy_raw);
+      attend_full<D, false>(kb, vb, qf, br, c, lazy_raw, kNoRange, kNoRange);
+      return;
+    }
+    if (act[0] && act[1]) {   // edge of the windows: this lane's query keeps [lo, lo + span)
+      int lo[2], span[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int t = tw + 16 * s + lr;
+        lo[s] = t - lo_off - u0;
+        span[s] = max(0, (int)min((long long)N, (long long)t + hi_off) - u0 - lo[s]);
+      }
+      attend_full<D, true>(kb, vb, qf, br, c, lazy_raw, lo, span);
       return;
     }
     attend_chunk<D>(kb, vb, qf, br, act, msk, c, lazy_raw, [&](int s, int kappa) {
