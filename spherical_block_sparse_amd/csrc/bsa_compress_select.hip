@@ -128,8 +128,6 @@ __device__ __forceinline__ void sort_rows4(double (&v)[8], int (&ix)[8], int l) 
   }
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void global_void;
 
 // 16 zero bytes: the direct-load source of rows past the last key block
 __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
@@ -148,33 +146,40 @@ __device__ __forceinline__ int kswz(int r) { return r & (D / 2 - 1) & 15; }
 template <int D>
 __device__ __forceinline__ int vswz(int r) { return (4 * (r & 3)) & (D / 4 - 1); }
 
-// Direct global -> LDS loads of the kCols key blocks starting at c0: lane
-// l of a 1 KB load writes bytes 16*l.. of that span, i.e. physical chunk
+// Loads of the kCols key blocks starting at c0 into LDS: lane l of a 1 KB
+// load writes bytes 16*l.. of that span, i.e. physical chunk
 // (1024*g + 16*l) % ROW / 16 of row (1024*g + 16*l) / ROW, which holds the
-// logical chunk given by the row's swizzle.  Rows past m read zeros.
+// logical chunk given by the row's swizzle.  A whole chunk goes through
+// buffer loads (fixed per-lane offsets, the chunk start as a scalar
+// offset); a chunk reaching past m reads zeros for the missing rows.  The
+// loads are untracked by the compiler (see dma_buffer); the caller waits.
 template <int D>
 __device__ __forceinline__ void issue_chunk(int c0, double* kb, float* vb, const char* kbytes,
-                                            const char* vbytes, int m, int w, int lane) {
+                                            const char* vbytes, int32x4 rk, int32x4 rv, bool use_rsrc,
+                                            int m, int w, int lane) {
   constexpr int KROW = D * 8, VROW = D * 4;   // bytes per LDS row
   constexpr int KLOADS = kCols * KROW / 1024 / 4, VLOADS = kCols * VROW / 1024 / 4;   // 1 KB loads per wave
   static_assert(KLOADS >= 1 && VLOADS >= 1, "chunk split");
+  const bool whole = use_rsrc && c0 + kCols <= m;
 #pragma unroll
   for (int gg = 0; gg < KLOADS; ++gg) {
     const int g = w + 4 * gg;
     const int byte = 1024 * g + 16 * lane;
     const int r = byte / KROW, pc = (byte % KROW) / 16;
-    const int lc = pc ^ kswz<D>(r);
-    const void* src = c0 + r < m ? (const void*)(kbytes + (size_t)(c0 + r) * KROW + 16 * lc) : (const void*)&kZero16;
-    __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(reinterpret_cast<char*>(kb) + 1024 * g), 16, 0, 0);
+    const int off = r * KROW + 16 * (pc ^ kswz<D>(r));
+    char* dst = reinterpret_cast<char*>(kb) + 1024 * g;
+    if (whole) dma_buffer(dst, off, rk, c0 * KROW);
+    else dma_global(dst, c0 + r < m ? (const void*)(kbytes + (size_t)c0 * KROW + off) : (const void*)&kZero16);
   }
 #pragma unroll
   for (int gg = 0; gg < VLOADS; ++gg) {
     const int g = w + 4 * gg;
     const int byte = 1024 * g + 16 * lane;
     const int r = byte / VROW, pc = (byte % VROW) / 16;
-    const int lc = pc ^ vswz<D>(r);
-    const void* src = c0 + r < m ? (const void*)(vbytes + (size_t)(c0 + r) * VROW + 16 * lc) : (const void*)&kZero16;
-    __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(reinterpret_cast<char*>(vb) + 1024 * g), 16, 0, 0);
+    const int off = r * VROW + 16 * (pc ^ vswz<D>(r));
+    char* dst = reinterpret_cast<char*>(vb) + 1024 * g;
+    if (whole) dma_buffer(dst, off, rv, c0 * VROW);
+    else dma_global(dst, c0 + r < m ? (const void*)(vbytes + (size_t)c0 * VROW + off) : (const void*)&kZero16);
   }
 }
 
@@ -193,11 +198,13 @@ __device__ __forceinline__ void chunk_logits(doublex4 (&acc)[2], const double* k
       const double kv = kb[r * D + 2 * ((k >> 1) ^ kswz<D>(r)) + (k & 1)];
       acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qa[ks], acc[ct], 0, 0, 0);
     }
+  if (c0 + kCols > m) {   // the last chunk may reach past the key blocks
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (c0 + 16 * ct + 4 * i + lg >= m) acc[ct][i] = -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (c0 + 16 * ct + 4 * i + lg >= m) acc[ct][i] = -INFINITY;
+  }
 }
 
 // Online softmax of row lr over one chunk and O^T += V̄^T P^T.  m_run is the
@@ -210,23 +217,28 @@ __device__ __forceinline__ void chunk_logits(doublex4 (&acc)[2], const double* k
 // is an exact convex combination of the v̄ rows as the product sees them.
 template <int D>
 __device__ __forceinline__ void chunk_softmax_pv(const doublex4 (&acc)[2], const float* vb, double c_exp2,
-                                                 double& m_run, float& l_run, floatx4 (&oacc)[D / 16],
-                                                 int lr, int lg) {
-  double cmax = acc[0][0];
+                                                 double lazy, double& m_run, float& l_run,
+                                                 floatx4 (&oacc)[D / 16], int lr, int lg) {
+  // The reference m_run moves only when a logit exceeds it by more than
+  // 2^8 after scaling (weights stay <= 256).  Each lane checks its own 8
+  // logits and the wave votes, so the row maxima across the four lanes of a
+  // row are formed only when some reference moves (a scalar branch).
+  double lmax = acc[0][0];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cmax = fmax(cmax, acc[ct][i]);
-  cmax = fmax(cmax, __shfl_xor(cmax, 16));
-  cmax = fmax(cmax, __shfl_xor(cmax, 32));
-  const double m_new = fmax(m_run, cmax);
-  if (m_new > m_run) {   // differs only between the four lanes of a row's group
-    const float alpha = __builtin_amdgcn_exp2f((float)((m_run - m_new) * c_exp2));
+    for (int i = 0; i < 4; ++i) lmax = fmax(lmax, acc[ct][i]);
+  if (__ballot(lmax > m_run + lazy)) {
+    double row = fmax(lmax, __shfl_xor(lmax, 16));
+    row = fmax(row, __shfl_xor(row, 32));
+    const double m_new = fmax(m_run, row);
+    const float alpha = m_run == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((float)((m_run - m_new) * c_exp2));
+    m_run = m_new;
     l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
   }
-  const double nmc = -m_new * c_exp2;
+  const double nmc = -m_run * c_exp2;
   bf16x8 pb;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -244,7 +256,6 @@ __device__ __forceinline__ void chunk_softmax_pv(const doublex4 (&acc)[2], const
     }
     oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
   }
-  m_run = m_new;
 }
 
 // o_CG = O / l for row `row`; lane l holds head-dim entries dt*16 + 4*lg + i
@@ -355,6 +366,10 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
   const double* qb = a.qbar + (size_t)slice * m * D;
   const char* kbytes = reinterpret_cast<const char*>(a.kbar + (size_t)slice * m * D);
   const char* vbytes = reinterpret_cast<const char*>(a.vbar + (size_t)slice * m * D);
+  const bool use_rsrc = (long long)m * D * 8 < 0x7fffffffLL;   // 32-bit buffer offsets
+  const int32x4 rk = slice_rsrc(kbytes, use_rsrc ? m * D * 8 : 0);
+  const int32x4 rv = slice_rsrc(vbytes, use_rsrc ? m * D * 4 : 0);
+  const double lazy = 8.0 / a.c_exp2;   // 2^8 in weight, in units of raw dot products
 
   double qa[D / 4];
 #pragma unroll
@@ -376,7 +391,7 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
   auto chunk = [&](int c0, const double* kb, const float* vb) __attribute__((always_inline)) {
     doublex4 acc[2];
     chunk_logits<D>(acc, kb, qa, c0, m, lr, lg);
-    chunk_softmax_pv<D>(acc, vb, a.c_exp2, m_run, l_run, oacc, lr, lg);
+    chunk_softmax_pv<D>(acc, vb, a.c_exp2, lazy, m_run, l_run, oacc, lr, lg);
     // a key below `bound` is beaten by n keys of its row: never needed
     double bound = tv[0];
 #pragma unroll
@@ -393,16 +408,16 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
       }
   };
 
-  issue_chunk<D>(0, Kb0, Vb0, kbytes, vbytes, m, w, lane);
+  issue_chunk<D>(0, Kb0, Vb0, kbytes, vbytes, rk, rv, use_rsrc, m, w, lane);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   for (int c0 = 0; c0 < m; c0 += 2 * kCols) {
-    if (c0 + kCols < m) issue_chunk<D>(c0 + kCols, Kb1, Vb1, kbytes, vbytes, m, w, lane);
+    if (c0 + kCols < m) issue_chunk<D>(c0 + kCols, Kb1, Vb1, kbytes, vbytes, rk, rv, use_rsrc, m, w, lane);
     chunk(c0, Kb0, Vb0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (c0 + kCols >= m) break;
-    if (c0 + 2 * kCols < m) issue_chunk<D>(c0 + 2 * kCols, Kb0, Vb0, kbytes, vbytes, m, w, lane);
+    if (c0 + 2 * kCols < m) issue_chunk<D>(c0 + 2 * kCols, Kb0, Vb0, kbytes, vbytes, rk, rv, use_rsrc, m, w, lane);
     chunk(c0 + kCols, Kb1, Vb1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -469,6 +484,10 @@ __global__ __launch_bounds__(256) void compress_select_buffered_kernel(CSArgs a)
   const double* qb = a.qbar + (size_t)slice * m * D;
   const char* kbytes = reinterpret_cast<const char*>(a.kbar + (size_t)slice * m * D);
   const char* vbytes = reinterpret_cast<const char*>(a.vbar + (size_t)slice * m * D);
+  const bool use_rsrc = (long long)m * D * 8 < 0x7fffffffLL;   // 32-bit buffer offsets
+  const int32x4 rk = slice_rsrc(kbytes, use_rsrc ? m * D * 8 : 0);
+  const int32x4 rv = slice_rsrc(vbytes, use_rsrc ? m * D * 4 : 0);
+  const double lazy = 8.0 / a.c_exp2;   // 2^8 in weight, in units of raw dot products
 
   {
     const int rw = tile * 64 + w * 16;
@@ -547,7 +566,7 @@ __global__ __launch_bounds__(256) void compress_select_buffered_kernel(CSArgs a)
     auto chunk = [&](int c0, const double* kb, const float* vb) __attribute__((always_inline)) {
       doublex4 acc[2];
       chunk_logits<D>(acc, kb, qa, c0, m, lr, lg);
-      chunk_softmax_pv<D>(acc, vb, a.c_exp2, m_run, l_run, oacc, lr, lg);
+      chunk_softmax_pv<D>(acc, vb, a.c_exp2, lazy, m_run, l_run, oacc, lr, lg);
 
       // selection: append the logits that beat the row's current n-th key.
       // The four lanes of a row (lanes lr, lr+16, lr+32, lr+48) take
@@ -599,16 +618,16 @@ __global__ __launch_bounds__(256) void compress_select_buffered_kernel(CSArgs a)
 
     // double-buffered stream over the key blocks (the counters above are
     // published by the first barrier)
-    issue_chunk<D>(0, Kb0, Vb0, kbytes, vbytes, m, w, lane);
+    issue_chunk<D>(0, Kb0, Vb0, kbytes, vbytes, rk, rv, use_rsrc, m, w, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
     for (int c0 = 0; c0 < m; c0 += 2 * kCols) {
-      if (c0 + kCols < m) issue_chunk<D>(c0 + kCols, Kb1, Vb1, kbytes, vbytes, m, w, lane);
+      if (c0 + kCols < m) issue_chunk<D>(c0 + kCols, Kb1, Vb1, kbytes, vbytes, rk, rv, use_rsrc, m, w, lane);
       chunk(c0, Kb0, Vb0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       if (c0 + kCols >= m) break;
-      if (c0 + 2 * kCols < m) issue_chunk<D>(c0 + 2 * kCols, Kb0, Vb0, kbytes, vbytes, m, w, lane);
+      if (c0 + 2 * kCols < m) issue_chunk<D>(c0 + 2 * kCols, Kb0, Vb0, kbytes, vbytes, rk, rv, use_rsrc, m, w, lane);
       chunk(c0 + kCols, Kb1, Vb1);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();

@@ -75,10 +75,6 @@ struct FineArgs {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-// word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format,
-// no swizzle, stride 0 (offsets are plain byte offsets, range-checked
-// against the record count)
-constexpr int kRsrcWord3 = 0x00020000;
 
 constexpr float kLazy = 8.0f;
 
@@ -283,58 +279,6 @@ constexpr int kNoRange[2] = {0, 0};   // key range argument of unmasked chunks
 // then read exact zeros, as a zero-filled chunk would hold)
 __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void global_void;
-
-// Direct loads into LDS (lane l's 16 bytes land at M0 + 16*l), written as
-// inline assembly so that the compiler does not track them: it would
-// otherwise make every transposing LDS read wait for all loads in flight
-// (it cannot tell which buffer those reads touch), which serialises the
-// prefetch of the next chunk with the current one.  The loads have no
-// register results; their completion is awaited explicitly (s_waitcnt
-// vmcnt, then a barrier) before a buffer is read.  M0 is restored.
-typedef int int32x4 __attribute__((ext_vector_type(4)));
-
-// LDS byte address of p as a scalar (the asm operands below must be SGPRs;
-// every caller passes a workgroup-uniform address)
-__device__ __forceinline__ int lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((int)(unsigned)(uintptr_t)(lds_void*)p);
-}
-
-__device__ __forceinline__ void dma_buffer(const void* lds, int voff, int32x4 rsrc, int soff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
-      : "memory");
-}
-
-__device__ __forceinline__ void dma_global(const void* lds, const void* src) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr(lds)), "v"(src)
-      : "memory");
-}
-
-// buffer resource of one slice's tensor: base, stride 0, byte range, word 3
-__device__ __forceinline__ int32x4 slice_rsrc(const void* base, int bytes) {
-  const unsigned long long b = (unsigned long long)base;
-  int32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffull));
-  r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffull));
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = kRsrcWord3;
-  return r;
-}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (lgkm and exp counters not waited on)
