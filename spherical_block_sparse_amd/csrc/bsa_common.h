@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mosaic {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -67,6 +69,46 @@ __device__ __forceinline__ void dma_global(const void* lds, const void* src) {
       : "=&s"(saved)
       : "s"(lds_addr(lds)), "v"(src)
       : "memory");
+}
+
+// The same two loads with the LDS destination given as a scalar base plus a
+// compile-time byte offset, added to M0 inside the asm.  A loop that issues
+// many loads into a few buffers then keeps one base register live instead of
+// one hoisted address per load (which spills scalar registers).
+template <int OFF>
+__device__ __forceinline__ void dma_buffer_at(int lds_base, int voff, int32x4 rsrc, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %5\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "n"(OFF)
+      : "memory", "scc");
+}
+
+template <int OFF>
+__device__ __forceinline__ void dma_global_at(int lds_base, const void* src) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %3\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(src), "n"(OFF)
+      : "memory", "scc");
+}
+
+// calls f(std::integral_constant<int, i>) for i = I .. N-1, so that i can
+// feed a template argument
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // buffer resource of one slice's tensor: base, stride 0, byte range, word 3

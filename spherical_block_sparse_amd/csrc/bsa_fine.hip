@@ -292,12 +292,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int RPG = 64 / CPR;           // key rows per 1 KB load (one wave instruction)
   constexpr int GPC = 64 / RPG;           // 1 KB loads per tensor per 64-key chunk
   static_assert(GPC % WAVES == 0, "loads split evenly over the waves");
-  // two LDS buffers as separate objects, so the compiler can tell the chunk
-  // being read from the one the DMA is filling
-  __shared__ __attribute__((aligned(16))) uint16_t Kb0[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vb0[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Kb1[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vb1[64 * D];
+  // the two K/V buffer pairs in one array, 64*D bf16 each: K0, V0, K1, V1
+  // (the loads address them from one scalar base plus immediate offsets)
+  __shared__ __attribute__((aligned(16))) uint16_t KVb[4 * 64 * D];
+  uint16_t* const Kb0 = KVb;
+  uint16_t* const Vb0 = KVb + 64 * D;
+  uint16_t* const Kb1 = KVb + 2 * 64 * D;
+  uint16_t* const Vb1 = KVb + 3 * 64 * D;
   __shared__ int SelT[4 * 64];   // selection rows of the tile's query blocks (<= T/16 rows of <= 64)
 
   // contiguous run of tiles per XCD (workgroups are dispatched round-robin)
@@ -387,51 +388,55 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   const int slice_bytes = use_rsrc ? N * D * 2 : 0;
   const int32x4 rk = slice_rsrc(ks, slice_bytes);
   const int32x4 rv = slice_rsrc(vs, slice_bytes);
-  auto issue_rows = [&](int tok0, int valid, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
+  // LDS byte address of this wave's first 1 KB load into K0; load gg of
+  // buffer pair P lands (4*P + 2*tensor) * 64*D + gg*WAVES*1024 bytes further
+  const int lds_base = lds_addr(KVb) + w * 1024;
+  // byte offset of load gg of tensor TS (0 = K, 1 = V) of buffer pair P
+  auto at = [](auto P, int TS, auto gg) constexpr { return (2 * decltype(P)::value + TS) * 64 * D * 2 + decltype(gg)::value * WAVES * 1024; };
+  auto issue_rows = [&](int tok0, int valid, auto P) __attribute__((always_inline)) {
     if (valid >= 64 && use_rsrc) {   // whole chunk of consecutive tokens: no per-lane checks
       const int soff = __builtin_amdgcn_readfirstlane(tok0 * (D * 2));   // uniform by construction
-#pragma unroll
-      for (int gg = 0; gg < LPW; ++gg) {
-        const int grp = w + WAVES * gg;
+      static_for<0, LPW>([&](auto gg) __attribute__((always_inline)) {
         const int off = 2 * lane_off[gg];
-        dma_buffer(kb + grp * 512, off, rk, soff);
-        dma_buffer(vb + grp * 512, off, rv, soff);
-      }
+        dma_buffer_at<at(P, 0, gg)>(lds_base, off, rk, soff);
+        dma_buffer_at<at(P, 1, gg)>(lds_base, off, rv, soff);
+      });
       return;
     }
     const char* kbase = reinterpret_cast<const char*>(ks + (size_t)tok0 * D);   // uniform
     const char* vbase = reinterpret_cast<const char*>(vs + (size_t)tok0 * D);
-#pragma unroll
-    for (int gg = 0; gg < LPW; ++gg) {
-      const int grp = w + WAVES * gg;
+    static_for<0, LPW>([&](auto gg) __attribute__((always_inline)) {
       const bool ok = lane_row[gg] < valid;
       const unsigned off = 2u * (unsigned)lane_off[gg];
-      dma_global(kb + grp * 512, ok ? (const void*)(kbase + off) : (const void*)&kZero16);
-      dma_global(vb + grp * 512, ok ? (const void*)(vbase + off) : (const void*)&kZero16);
-    }
+      dma_global_at<at(P, 0, gg)>(lds_base, ok ? (const void*)(kbase + off) : (const void*)&kZero16);
+      dma_global_at<at(P, 1, gg)>(lds_base, ok ? (const void*)(vbase + off) : (const void*)&kZero16);
+    });
   };
-  auto issue_gather = [&](int ci, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int gg = 0; gg < LPW; ++gg) {
-      const int grp = w + WAVES * gg;
+  auto issue_gather = [&](int ci, auto P) __attribute__((always_inline)) {
+    static_for<0, LPW>([&](auto gg) __attribute__((always_inline)) {
       const int row = lane_row[gg];
       const int lc = (lane % CPR) ^ swz<D>(row);
       const int tok = token_of(ci, row);
-      dma_global(kb + grp * 512, tok >= 0 ? (const void*)(ks + (size_t)tok * D + 8 * lc) : (const void*)&kZero16);
-      dma_global(vb + grp * 512, tok >= 0 ? (const void*)(vs + (size_t)tok * D + 8 * lc) : (const void*)&kZero16);
-    }
+      dma_global_at<at(P, 0, gg)>(lds_base, tok >= 0 ? (const void*)(ks + (size_t)tok * D + 8 * lc)
+                                                     : (const void*)&kZero16);
+      dma_global_at<at(P, 1, gg)>(lds_base, tok >= 0 ? (const void*)(vs + (size_t)tok * D + 8 * lc)
+                                                     : (const void*)&kZero16);
+    });
   };
-  auto issue = [&](int ci, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
+  // loads of chunk ci into buffer pair P (std::integral_constant 0 or 1)
+  auto issue = [&](int ci, auto P) __attribute__((always_inline)) {
     if (ci >= c_sel) {
       const int u0 = wlo + (ci - c_sel) * 64;
-      issue_rows(u0, whi - u0, kb, vb);
+      issue_rows(u0, whi - u0, P);
     } else if (B >= 64) {   // one group: 128-query tiles only come with blocks of >= 128
       const int vk0 = ci * 64;   // a multiple of 64 inside one key block
-      issue_rows((SelT[vk0 >> lb] << lb) + (vk0 & (B - 1)), nB - vk0, kb, vb);
+      issue_rows((SelT[vk0 >> lb] << lb) + (vk0 & (B - 1)), nB - vk0, P);
     } else {
-      issue_gather(ci, kb, vb);
+      issue_gather(ci, P);
     }
   };
+  constexpr std::integral_constant<int, 0> P0{};
+  constexpr std::integral_constant<int, 1> P1{};
 
   Branch<D> br[2];
 #pragma unroll
@@ -509,16 +514,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   // ci is computed; each barrier follows the wave's wait for its own loads.
   auto run = [&](int c0, int c1, auto step) __attribute__((always_inline)) {
     if (c0 >= c1) return;
-    issue(c0, Kb0, Vb0);
+    issue(c0, P0);
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     for (int ci = c0; ci < c1; ci += 2) {
-      if (ci + 1 < c1) issue(ci + 1, Kb1, Vb1);
+      if (ci + 1 < c1) issue(ci + 1, P1);
       step(ci, Kb0, Vb0);
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       __syncthreads();
       if (ci + 1 >= c1) break;
-      if (ci + 2 < c1) issue(ci + 2, Kb0, Vb0);
+      if (ci + 2 < c1) issue(ci + 2, P0);
       step(ci + 1, Kb1, Vb1);
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       __syncthreads();
