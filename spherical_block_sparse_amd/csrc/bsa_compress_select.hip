@@ -399,12 +399,19 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
       if (jb == j) bound = tv[j];
     bound = fmin(bound, __shfl_xor(bound, 16));
     bound = fmin(bound, __shfl_xor(bound, 32));
+    // A key enters the list step when it reaches max(tv[K-1], bound).  That
+    // admits, besides the keys with x > tv[K-1] and x >= bound, only
+    // x == tv[K-1], which the strict compares of list_insert leave out.
+    double thr = fmax(tv[K - 1], bound);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const double x = acc[ct][i];
-        if (__ballot(x > tv[K - 1] && x >= bound)) list_insert<K>(tv, ti, x, c0 + 16 * ct + 4 * i + lg);
+        if (__ballot(x >= thr)) {
+          list_insert<K>(tv, ti, x, c0 + 16 * ct + 4 * i + lg);
+          thr = fmax(tv[K - 1], bound);
+        }
       }
   };
 
