@@ -39,8 +39,14 @@ def hipcc() -> str:
 
 # per-source extra flags: the fine-attention and selection kernels never rely on NaN
 # semantics (masked scores are -inf, which stays honoured), and without this
-# every fmaxf of an MFMA result is preceded by a NaN-quieting instruction
-EXTRA = {"bsa_fine.hip": ["-fno-honor-nans"], "bsa_compress_select.hip": ["-fno-honor-nans"]}
+# every fmaxf of an MFMA result is preceded by a NaN-quieting instruction.  The
+# selection kernels keep their fp64 MFMA accumulators in VGPRs
+# (-amdgpu-mfma-vgpr-form): in AGPRs each chunk pays 16 accumulator reads,
+# and no vector work runs beside an fp64 MFMA to hide them.
+EXTRA = {
+    "bsa_fine.hip": ["-fno-honor-nans"],
+    "bsa_compress_select.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:

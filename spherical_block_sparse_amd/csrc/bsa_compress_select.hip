@@ -213,8 +213,9 @@ __device__ __forceinline__ void chunk_logits(doublex4 (&acc)[2], const double* k
 // v_mfma_f32_16x16x32_bf16 per 16 head-dim rows: k-slot 8*g + e of that
 // product holds key 16*(e/4) + 4*(e%4) + g, which is exactly the key whose
 // logit lane lr + 16*g holds in acc[e/4][e%4], so the weights need no
-// exchange between lanes.  The denominator adds the rounded weights, so o_CG
-// is an exact convex combination of the v̄ rows as the product sees them.
+// exchange between lanes.  The denominator adds the rounded weights (pairwise,
+// v_dot2 with ones), so o_CG is an exact convex combination of the v̄ rows as
+// the product sees them.
 template <int D>
 __device__ __forceinline__ void chunk_softmax_pv(const doublex4 (&acc)[2], const float* vb, double c_exp2,
                                                  double lazy, double& m_run, float& l_run,
@@ -241,10 +242,12 @@ __device__ __forceinline__ void chunk_softmax_pv(const doublex4 (&acc)[2], const
   const double nmc = -m_run * c_exp2;
   bf16x8 pb;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 8; ++e)
     pb[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f((float)fma(acc[e / 4][e % 4], c_exp2, nmc)));
-    l_run += static_cast<float>(pb[e]);
-  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e], pb[e + 1]}, ones, l_run, false);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
     const int col = dt * 16 + lr;   // A operand v̄^T[col][slot 8*lg + e]
