@@ -119,6 +119,38 @@ mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const
                               int head_dim, int nside, int block, int topn, int window, float* out,
                               void* stream);
 
+/* Workspace bytes mosaic_bsa_backward needs for these sizes, or 0 when the
+ * sizes are invalid or outside what the backward implements. */
+size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, int nside, int block,
+                                           int topn);
+
+/* Gradient of mosaic_bsa_forward's `out` with respect to q, k, v and the
+ * gates, given dout = dL/dout.  The papernotes.org ICML2026 notes (关键设计 ›
+ * Mesh-aligned Block-Sparse Attention) describe a model trained end to end;
+ * the gradient is that of the forward with the selection sel_idx held fixed
+ * (top-n is piecewise constant) and each pooled mean's gradient spread evenly
+ * over its block.
+ *   q, k, v   in : bf16 bits [batch][heads][N][head_dim] (the forward's inputs)
+ *   gates     in : float32 [batch][heads][N][3]
+ *   sel_idx   in : int32 [batch][heads][m][topn], the forward's selection
+ *                  (any valid block indices; clamped into [0, m))
+ *   dout      in : float32 [batch][heads][N][head_dim]
+ *   dq, dk, dv out: float32 [batch][heads][N][head_dim], overwritten
+ *   dgates    out: float32 [batch][heads][N][3], overwritten
+ *   workspace in/out scratch of at least mosaic_bsa_backward_workspace_bytes(...)
+ * All launches go to `stream`; the forward's pooling and compressed branch
+ * are recomputed.  bf16 products with float32 accumulation (dout is rounded
+ * to bf16 for the products; D = dout·o uses it in float32).  Besides the
+ * forward's limits, block >= 64 and m = N/block a multiple of 64 are needed
+ * (MOSAIC_ERR_UNSUPPORTED otherwise).  Alignment: q, k, v, dout, dq, dk, dv 16
+ * bytes; gates, sel_idx, dgates 4; workspace 256.  Errors as for the forward:
+ * nothing is launched and the outputs are untouched. */
+mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, const float* gates,
+                                  const int32_t* sel_idx, const float* dout, int batch, int heads,
+                                  int head_dim, int nside, int block, int topn, int window, float* dq,
+                                  float* dk, float* dv, float* dgates, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

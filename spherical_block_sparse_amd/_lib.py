@@ -28,6 +28,7 @@ EXPORTED = (
     "mosaic_bsa_abi_version", "mosaic_status_string", "mosaic_last_error",
     "mosaic_bsa_workspace_bytes", "mosaic_bsa_forward", "mosaic_bsa_pool",
     "mosaic_bsa_compress_select", "mosaic_bsa_fine",
+    "mosaic_bsa_backward_workspace_bytes", "mosaic_bsa_backward",
 )
 
 
@@ -64,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_compress_select.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
         L.mosaic_bsa_fine.restype = I
         L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+        L.mosaic_bsa_backward_workspace_bytes.restype = S
+        L.mosaic_bsa_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.mosaic_bsa_backward.restype = I
+        L.mosaic_bsa_backward.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, S, P]
         _lib = L
     return _lib
 
@@ -175,3 +180,33 @@ def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, o
         _ptr(o_cg, torch.float32, (b, h, m, d), "o_cg"), _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"),
         b, h, d, nside, block, topn, window, _ptr(out, torch.float32, (b, h, n, d), "out"), _stream(stream)))
     return out
+
+
+def mosaic_bsa_backward_workspace_bytes(batch, heads, head_dim, nside, block, topn) -> int:
+    return lib().mosaic_bsa_backward_workspace_bytes(batch, heads, head_dim, nside, block, topn)
+
+
+def mosaic_bsa_backward(q, k, v, gates, sel_idx, dout, nside, block, topn, window, dq=None, dk=None, dv=None,
+                        dgates=None, workspace=None, stream=None):
+    """dq, dk, dv [b,H,N,d] and dgates [b,H,N,3] (fp32): gradient of the forward's out given dout,
+    with the selection sel_idx held fixed."""
+    b, h, n, d = _dims(q, nside)
+    m = n // block
+    dq = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    dgates = torch.empty((b, h, n, 3), dtype=torch.float32, device=q.device) if dgates is None else dgates
+    need = mosaic_bsa_backward_workspace_bytes(b, h, d, nside, block, topn)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or workspace.device.type != "cuda":
+        raise ValueError("workspace must be a 1-D uint8 device tensor")
+    _check(lib().mosaic_bsa_backward(
+        _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
+        _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
+        _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"), _ptr(dout, torch.float32, (b, h, n, d), "dout"),
+        b, h, d, nside, block, topn, window,
+        _ptr(dq, torch.float32, (b, h, n, d), "dq"), _ptr(dk, torch.float32, (b, h, n, d), "dk"),
+        _ptr(dv, torch.float32, (b, h, n, d), "dv"), _ptr(dgates, torch.float32, (b, h, n, 3), "dgates"),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return dq, dk, dv, dgates

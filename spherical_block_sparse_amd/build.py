@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmosaic_bsa.so")
 
-SOURCES = ["bsa_pool.hip", "bsa_compress_select.hip", "bsa_fine.hip", "mosaic_bsa_api.cpp"]
+SOURCES = ["bsa_pool.hip", "bsa_compress_select.hip", "bsa_fine.hip", "bsa_backward.hip", "mosaic_bsa_api.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -45,6 +45,7 @@ def hipcc() -> str:
 # and no vector work runs beside an fp64 MFMA to hide them.
 EXTRA = {
     "bsa_fine.hip": ["-fno-honor-nans"],
+    "bsa_backward.hip": ["-fno-honor-nans"],
     "bsa_compress_select.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

@@ -136,4 +136,42 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        int n_tok, int head_dim, int block, int topn, int window,
                        hipStream_t stream);
 
+// Everything the backward launches read and write (device pointers; the
+// workspace buffers are carved by the C-ABI entry point).
+struct BwdLaunch {
+  const uint16_t* q;        // bf16 [S][N][d]
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* gates;       // [S][N][3]
+  const int32_t* sel;       // [S][m][topn] from the forward
+  const float* dout;        // [S][N][d]
+  float* dq;                // outputs, fp32 [S][N][d]
+  float* dk;
+  float* dv;
+  float* dgates;            // [S][N][3]
+  int head_dim;
+  long long slices;
+  int n_tok, block, topn, window;
+  const double* qbar;       // recomputed pooled means [S][m][d]
+  const double* kbar;
+  const float* vbar;
+  const float* o_cg;        // recomputed compressed output [S][m][d]
+  uint16_t* dob;            // workspace: bf16 dO [S][N][d]
+  float* docg;              // [S][m][d] and its bf16 copy
+  uint16_t* docg_b;
+  uint16_t* qbar_b;         // bf16 pooled rows [S][m][d]
+  uint16_t* kbar_b;
+  uint16_t* vbar_b;
+  float* stats;             // [2][S][N][4]
+  float* stats_cg;          // [2][S][m][4]
+  float* dqbar;             // [S][m][d]
+  float* dkbar;
+  float* dvbar;
+  int32_t* inv_off;         // [S][m+1]
+  int32_t* inv_cursor;      // [S][m]
+  int32_t* inv_list;        // [S][m*topn]
+};
+
+hipError_t launch_backward(const BwdLaunch& L, hipStream_t stream);
+
 }  // namespace mosaic

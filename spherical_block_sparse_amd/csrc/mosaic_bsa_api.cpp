@@ -97,6 +97,48 @@ Workspace layout(const Shape& s) {
   return w;
 }
 
+// Backward workspace: recomputed forward pieces, bf16 copies, per-query
+// statistics, pooled gradients and the inverted selection.
+struct BwdWorkspace {
+  size_t qbar, kbar, vbar, ocg, sel, dob, docg, docg_b, qbar_b, kbar_b, vbar_b, stats, stats_cg, dqbar, dkbar,
+      dvbar, inv_off, inv_cur, inv_list, total;
+};
+
+BwdWorkspace bwd_layout(const Shape& s) {
+  const size_t em = (size_t)s.slices * s.m * s.d, en = (size_t)s.slices * s.n_tok * s.d;
+  BwdWorkspace w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t r = o; o += align256(bytes); return r; };
+  w.qbar = take(em * sizeof(double));
+  w.kbar = take(em * sizeof(double));
+  w.vbar = take(em * sizeof(float));
+  w.ocg = take(em * sizeof(float));
+  w.sel = take((size_t)s.slices * s.m * s.topn * sizeof(int32_t));
+  w.dob = take(en * sizeof(uint16_t));
+  w.docg = take(em * sizeof(float));
+  w.docg_b = take(em * sizeof(uint16_t));
+  w.qbar_b = take(em * sizeof(uint16_t));
+  w.kbar_b = take(em * sizeof(uint16_t));
+  w.vbar_b = take(em * sizeof(uint16_t));
+  w.stats = take((size_t)2 * s.slices * s.n_tok * 4 * sizeof(float));
+  w.stats_cg = take((size_t)2 * s.slices * s.m * 4 * sizeof(float));
+  w.dqbar = take(em * sizeof(float));
+  w.dkbar = take(em * sizeof(float));
+  w.dvbar = take(em * sizeof(float));
+  w.inv_off = take((size_t)s.slices * (s.m + 1) * sizeof(int32_t));
+  w.inv_cur = take((size_t)s.slices * s.m * sizeof(int32_t));
+  w.inv_list = take((size_t)s.slices * s.m * s.topn * sizeof(int32_t));
+  w.total = o;
+  return w;
+}
+
+// what the backward kernels implement beyond the forward's own limits
+mosaic_status check_backward_shape(const Shape& s) {
+  if (s.block < 64) return fail(MOSAIC_ERR_UNSUPPORTED, "backward: block %d, the kernels need block >= 64", s.block);
+  if (s.m % 64) return fail(MOSAIC_ERR_UNSUPPORTED, "backward: m = N/block = %d must be a multiple of 64", s.m);
+  return MOSAIC_OK;
+}
+
 mosaic_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MOSAIC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -212,6 +254,80 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
                           s.block, s.topn, s.window, hs);
   return hip_status(e, "bsa_fine launch");
+}
+
+size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn) {
+  Shape s;
+  if (check_shape(batch, heads, head_dim, nside, block, topn, 0, kUsesTopn, &s) != MOSAIC_OK) return 0;
+  if (check_backward_shape(s) != MOSAIC_OK) return 0;
+  return bwd_layout(s).total;
+}
+
+mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, const float* gates,
+                                  const int32_t* sel_idx, const float* dout, int batch, int heads, int head_dim,
+                                  int nside, int block, int topn, int window, float* dq, float* dk, float* dv,
+                                  float* dgates, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(sel_idx); REQUIRE_PTR(dout);
+  REQUIRE_PTR(dq); REQUIRE_PTR(dk); REQUIRE_PTR(dv); REQUIRE_PTR(dgates); REQUIRE_PTR(workspace);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
+  REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(dout, 16); REQUIRE_ALIGN(dq, 16); REQUIRE_ALIGN(dk, 16);
+  REQUIRE_ALIGN(dv, 16); REQUIRE_ALIGN(dgates, 4); REQUIRE_ALIGN(workspace, 256);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
+  if (st != MOSAIC_OK) return st;
+  if ((st = check_backward_shape(s)) != MOSAIC_OK) return st;
+  const BwdWorkspace w = bwd_layout(s);
+  if (workspace_bytes < w.total)
+    return fail(MOSAIC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  mosaic::BwdLaunch L;
+  L.q = static_cast<const uint16_t*>(q);
+  L.k = static_cast<const uint16_t*>(k);
+  L.v = static_cast<const uint16_t*>(v);
+  L.gates = gates;
+  L.sel = sel_idx;
+  L.dout = dout;
+  L.dq = dq;
+  L.dk = dk;
+  L.dv = dv;
+  L.dgates = dgates;
+  L.head_dim = s.d;
+  L.slices = s.slices;
+  L.n_tok = s.n_tok;
+  L.block = s.block;
+  L.topn = s.topn;
+  L.window = s.window;
+  double* qbar = reinterpret_cast<double*>(ws + w.qbar);
+  double* kbar = reinterpret_cast<double*>(ws + w.kbar);
+  float* vbar = reinterpret_cast<float*>(ws + w.vbar);
+  float* ocg = reinterpret_cast<float*>(ws + w.ocg);
+  L.qbar = qbar;
+  L.kbar = kbar;
+  L.vbar = vbar;
+  L.o_cg = ocg;
+  L.dob = reinterpret_cast<uint16_t*>(ws + w.dob);
+  L.docg = reinterpret_cast<float*>(ws + w.docg);
+  L.docg_b = reinterpret_cast<uint16_t*>(ws + w.docg_b);
+  L.qbar_b = reinterpret_cast<uint16_t*>(ws + w.qbar_b);
+  L.kbar_b = reinterpret_cast<uint16_t*>(ws + w.kbar_b);
+  L.vbar_b = reinterpret_cast<uint16_t*>(ws + w.vbar_b);
+  L.stats = reinterpret_cast<float*>(ws + w.stats);
+  L.stats_cg = reinterpret_cast<float*>(ws + w.stats_cg);
+  L.dqbar = reinterpret_cast<float*>(ws + w.dqbar);
+  L.dkbar = reinterpret_cast<float*>(ws + w.dkbar);
+  L.dvbar = reinterpret_cast<float*>(ws + w.dvbar);
+  L.inv_off = reinterpret_cast<int32_t*>(ws + w.inv_off);
+  L.inv_cursor = reinterpret_cast<int32_t*>(ws + w.inv_cur);
+  L.inv_list = reinterpret_cast<int32_t*>(ws + w.inv_list);
+  // the forward's pooling and compressed branch (its own selection goes to
+  // scratch: the backward uses the caller's)
+  hipError_t e = mosaic::launch_pool(L.q, L.k, L.v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, reinterpret_cast<int32_t*>(ws + w.sel), s.slices, s.m,
+                                     s.d, s.topn, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  return hip_status(mosaic::launch_backward(L, hs), "bsa_backward launch");
 }
 
 }  // extern "C"

@@ -107,3 +107,38 @@ def test_python_binding_rejects_bad_tensors_without_launch():
                                 out=torch.zeros(1), sel_idx=torch.zeros(1), workspace=torch.zeros(1, dtype=torch.uint8))
     with pytest.raises(ValueError):
         _lib.mosaic_bsa_forward(q[:, :, :700], q, q, q, 8, 16, 4, 32)
+
+
+def bwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, sel=FAKE, dout=FAKE, batch=1, heads=2, d=64, nside=32, block=64,
+        topn=16, window=256, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, ws=FAKE, ws_bytes=None):
+    L = _lib.lib()
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return L.mosaic_bsa_backward(q, k, v, gates, sel, dout, batch, heads, d, nside, block, topn, window,
+                                 dq, dk, dv, dg, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(sel=None), NULL), (dict(dout=None), NULL), (dict(dq=None), NULL),
+    (dict(dk=None), NULL), (dict(dv=None), NULL), (dict(dg=None), NULL), (dict(ws=None), NULL),
+    (dict(dout=FAKE + 8), MISAL), (dict(dq=FAKE + 4), MISAL), (dict(sel=FAKE + 2), MISAL),
+    (dict(ws=FAKE + 16), MISAL),
+    (dict(batch=0), SHAPE), (dict(topn=0), SHAPE), (dict(window=0), SHAPE), (dict(block=32), SHAPE),
+    (dict(block=16), UNSUP),                     # backward needs block >= 64
+    (dict(nside=16, block=64), UNSUP),           # m = 48, not a multiple of 64
+    (dict(d=48), UNSUP),
+    (dict(ws_bytes=1000), WS),
+])
+def test_backward_validation(kw, code):
+    assert bwd(**kw) == code
+    assert _lib.lib().mosaic_last_error().decode() != ""
+
+
+def test_backward_workspace_bytes():
+    L = _lib.lib()
+    assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 64, 16) > 0
+    assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 16, 16) == 0   # block < 64
+    assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 16, 64, 16) == 0   # m = 48
+    # the largest section is the bf16 copy of dout plus the per-query statistics
+    n, s = 12 * 32 * 32, 2
+    assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 64, 16) >= s * n * 64 * 2 + 2 * s * n * 16
