@@ -141,8 +141,8 @@ size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, i
  * All launches go to `stream`; the forward's pooling and compressed branch
  * are recomputed.  bf16 products with float32 accumulation (dout is rounded
  * to bf16 for the products; D = dout·o uses it in float32).  Besides the
- * forward's limits, block >= 64 and m = N/block a multiple of 64 are needed
- * (MOSAIC_ERR_UNSUPPORTED otherwise).  Alignment: q, k, v, dout, dq, dk, dv 16
+ * forward's limits, block >= 64 and m = N/block a multiple of 64 and at most
+ * 16384 are needed (MOSAIC_ERR_UNSUPPORTED otherwise).  Alignment: q, k, v, dout, dq, dk, dv 16
  * bytes; gates, sel_idx, dgates 4; workspace 256.  Errors as for the forward:
  * nothing is launched and the outputs are untouched. */
 mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, const float* gates,

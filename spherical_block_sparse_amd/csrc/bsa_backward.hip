@@ -36,6 +36,7 @@
 // N and m = N/block multiples of 64.
 #include "bsa_common.h"
 
+#include <climits>
 #include <math.h>
 
 namespace mosaic {
@@ -117,12 +118,17 @@ __device__ __forceinline__ void stage_rows(uint16_t* buf, const uint16_t* base, 
   }
 }
 
-// Stage the 64 per-query records (lse, D, g, 0) of rows r0 .. r0+63 (one 1 KB
-// load by wave 0; rows past `valid` read as zeros).
-__device__ __forceinline__ void stage_stats(float* buf, const float* stats, long long r0, int valid, int w) {
+// Stage the per-query statistics of rows r0 .. r0+63 as three arrays of 64
+// floats (lse, D, g) from their [3][N] planes: lane L of wave 0 loads rows
+// r0 + 4(L%16) .. +3 of plane L/16.  r0 is a multiple of 4 and the plane
+// rows past `valid` either exist or are past N in whole groups of 4, which
+// read as zeros (lanes 48..63 fill the unused fourth array with zeros).
+__device__ __forceinline__ void stage_stats(float* buf, const float* stats, long long r0, int valid, int n_tok,
+                                            int w) {
   if (w != 0) return;
-  const int lane = threadIdx.x % kWave;
-  dma_global(buf, lane < valid ? (const void*)(stats + (r0 + lane) * 4) : (const void*)&kZero16B);
+  const int lane = threadIdx.x % kWave, plane = lane / 16, g4 = 4 * (lane % 16);
+  const bool ok = plane < 3 && g4 < valid;
+  dma_global(buf, ok ? (const void*)(stats + (size_t)plane * n_tok + r0 + g4) : (const void*)&kZero16B);
 }
 
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
@@ -137,7 +143,7 @@ struct BwdArgs {
   const int32_t* sel;     // [S][m][n] selection, or null: no selected branch
   const int32_t* inv_off; // [S][m+1] inverted selection offsets
   const int32_t* inv_list;// [S][m*n] query blocks per key block
-  float* stats;           // [2][S][N][4] per branch (lse, D, g, 0); branch 0 selected, 1 local
+  float* stats;           // [2][S][3][N] per branch planes lse, D, g; branch 0 selected, 1 local
   float* dq;              // [S][N][D] fp32 out
   float* dk;
   float* dv;
@@ -345,8 +351,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
       lse[s] = st[s].m * c + log2f(st[s].l[0]);
       dsub[s] = g[s] * dg;
       if (lg == 0) {
-        *reinterpret_cast<float4*>(a.stats + (((size_t)br_id * a.slices + slice) * N + t) * 4) =
-            make_float4(lse[s], dsub[s], g[s], 0.f);
+        float* sp = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N + t;
+        sp[0] = lse[s];
+        sp[N] = dsub[s];
+        sp[2 * N] = g[s];
         if (a.dgates) a.dgates[((size_t)slice * N + t) * 3 + 1 + br_id] = dg;
       }
     }
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   using G = Dims<D>;
   constexpr int KK = G::KK, DT = G::DT;
   __shared__ __attribute__((aligned(16))) uint16_t QO[4 * 64 * D];   // Q0, dO0, Q1, dO1
-  __shared__ __attribute__((aligned(16))) float ST[2][64 * 4];        // per-query (lse, D, g, 0)
+  __shared__ __attribute__((aligned(16))) float ST[2][4 * 64];        // per-query lse[64], D[64], g[64]
   const int N = a.n_tok, B = a.block;
   const int tiles = N / kTile;
   const long long slice = blockIdx.x / tiles;
@@ -469,11 +477,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   // count chunk_valid(ci); LOCAL masks by the windows
   auto phase = [&](int br_id, int nc, auto chunk_row, auto chunk_valid, auto local) __attribute__((always_inline)) {
     constexpr bool LOCAL = decltype(local)::value;
-    const float* stats = a.stats + ((size_t)br_id * a.slices + slice) * N * 4;
+    const float* stats = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N;
     auto stage = [&](int ci, int p) __attribute__((always_inline)) {
       stage_rows<D>(Qb(p), qs, chunk_row(ci), chunk_valid(ci), w);
       stage_rows<D>(Ob(p), dos, chunk_row(ci), chunk_valid(ci), w);
-      stage_stats(&ST[p][0], stats, chunk_row(ci), chunk_valid(ci), w);
+      stage_stats(&ST[p][0], stats, chunk_row(ci), chunk_valid(ci), N, w);
     };
     if (nc <= 0) return;
     stage(0, 0);
@@ -512,24 +520,36 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
             }
           }
         bf16x8 pg[2], ds[2];
+        // P = exp2(S c - lse); P g and dS = P (g dP - D).  Padded rows and
+        // (local phase) keys outside the query's window get exponent -inf;
+        // key u is inside the window of query t iff u - t + lo_off < window
+        // (unsigned), and u - t is a per-lane base plus a constant.
+        const int dbase = uw + lr - r0 - 32 * j - 4 * lg + lo_off;
+        const int vbase = nv - 32 * j - 4 * lg;   // row qi valid iff qi - 32j - 4lg < vbase
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          const int q0 = 32 * j + 16 * h + 4 * lg;   // the lane's first query row of the chunk
+          const float4 lse4 = *reinterpret_cast<const float4*>(stt + q0);
+          const float4 d4 = *reinterpret_cast<const float4*>(stt + 64 + q0);
+          const float4 g4 = *reinterpret_cast<const float4*>(stt + 128 + q0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int qi = 32 * j + 16 * h + 4 * lg + i;   // query row of the chunk
-            const float4 q4 = *reinterpret_cast<const float4*>(stt + 4 * qi);   // (lse, D, g, 0)
+            const float lse = i == 0 ? lse4.x : i == 1 ? lse4.y : i == 2 ? lse4.z : lse4.w;
+            const float dd = i == 0 ? d4.x : i == 1 ? d4.y : i == 2 ? d4.z : d4.w;
+            const float gg = i == 0 ? g4.x : i == 1 ? g4.y : i == 2 ? g4.z : g4.w;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-              bool ok = qi < nv;
+              float x = fmaf(sa[s][h][i], c, -lse);
               if constexpr (LOCAL) {
-                const int u = uw + 16 * s + lr, t = r0 + qi;
-                ok = ok && u >= t - lo_off && u < t + hi_off;
+                const bool ok = 16 * h + i < vbase && (unsigned)(dbase + 16 * s - 16 * h - i) < (unsigned)a.window;
+                x = ok ? x : -INFINITY;
               }
-              const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sa[s][h][i], c, -q4.x)) : 0.f;
-              pg[s][4 * h + i] = static_cast<__bf16>(p * q4.z);
-              ds[s][4 * h + i] = static_cast<__bf16>(p * (q4.z * dpa[s][h][i] - q4.y));
+              const float p = __builtin_amdgcn_exp2f(x);
+              pg[s][4 * h + i] = static_cast<__bf16>(p * gg);
+              ds[s][4 * h + i] = static_cast<__bf16>(p * (gg * dpa[s][h][i] - dd));
             }
           }
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const bf16x8 ot = tr_operand<D>(ob, j, dt);
@@ -557,7 +577,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
           std::integral_constant<bool, false>{});
   }
   {
-    const int tlo = max(0, u0 - hi_off + 1);
+    const int tlo = max(0, u0 - hi_off + 1) & ~3;   // a multiple of 4 for the statistics staging
     const int thi = min(N, u0 + kTile + lo_off);
     phase(1, (thi - tlo + 63) / 64, [&](int ci) { return tlo + ci * 64; },
           [&](int ci) { return min(64, thi - tlo - ci * 64); }, std::integral_constant<bool, true>{});
@@ -658,41 +678,73 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 // ---------------------------------------------------------------------------
 // inverted selection, one workgroup per slice: off[j] .. off[j+1] indexes
 // the ascending list of query blocks whose selection holds key block j.
+// Counts and cursors live in LDS (m <= kIndexMaxBlocks); the entries are
+// scattered into `tmp` in arrival order and then each list is rank-sorted by
+// one wave into `list`, ordered by (query block, position in `tmp`) so that
+// the result is deterministic and a permutation even if a selection row
+// repeats an index.
 
-__global__ __launch_bounds__(256) void bwd_index_kernel(const int32_t* sel, int32_t* off, int32_t* cursor,
-                                                         int32_t* list, int m, int n) {
+constexpr int kIndexThreads = 1024;
+
+__global__ __launch_bounds__(kIndexThreads) void bwd_index_kernel(const int32_t* sel, int32_t* off, int32_t* tmp,
+                                                                   int32_t* list, int m, int n) {
+  __shared__ int32_t cnt[kIndexMaxBlocks + 1];
+  __shared__ int32_t wsum[kIndexThreads / 64];
   const long long slice = blockIdx.x;
-  const int32_t* s = sel + slice * m * n;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int total = m * n;
+  const int32_t* s = sel + slice * total;
   int32_t* o = off + slice * (m + 1);
-  int32_t* cur = cursor + slice * m;
-  int32_t* l = list + slice * m * n;
-  for (int j = threadIdx.x; j <= m; j += 256) o[j] = 0;
+  int32_t* t = tmp + slice * total;
+  int32_t* l = list + slice * total;
+  for (int j = tid; j < m; j += kIndexThreads) cnt[j] = 0;
   __syncthreads();
-  for (int e = threadIdx.x; e < m * n; e += 256) {
-    const int j = min(max(s[e], 0), m - 1);
-    atomicAdd(&o[j + 1], 1);
+  for (int e = tid; e < total; e += kIndexThreads) atomicAdd(&cnt[min(max(s[e], 0), m - 1)], 1);
+  __syncthreads();
+
+  // exclusive scan: each thread owns a contiguous run of counts
+  const int per = (m + kIndexThreads - 1) / kIndexThreads;
+  const int jb = min(tid * per, m), je = min(jb + per, m);
+  int run = 0;
+  for (int j = jb; j < je; ++j) run += cnt[j];
+  int incl = run;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
   }
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  if (threadIdx.x == 0)
-    for (int j = 0; j < m; ++j) o[j + 1] += o[j];
-  __syncthreads();
-  for (int j = threadIdx.x; j < m; j += 256) cur[j] = o[j];
-  __syncthreads();
-  for (int e = threadIdx.x; e < m * n; e += 256) {
-    const int j = min(max(s[e], 0), m - 1);
-    l[atomicAdd(&cur[j], 1)] = e / n;
+  int base = incl - run;
+  for (int x = 0; x < w; ++x) base += wsum[x];
+  for (int j = jb; j < je; ++j) {
+    const int c = cnt[j];
+    cnt[j] = base;
+    o[j] = base;
+    base += c;
   }
+  if (tid == 0) o[m] = total;
   __syncthreads();
-  for (int j = threadIdx.x; j < m; j += 256) {   // insertion sort of each (short) list
-    const int b = o[j], e = o[j + 1];
-    for (int x = b + 1; x < e; ++x) {
-      const int v = l[x];
-      int y = x - 1;
-      while (y >= b && l[y] > v) {
-        l[y + 1] = l[y];
-        --y;
+
+  for (int e = tid; e < total; e += kIndexThreads) t[atomicAdd(&cnt[min(max(s[e], 0), m - 1)], 1)] = e / n;
+  __syncthreads();
+
+  // rank sort, one wave per list: the element at position p of the list
+  // goes to the number of elements before it in (value, position) order
+  for (int j = w; j < m; j += kIndexThreads / 64) {
+    const int b = j ? cnt[j - 1] : 0, len = cnt[j] - b;   // cnt[j] is now the end of list j
+    for (int pc = 0; pc < len; pc += 64) {
+      const int p = pc + lane;
+      const int x = p < len ? t[b + p] : INT_MAX;
+      int rank = 0;
+      for (int qc = 0; qc < len; qc += 64) {
+        const int y = qc + lane < len ? t[b + qc + lane] : INT_MAX;
+        const int qn = min(64, len - qc);
+        for (int r = 0; r < qn; ++r) {
+          const int yr = __shfl(y, r);
+          rank += (yr < x) || (yr == x && qc + r < p);
+        }
       }
-      l[y + 1] = v;
+      if (p < len) l[b + rank] = x;
     }
   }
 }
@@ -725,8 +777,9 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // fine branches
-  hipLaunchKernelGGL(bwd_index_kernel, dim3((unsigned)S), dim3(256), 0, stream, L.sel, L.inv_off, L.inv_cursor,
-                     L.inv_list, m, L.topn);
+  if (m > kIndexMaxBlocks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_index_kernel, dim3((unsigned)S), dim3(kIndexThreads), 0, stream, L.sel, L.inv_off,
+                     L.inv_tmp, L.inv_list, m, L.topn);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   BwdArgs f = {};
   f.q = L.q; f.k = L.k; f.v = L.v; f.dob = L.dob; f.dof = L.dout; f.gates = L.gates; f.sel = L.sel;

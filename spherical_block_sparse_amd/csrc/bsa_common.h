@@ -162,15 +162,18 @@ struct BwdLaunch {
   uint16_t* qbar_b;         // bf16 pooled rows [S][m][d]
   uint16_t* kbar_b;
   uint16_t* vbar_b;
-  float* stats;             // [2][S][N][4]
-  float* stats_cg;          // [2][S][m][4]
+  float* stats;             // [2][S][3][N] planes lse, D, g
+  float* stats_cg;          // [2][S][3][m]
   float* dqbar;             // [S][m][d]
   float* dkbar;
   float* dvbar;
   int32_t* inv_off;         // [S][m+1]
-  int32_t* inv_cursor;      // [S][m]
+  int32_t* inv_tmp;         // [S][m*topn] unsorted inverted lists
   int32_t* inv_list;        // [S][m*topn]
 };
+
+// largest m = N/block the backward's inverted-selection kernel holds in LDS
+constexpr int kIndexMaxBlocks = 16384;
 
 hipError_t launch_backward(const BwdLaunch& L, hipStream_t stream);
 

@@ -101,7 +101,7 @@ Workspace layout(const Shape& s) {
 // statistics, pooled gradients and the inverted selection.
 struct BwdWorkspace {
   size_t qbar, kbar, vbar, ocg, sel, dob, docg, docg_b, qbar_b, kbar_b, vbar_b, stats, stats_cg, dqbar, dkbar,
-      dvbar, inv_off, inv_cur, inv_list, total;
+      dvbar, inv_off, inv_tmp, inv_list, total;
 };
 
 BwdWorkspace bwd_layout(const Shape& s) {
@@ -120,13 +120,13 @@ BwdWorkspace bwd_layout(const Shape& s) {
   w.qbar_b = take(em * sizeof(uint16_t));
   w.kbar_b = take(em * sizeof(uint16_t));
   w.vbar_b = take(em * sizeof(uint16_t));
-  w.stats = take((size_t)2 * s.slices * s.n_tok * 4 * sizeof(float));
-  w.stats_cg = take((size_t)2 * s.slices * s.m * 4 * sizeof(float));
+  w.stats = take((size_t)2 * s.slices * 3 * s.n_tok * sizeof(float));
+  w.stats_cg = take((size_t)2 * s.slices * 3 * s.m * sizeof(float));
   w.dqbar = take(em * sizeof(float));
   w.dkbar = take(em * sizeof(float));
   w.dvbar = take(em * sizeof(float));
   w.inv_off = take((size_t)s.slices * (s.m + 1) * sizeof(int32_t));
-  w.inv_cur = take((size_t)s.slices * s.m * sizeof(int32_t));
+  w.inv_tmp = take((size_t)s.slices * s.m * s.topn * sizeof(int32_t));
   w.inv_list = take((size_t)s.slices * s.m * s.topn * sizeof(int32_t));
   w.total = o;
   return w;
@@ -136,6 +136,8 @@ BwdWorkspace bwd_layout(const Shape& s) {
 mosaic_status check_backward_shape(const Shape& s) {
   if (s.block < 64) return fail(MOSAIC_ERR_UNSUPPORTED, "backward: block %d, the kernels need block >= 64", s.block);
   if (s.m % 64) return fail(MOSAIC_ERR_UNSUPPORTED, "backward: m = N/block = %d must be a multiple of 64", s.m);
+  if (s.m > mosaic::kIndexMaxBlocks)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "backward: m = N/block = %d, at most %d blocks", s.m, mosaic::kIndexMaxBlocks);
   return MOSAIC_OK;
 }
 
@@ -318,7 +320,7 @@ mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, c
   L.dkbar = reinterpret_cast<float*>(ws + w.dkbar);
   L.dvbar = reinterpret_cast<float*>(ws + w.dvbar);
   L.inv_off = reinterpret_cast<int32_t*>(ws + w.inv_off);
-  L.inv_cursor = reinterpret_cast<int32_t*>(ws + w.inv_cur);
+  L.inv_tmp = reinterpret_cast<int32_t*>(ws + w.inv_tmp);
   L.inv_list = reinterpret_cast<int32_t*>(ws + w.inv_list);
   // the forward's pooling and compressed branch (its own selection goes to
   // scratch: the backward uses the caller's)

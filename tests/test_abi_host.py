@@ -139,6 +139,8 @@ def test_backward_workspace_bytes():
     assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 64, 16) > 0
     assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 16, 16) == 0   # block < 64
     assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 16, 64, 16) == 0   # m = 48
+    assert L.mosaic_bsa_backward_workspace_bytes(1, 1, 64, 256, 64, 16) > 0   # m = 12288
+    assert L.mosaic_bsa_backward_workspace_bytes(1, 1, 64, 512, 64, 16) == 0  # m = 49152 > 16384
     # the largest section is the bf16 copy of dout plus the per-query statistics
     n, s = 12 * 32 * 32, 2
-    assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 64, 16) >= s * n * 64 * 2 + 2 * s * n * 16
+    assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 64, 16) >= s * n * 64 * 2 + 2 * s * n * 12
