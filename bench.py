@@ -8,7 +8,11 @@ synthetic HEALPix-NESTED fields already resident in HBM.  The default
 workload is Nside = 128 (24 ensemble members x 8 heads x head_dim 64, block
 64, top-n 16, window 512); the Nside = 256 workload (2 x 16 heads, block 256,
 top-n 8, window 1024) is measured in the same run and reported under
-"secondary".  Prints one JSON line.
+"secondary".  The training forward (mosaic_bsa_forward_train) and the
+backward from its saved state (mosaic_bsa_backward, float32 upstream
+gradient), and the backward that recomputes that state, are timed after each
+forward and reported under "backward"; they are not part of the step.
+Prints one JSON line.
 
 Roofline of the dominant kernel (the fine-attention kernel, bf16 MFMA):
 algorithmic FLOPs per launch = sum over queries of 4*d*(n*block + |window(t)|)
@@ -53,6 +57,14 @@ def fine_flops(cfg: BSAConfig) -> float:
     d = cfg.head_dim
     per_slice = 4 * d * (cfg.n_tokens * cfg.topn * cfg.block + window_keys_total(cfg.n_tokens, cfg.window))
     return float(per_slice) * cfg.slices
+
+
+def backward_flops(cfg: BSAConfig) -> float:
+    """Algorithmic FLOPs of the backward's fine branches: per (query, key) pair
+    of the selected and local sets, five products of 2*d FLOPs (S = QK^T
+    recomputed, dP = dO V^T, dV += P^T dO, dQ += dS K, dK += dS^T Q), i.e.
+    2.5x the forward's two; the pooled branch's m^2 share is left out."""
+    return 2.5 * fine_flops(cfg)
 
 
 def compress_flops(cfg: BSAConfig) -> float:
@@ -101,7 +113,7 @@ def time_stream(fn, steps: int) -> float:
     return start.elapsed_time(stop) / steps
 
 
-def measure(cfg: BSAConfig, steps: int, warmup: int) -> dict:
+def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> dict:
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     q, k, v, g = make_inputs(cfg, device="cuda", dtype=torch.bfloat16)
     b, h, n, d = cfg.batch, cfg.heads, cfg.n_tokens, cfg.head_dim
@@ -139,7 +151,40 @@ def measure(cfg: BSAConfig, steps: int, warmup: int) -> dict:
     same = bool(torch.equal(sel, sel2) and torch.equal(out, out2))
 
     ff = fine_flops(cfg)
-    res = dict(
+    bwd = None
+    if backward:
+        gen = torch.Generator(device=dev).manual_seed(cfg.seed + 7)
+        dout = torch.randn((b, h, n, d), generator=gen, device=dev, dtype=torch.float32)
+        grads = [torch.empty((b, h, n, d), dtype=torch.float32, device=dev) for _ in range(3)]
+        dgates = torch.empty((b, h, n, 3), dtype=torch.float32, device=dev)
+        bws = torch.empty(_lib.mosaic_bsa_backward_workspace_bytes(b, h, d, cfg.nside, cfg.block, cfg.topn),
+                          dtype=torch.uint8, device=dev)
+        saved = torch.empty(_lib.mosaic_bsa_saved_bytes(b, h, d, cfg.nside, cfg.block), dtype=torch.uint8,
+                            device=dev)
+        out_t, sel_t = torch.empty_like(out), torch.empty_like(sel)
+        fwd_t = lambda: _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                                      out=out_t, sel_idx=sel_t, saved=saved)
+        print(f"[bench] {cfg.name}: training forward + backward", file=sys.stderr, flush=True)
+        fwd_t()
+        kb = max(3, steps // 4)
+        fwd_t_ms = time_stream(fwd_t, kb)
+        bw = lambda: _lib.mosaic_bsa_backward(q, k, v, g, sel_t, dout, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                              *grads, dgates, workspace=bws, saved=saved)
+        bw_r = lambda: _lib.mosaic_bsa_backward(q, k, v, g, sel_t, dout, cfg.nside, cfg.block, cfg.topn,
+                                                cfg.window, *grads, dgates, workspace=bws)
+        bw()
+        bwd_ms = time_stream(bw, kb)
+        bw_r()
+        bwd_r_ms = time_stream(bw_r, kb)
+        bf = backward_flops(cfg)
+        bwd = {"ms": bwd_ms, "tokens_per_s": cfg.tokens / (bwd_ms * 1e-3), "algorithmic_flops": bf,
+               "achieved_TFLOPs": bf / (bwd_ms * 1e-3) / 1e12,
+               "frac_bf16_peak": bf / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "from": "mosaic_bsa_forward_train state",
+               "training_forward_ms": fwd_t_ms, "recompute_ms": bwd_r_ms,
+               "training_step_tokens_per_s": cfg.tokens / ((fwd_t_ms + bwd_ms) * 1e-3)}
+        del dout, grads, dgates, bws, saved, out_t, sel_t
+    res = dict(backward=bwd,
         cfg=cfg, ms=ms, tokens_per_s=cfg.tokens / (ms * 1e-3),
         pool_ms=pool_ms, cs_ms=cs_ms, fine_ms=fine_ms, stages_match_forward=same,
         fine_tflops=ff / (fine_ms * 1e-3) / 1e12, fine_flops=ff,
@@ -191,6 +236,7 @@ def main() -> int:
     ap.add_argument("--secondary", default="ns256", help="second workload reported alongside ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the (secondary) backward timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the BSA slices are independent and this build has no "
@@ -203,7 +249,7 @@ def main() -> int:
     _lib.lib()
 
     cfg = CONFIGS[args.config]
-    r = measure(cfg, args.steps, args.warmup)
+    r = measure(cfg, args.steps, args.warmup, backward=not args.no_backward)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, r["inputs"], args.cpu_budget)
@@ -212,7 +258,8 @@ def main() -> int:
 
     secondary = None
     if args.secondary and args.secondary != args.config:
-        s = measure(CONFIGS[args.secondary], max(5, args.steps // 2), max(2, args.warmup // 2))
+        s = measure(CONFIGS[args.secondary], max(5, args.steps // 2), max(2, args.warmup // 2),
+                    backward=not args.no_backward)
         del s["inputs"]
         secondary = {
             "workload": s["cfg"].name, "value": s["tokens_per_s"], "unit": "tokens/s", "ms_per_step": s["ms"],
@@ -220,6 +267,7 @@ def main() -> int:
             "fine_mfma_frac": s["fine_tflops"] / PEAK_BF16_TFLOPS,
             "compress_select_frac": compress_bound_ms(s["cfg"]) / s["cs_ms"],
             "pool_hbm_frac": s["pool_gbs"] / PEAK_HBM_GBS,
+            "backward": s["backward"],
         }
 
     c = r["cfg"]
@@ -261,6 +309,7 @@ def main() -> int:
             "fine": {"ms": r["fine_ms"], "frac_bf16_peak": r["fine_tflops"] / PEAK_BF16_TFLOPS},
             "stages_match_forward": r["stages_match_forward"],
         },
+        "backward": r["backward"],
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 1
+#define MOSAIC_BSA_ABI_VERSION 2
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -119,6 +119,26 @@ mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const
                               int head_dim, int nside, int block, int topn, int window, float* out,
                               void* stream);
 
+/* Bytes of the state mosaic_bsa_forward_train leaves for mosaic_bsa_backward,
+ * or 0 when the sizes are invalid or unsupported.  Layout (256-byte aligned
+ * sections): float32 o_FG_t, o_L_t [batch][heads][N][2][head_dim] (each
+ * normalised), float32 [batch][heads][N][2] their base-2 log-sum-exp of
+ * q_t·k_u·log2(e)/sqrt(d), then the forward workspace of
+ * mosaic_bsa_workspace_bytes (q̄, k̄, v̄, o_CG). */
+size_t mosaic_bsa_saved_bytes(int batch, int heads, int head_dim, int nside, int block);
+
+/* mosaic_bsa_forward for training: the same sel_idx and out (up to float32
+ * rounding of the gated sum), plus the state above in `saved` (in place of the
+ * workspace, at least mosaic_bsa_saved_bytes(...) bytes, 256-byte aligned),
+ * so that the backward need not recompute the pooled tensors, the compressed
+ * branch or the two fine branches' softmax statistics.  The papernotes.org
+ * ICML2026 notes (关键设计) describe a model trained end to end; this is the
+ * forward such training runs. */
+mosaic_status mosaic_bsa_forward_train(const void* q, const void* k, const void* v, const float* gates,
+                                       int batch, int heads, int head_dim, int nside, int block, int topn,
+                                       int window, float* out, int32_t* sel_idx, void* saved,
+                                       size_t saved_bytes, void* stream);
+
 /* Workspace bytes mosaic_bsa_backward needs for these sizes, or 0 when the
  * sizes are invalid or outside what the backward implements. */
 size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, int nside, int block,
@@ -135,21 +155,27 @@ size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, i
  *   sel_idx   in : int32 [batch][heads][m][topn], the forward's selection
  *                  (any valid block indices; clamped into [0, m))
  *   dout      in : float32 [batch][heads][N][head_dim]
+ *   saved     in : the state of mosaic_bsa_forward_train for the same q, k,
+ *                  v, gates and sizes (and sel_idx its selection), and its
+ *                  size in bytes; or NULL (saved_bytes ignored): the
+ *                  backward then recomputes that state itself
  *   dq, dk, dv out: float32 [batch][heads][N][head_dim], overwritten
  *   dgates    out: float32 [batch][heads][N][3], overwritten
  *   workspace in/out scratch of at least mosaic_bsa_backward_workspace_bytes(...)
- * All launches go to `stream`; the forward's pooling and compressed branch
- * are recomputed.  bf16 products with float32 accumulation (dout is rounded
- * to bf16 for the products; D = dout·o uses it in float32).  Besides the
- * forward's limits, block >= 64 and m = N/block a multiple of 64 and at most
- * 16384 are needed (MOSAIC_ERR_UNSUPPORTED otherwise).  Alignment: q, k, v, dout, dq, dk, dv 16
- * bytes; gates, sel_idx, dgates 4; workspace 256.  Errors as for the forward:
- * nothing is launched and the outputs are untouched. */
+ * All launches go to `stream`.  Without `saved` the forward's pooling,
+ * compressed branch and fine-branch statistics are recomputed.  bf16
+ * products with float32 accumulation (dout is rounded to bf16 for the
+ * products; D = dout·o uses it in float32).
+ * Besides the forward's limits, block >= 64 and m = N/block a multiple of 64
+ * and at most 16384 are needed (MOSAIC_ERR_UNSUPPORTED otherwise).
+ * Alignment: q, k, v, dout, dq, dk, dv 16 bytes; gates, sel_idx, dgates 4;
+ * workspace and saved 256.  Errors as for the forward: nothing is launched
+ * and the outputs are untouched. */
 mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, const float* gates,
                                   const int32_t* sel_idx, const float* dout, int batch, int heads,
-                                  int head_dim, int nside, int block, int topn, int window, float* dq,
-                                  float* dk, float* dv, float* dgates, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  int head_dim, int nside, int block, int topn, int window,
+                                  const void* saved, size_t saved_bytes, float* dq, float* dk, float* dv,
+                                  float* dgates, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

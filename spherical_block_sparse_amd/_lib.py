@@ -28,6 +28,7 @@ EXPORTED = (
     "mosaic_bsa_abi_version", "mosaic_status_string", "mosaic_last_error",
     "mosaic_bsa_workspace_bytes", "mosaic_bsa_forward", "mosaic_bsa_pool",
     "mosaic_bsa_compress_select", "mosaic_bsa_fine",
+    "mosaic_bsa_saved_bytes", "mosaic_bsa_forward_train",
     "mosaic_bsa_backward_workspace_bytes", "mosaic_bsa_backward",
 )
 
@@ -67,8 +68,12 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
         L.mosaic_bsa_backward_workspace_bytes.restype = S
         L.mosaic_bsa_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.mosaic_bsa_saved_bytes.restype = S
+        L.mosaic_bsa_saved_bytes.argtypes = [I, I, I, I, I]
+        L.mosaic_bsa_forward_train.restype = I
+        L.mosaic_bsa_forward_train.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, P, S, P]
         L.mosaic_bsa_backward.restype = I
-        L.mosaic_bsa_backward.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, S, P]
+        L.mosaic_bsa_backward.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, S, P, P, P, P, P, S, P]
         _lib = L
     return _lib
 
@@ -96,6 +101,15 @@ def _ptr(t: torch.Tensor, dtype: torch.dtype, shape: tuple, name: str) -> int:
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
     return t.data_ptr()
+
+
+def _saved_ptr(saved):
+    if saved is None:
+        return None
+    if not isinstance(saved, torch.Tensor) or saved.dtype != torch.uint8 or saved.dim() != 1 \
+            or saved.device.type != "cuda":
+        raise ValueError("saved must be the 1-D uint8 device tensor of mosaic_bsa_forward_train")
+    return saved.data_ptr()
 
 
 def _dims(q: torch.Tensor, nside: int):
@@ -182,14 +196,44 @@ def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, o
     return out
 
 
+def mosaic_bsa_saved_bytes(batch, heads, head_dim, nside, block) -> int:
+    return lib().mosaic_bsa_saved_bytes(batch, heads, head_dim, nside, block)
+
+
+def mosaic_bsa_forward_train(q, k, v, gates, nside, block, topn, window, out=None, sel_idx=None, saved=None,
+                             stream=None):
+    """mosaic_bsa_forward plus the state the backward reads: returns (out, sel_idx, saved), saved a
+    1-D uint8 device tensor of mosaic_bsa_saved_bytes(...) bytes."""
+    b, h, n, d = _dims(q, nside)
+    m = n // block
+    if out is None:
+        out = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((b, h, m, topn), dtype=torch.int32, device=q.device)
+    need = mosaic_bsa_saved_bytes(b, h, d, nside, block)
+    if saved is None:
+        saved = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if saved.dtype != torch.uint8 or saved.dim() != 1 or saved.device.type != "cuda":
+        raise ValueError("saved must be a 1-D uint8 device tensor")
+    _check(lib().mosaic_bsa_forward_train(
+        _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
+        _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
+        b, h, d, nside, block, topn, window,
+        _ptr(out, torch.float32, (b, h, n, d), "out"),
+        _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"),
+        saved.data_ptr(), saved.numel(), _stream(stream)))
+    return out, sel_idx, saved
+
+
 def mosaic_bsa_backward_workspace_bytes(batch, heads, head_dim, nside, block, topn) -> int:
     return lib().mosaic_bsa_backward_workspace_bytes(batch, heads, head_dim, nside, block, topn)
 
 
 def mosaic_bsa_backward(q, k, v, gates, sel_idx, dout, nside, block, topn, window, dq=None, dk=None, dv=None,
-                        dgates=None, workspace=None, stream=None):
+                        dgates=None, workspace=None, stream=None, saved=None):
     """dq, dk, dv [b,H,N,d] and dgates [b,H,N,3] (fp32): gradient of the forward's out given dout,
-    with the selection sel_idx held fixed."""
+    with the selection sel_idx held fixed.  `saved`: the state of mosaic_bsa_forward_train for
+    these inputs (None: recomputed)."""
     b, h, n, d = _dims(q, nside)
     m = n // block
     dq = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device) if dq is None else dq
@@ -206,6 +250,7 @@ def mosaic_bsa_backward(q, k, v, gates, sel_idx, dout, nside, block, topn, windo
         _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
         _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"), _ptr(dout, torch.float32, (b, h, n, d), "dout"),
         b, h, d, nside, block, topn, window,
+        _saved_ptr(saved), 0 if saved is None else saved.numel(),
         _ptr(dq, torch.float32, (b, h, n, d), "dq"), _ptr(dk, torch.float32, (b, h, n, d), "dk"),
         _ptr(dv, torch.float32, (b, h, n, d), "dv"), _ptr(dgates, torch.float32, (b, h, n, 3), "dgates"),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))

@@ -171,7 +171,7 @@ struct SubState {
   float m;                  // running max, raw units
 };
 
-template <int D, bool SEL>
+template <int D, bool SEL, bool PASS1>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
   using G = Dims<D>;
   constexpr int KK = G::KK, DT = G::DT;
@@ -283,79 +283,88 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
       }
     };
 
-    // pass 1: forward (online softmax) for o, the log-sum-exp and D
-    SubState<D> st[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st[s].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      st[s].l = floatx4{0.f, 0.f, 0.f, 0.f};
-      st[s].m = -INFINITY;
-    }
-    bf16x8 ones;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
-    sweep([&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
-      floatx4 acc[2][4];
-      scores(kb, acc);
-      mask(ci, acc);
-      bf16x8 pb[2][2];
+    float lse[2], dsub[2];
+    if constexpr (PASS1) {
+      // pass 1: forward (online softmax) for o, the log-sum-exp and D
+      SubState<D> st[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        float mx = acc[s][0][0];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[s][kt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(st[s].m, mx);
-        const float alpha = st[s].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st[s].m - mnew) * c);
-        st[s].m = mnew;
-        st[s].l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st[s].o[dt] *= alpha;
-        const float nmc = mnew == -INFINITY ? 0.f : -mnew * c;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pb[s][kt >> 1][4 * (kt & 1) + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(acc[s][kt][i], c, nmc)));
+        for (int dt = 0; dt < DT; ++dt) st[s].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        st[s].l = floatx4{0.f, 0.f, 0.f, 0.f};
+        st[s].m = -INFINITY;
       }
+      bf16x8 ones;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
+      sweep([&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
+        floatx4 acc[2][4];
+        scores(kb, acc);
+        mask(ci, acc);
+        bf16x8 pb[2][2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) st[s].l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[s][j], st[s].l, 0, 0, 0);
+        for (int s = 0; s < 2; ++s) {
+          float mx = acc[s][0][0];
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[s][kt][i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mnew = fmaxf(st[s].m, mx);
+          const float alpha = st[s].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st[s].m - mnew) * c);
+          st[s].m = mnew;
+          st[s].l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) st[s].o[dt] *= alpha;
+          const float nmc = mnew == -INFINITY ? 0.f : -mnew * c;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pb[s][kt >> 1][4 * (kt & 1) + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(acc[s][kt][i], c, nmc)));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s) st[s].l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[s][j], st[s].l, 0, 0, 0);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8 va = tr_operand<D>(vb, j, dt);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) st[s].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[s][j], st[s].o[dt], 0, 0, 0);
+          }
+        }
+      });
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int t = tw + 16 * s + lr;
+        const float inv_l = 1.f / st[s].l[0];
+        float dg = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 va = tr_operand<D>(vb, j, dt);
-#pragma unroll
-          for (int s = 0; s < 2; ++s) st[s].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[s][j], st[s].o[dt], 0, 0, 0);
+          const float4 d4 = *reinterpret_cast<const float4*>(dofs + (size_t)t * D + dt * 16 + 4 * lg);
+          dg += d4.x * st[s].o[dt][0] + d4.y * st[s].o[dt][1] + d4.z * st[s].o[dt][2] + d4.w * st[s].o[dt][3];
+        }
+        dg *= inv_l;
+        dg += __shfl_xor(dg, 16);
+        dg += __shfl_xor(dg, 32);
+        lse[s] = st[s].m * c + log2f(st[s].l[0]);
+        dsub[s] = g[s] * dg;
+        if (lg == 0) {
+          float* sp = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N + t;
+          sp[0] = lse[s];
+          sp[N] = dsub[s];
+          sp[2 * N] = g[s];
+          if (a.dgates) a.dgates[((size_t)slice * N + t) * 3 + 1 + br_id] = dg;
         }
       }
-    });
-    float lse[2], dsub[2];
+    } else {   // the training forward saved lse; the prep kernel formed D and dgates
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int t = tw + 16 * s + lr;
-      const float inv_l = 1.f / st[s].l[0];
-      float dg = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const float4 d4 = *reinterpret_cast<const float4*>(dofs + (size_t)t * D + dt * 16 + 4 * lg);
-        dg += d4.x * st[s].o[dt][0] + d4.y * st[s].o[dt][1] + d4.z * st[s].o[dt][2] + d4.w * st[s].o[dt][3];
-      }
-      dg *= inv_l;
-      dg += __shfl_xor(dg, 16);
-      dg += __shfl_xor(dg, 32);
-      lse[s] = st[s].m * c + log2f(st[s].l[0]);
-      dsub[s] = g[s] * dg;
-      if (lg == 0) {
-        float* sp = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N + t;
-        sp[0] = lse[s];
-        sp[N] = dsub[s];
-        sp[2 * N] = g[s];
-        if (a.dgates) a.dgates[((size_t)slice * N + t) * 3 + 1 + br_id] = dg;
+      for (int s = 0; s < 2; ++s) {
+        const float* sp = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N + tw + 16 * s + lr;
+        lse[s] = sp[0];
+        dsub[s] = sp[N];
       }
     }
 
@@ -626,7 +635,11 @@ struct PrepArgs {
   uint16_t* qbar_b;        // out bf16 [S][m][D]
   uint16_t* kbar_b;
   uint16_t* vbar_b;
-  float* dgates;           // out column 0 (or null)
+  float* dgates;           // out column 0 (or null); with save_o also columns 1, 2
+  const float* save_o;     // [S][N][2][D] o_FG, o_L of the training forward, or null
+  const float* save_lse;   // [S][N][2]
+  float* stats;            // with save_o: out [2][S][3][N] planes lse, D = g dg, g
+  long long slices;
   int n_tok, block, m;
 };
 
@@ -658,6 +671,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int sh = 1; sh < C4; sh <<= 1) dg += __shfl_xor(dg, sh);
     if (c4 == 0 && a.dgates) a.dgates[row * 3] = dg;
+    if (a.save_o) {   // dg_br = dO·o_br for the selected (0) and local (1) branches
+#pragma unroll
+      for (int br = 0; br < 2; ++br) {
+        const float4 ob = *reinterpret_cast<const float4*>(a.save_o + (row * 2 + br) * D + 4 * c4);
+        float e = d4.x * ob.x + d4.y * ob.y + d4.z * ob.z + d4.w * ob.w;
+#pragma unroll
+        for (int sh = 1; sh < C4; sh <<= 1) e += __shfl_xor(e, sh);
+        if (c4 == 0) {
+          const float gb = a.gates[row * 3 + 1 + br];
+          float* sp = a.stats + ((size_t)br * a.slices + slice) * 3 * a.n_tok + t;
+          sp[0] = a.save_lse[row * 2 + br];
+          sp[a.n_tok] = gb * e;
+          sp[2 * (size_t)a.n_tok] = gb;
+          a.dgates[row * 3 + 1 + br] = e;
+        }
+      }
+    }
   }
   part[r0][4 * c4 + 0] = acc.x;
   part[r0][4 * c4 + 1] = acc.y;
@@ -758,6 +788,7 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
   p.dout = L.dout; p.gates = L.gates; p.o_cg = L.o_cg; p.qbar = L.qbar; p.kbar = L.kbar; p.vbar = L.vbar;
   p.dob = L.dob; p.docg = L.docg; p.docg_b = L.docg_b; p.qbar_b = L.qbar_b; p.kbar_b = L.kbar_b; p.vbar_b = L.vbar_b;
   p.dgates = L.dgates; p.n_tok = N; p.block = L.block; p.m = m;
+  p.save_o = L.save_o; p.save_lse = L.save_lse; p.stats = L.stats; p.slices = S;
   hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)(S * m)), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -771,7 +802,7 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
   cg.dq = L.dqbar; cg.dk = L.dkbar; cg.dv = L.dvbar; cg.dgates = nullptr;
   cg.n_tok = m; cg.block = 1; cg.topn = 0; cg.window = 2 * m + 1; cg.m = m; cg.slices = S;
   cg.scale_log2 = c; cg.inv_sqrt_d = isd;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)(S * (m / kTile))), dim3(64 * kWaves), 0, stream, cg);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), dim3((unsigned)(S * (m / kTile))), dim3(64 * kWaves), 0, stream, cg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)(S * (m / kTile))), dim3(64 * kWaves), 0, stream, cg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -788,7 +819,12 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
   f.addq = L.dqbar; f.addk = L.dkbar; f.addv = L.dvbar;
   f.n_tok = N; f.block = L.block; f.topn = L.topn; f.window = L.window; f.m = m; f.slices = S;
   f.scale_log2 = c; f.inv_sqrt_d = isd;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)(S * (N / kTile))), dim3(64 * kWaves), 0, stream, f);
+  if (L.save_o)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), dim3((unsigned)(S * (N / kTile))), dim3(64 * kWaves), 0, stream,
+                       f);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3((unsigned)(S * (N / kTile))), dim3(64 * kWaves), 0, stream,
+                       f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)(S * (N / kTile))), dim3(64 * kWaves), 0, stream, f);
   return hipGetLastError();

@@ -131,10 +131,12 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
                                   float* o_cg, int32_t* sel, long long slices, int m, int head_dim,
                                   int topn, hipStream_t stream);
 
+// save_o / save_lse non-null: also write each query's normalised selected and
+// local branch outputs (float32 [S][N][2][D]) and their log2-sum-exp ([S][N][2])
 hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gates,
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
-                       hipStream_t stream);
+                       hipStream_t stream, float* save_o = nullptr, float* save_lse = nullptr);
 
 // Everything the backward launches read and write (device pointers; the
 // workspace buffers are carved by the C-ABI entry point).
@@ -152,10 +154,12 @@ struct BwdLaunch {
   int head_dim;
   long long slices;
   int n_tok, block, topn, window;
-  const double* qbar;       // recomputed pooled means [S][m][d]
+  const double* qbar;       // pooled means [S][m][d] (recomputed, or the training forward's)
   const double* kbar;
   const float* vbar;
-  const float* o_cg;        // recomputed compressed output [S][m][d]
+  const float* o_cg;        // compressed output [S][m][d] (likewise)
+  const float* save_o;      // training forward's o_FG, o_L [S][N][2][d], or null: recompute
+  const float* save_lse;    // their log2-sum-exp [S][N][2]
   uint16_t* dob;            // workspace: bf16 dO [S][N][d]
   float* docg;              // [S][m][d] and its bf16 copy
   uint16_t* docg_b;

@@ -44,7 +44,10 @@
 //   * workgroup ids are remapped so each XCD (dispatched round-robin) gets a
 //     contiguous run of tiles: neighbouring tiles share window keys and
 //     largely the same selected blocks, and they now share an L2.
-//   * epilogue: out = g0·o_CG[t/block] + g1·o_FG + g2·o_L, float32.
+//   * epilogue: out = g0·o_CG[t/block] + g1·o_FG + g2·o_L, float32.  The
+//     SAVE instantiation (training forward) also stores o_FG, o_L (float32)
+//     and their log2-sum-exp, which the backward reads instead of
+//     recomputing both branches.
 // Roofline: bf16 matrix work 4*d*(n*block + W) per query, HBM traffic at
 // least q, k, v once plus gates, o_CG and out.
 #include "bsa_common.h"
@@ -62,6 +65,8 @@ struct FineArgs {
   const float* o_cg;
   const int32_t* sel;
   float* out;
+  float* save_o;      // [S][N][2][D] o_FG, o_L (normalised), SAVE only
+  float* save_lse;    // [S][N][2] their log2-sum-exp (log2 units of S*log2(e)/sqrt(d)), SAVE only
   int n_tok;
   int block;
   int topn;
@@ -284,7 +289,7 @@ __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
 // this wave are outstanding (lgkm and exp counters not waited on)
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
 
-template <int D, int WAVES>
+template <int D, int WAVES, bool SAVE>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void fine_kernel(FineArgs a) {
   constexpr int KK = Tile<D>::KK, DT = Tile<D>::DT;
   constexpr int T = 32 * WAVES;           // queries per workgroup
@@ -443,9 +448,26 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int s = 0; s < 2; ++s) branch_init(br[s]);
   float4 pre[2][DT];   // g_CG*o_CG + g_FG*o_FG, formed when the selected branch ends
 
+  // SAVE: the branch's normalised output and log2-sum-exp m*c + log2(l) of
+  // this lane's query, for a backward pass that then skips recomputing them
+  // (float32: the backward's D = dO·o must match the weights it recomputes
+  // closely, or dQ picks up D's error times the weighted mean key)
+  auto save_branch = [&](int s, int which) __attribute__((always_inline)) {
+    const int tq = tw + 16 * s + lr;
+    const size_t row = (size_t)slice * N + tq;
+    const float inv_l = 1.f / br[s].l[0];
+    float* dst = a.save_o + (row * 2 + which) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(dst + dt * 16 + 4 * lg) =
+          make_float4(br[s].o[dt][0] * inv_l, br[s].o[dt][1] * inv_l, br[s].o[dt][2] * inv_l, br[s].o[dt][3] * inv_l);
+    if (lg == 0) a.save_lse[row * 2 + which] = br[s].m * c + log2f(br[s].l[0]);
+  };
+
   auto finish_selected = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      if constexpr (SAVE) save_branch(s, 0);
       const int tq = tw + 16 * s + lr;
       const float* g = a.gates + ((size_t)slice * N + tq) * 3;
       const float g0 = g[0], g1 = g[1] / br[s].l[0];
@@ -536,6 +558,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   // gated sum: pre + g_L * o_L
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
+    if constexpr (SAVE) save_branch(s, 1);
     const int tq = tw + 16 * s + lr;
     const float g2 = a.gates[((size_t)slice * N + tq) * 3 + 2] / br[s].l[0];
     float* dst = a.out + ((size_t)slice * N + tq) * D;
@@ -558,7 +581,10 @@ hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
   a.tiles = a.n_tok / (32 * WAVES);
   a.groups = slices * a.tiles;
   dim3 grid((unsigned)a.groups);
-  hipLaunchKernelGGL((fine_kernel<D, WAVES>), grid, dim3(64 * WAVES), 0, stream, a);
+  if (a.save_o)
+    hipLaunchKernelGGL((fine_kernel<D, WAVES, true>), grid, dim3(64 * WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fine_kernel<D, WAVES, false>), grid, dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -567,7 +593,7 @@ hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
 hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gates,
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
-                       hipStream_t stream) {
+                       hipStream_t stream, float* save_o, float* save_lse) {
   FineArgs a;
   a.q = q;
   a.k = k;
@@ -576,6 +602,8 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.o_cg = o_cg;
   a.sel = sel;
   a.out = out;
+  a.save_o = save_o;
+  a.save_lse = save_lse;
   a.n_tok = n_tok;
   a.block = block;
   a.topn = topn;

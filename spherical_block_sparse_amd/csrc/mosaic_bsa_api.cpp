@@ -97,6 +97,23 @@ Workspace layout(const Shape& s) {
   return w;
 }
 
+// State the training forward leaves for the backward: the branch outputs
+// and log2-sum-exps of the fine kernel, then the pooled rows and the
+// compressed output (in the forward's own workspace layout).
+struct Saved {
+  size_t o, lse, pooled, total;
+};
+
+Saved saved_layout(const Shape& s) {
+  const size_t en = (size_t)s.slices * s.n_tok;
+  Saved v;
+  v.o = 0;
+  v.lse = align256(en * 2 * s.d * sizeof(float));
+  v.pooled = v.lse + align256(en * 2 * sizeof(float));
+  v.total = v.pooled + layout(s).total;
+  return v;
+}
+
 // Backward workspace: recomputed forward pieces, bf16 copies, per-query
 // statistics, pooled gradients and the inverted selection.
 struct BwdWorkspace {
@@ -258,6 +275,47 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
   return hip_status(e, "bsa_fine launch");
 }
 
+size_t mosaic_bsa_saved_bytes(int batch, int heads, int head_dim, int nside, int block) {
+  Shape s;
+  if (check_shape(batch, heads, head_dim, nside, block, 0, 0, 0, &s) != MOSAIC_OK) return 0;
+  return saved_layout(s).total;
+}
+
+mosaic_status mosaic_bsa_forward_train(const void* q, const void* k, const void* v, const float* gates,
+                                       int batch, int heads, int head_dim, int nside, int block, int topn,
+                                       int window, float* out, int32_t* sel_idx, void* saved,
+                                       size_t saved_bytes, void* stream) {
+  REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(out);
+  REQUIRE_PTR(sel_idx); REQUIRE_PTR(saved);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
+  REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(saved, 256);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
+  if (st != MOSAIC_OK) return st;
+  const Saved sv = saved_layout(s);
+  if (saved_bytes < sv.total)
+    return fail(MOSAIC_ERR_WORKSPACE, "saved buffer of %zu bytes, %zu needed", saved_bytes, sv.total);
+  char* base = static_cast<char*>(saved);
+  const Workspace w = layout(s);
+  char* ws = base + sv.pooled;
+  double* qbar = reinterpret_cast<double*>(ws + w.qbar);
+  double* kbar = reinterpret_cast<double*>(ws + w.kbar);
+  float* vbar = reinterpret_cast<float*>(ws + w.vbar);
+  float* ocg = reinterpret_cast<float*>(ws + w.ocg);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
+                                     s.d, s.block, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
+                          s.block, s.topn, s.window, hs, reinterpret_cast<float*>(base + sv.o),
+                          reinterpret_cast<float*>(base + sv.lse));
+  return hip_status(e, "bsa_fine launch");
+}
+
 size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn) {
   Shape s;
   if (check_shape(batch, heads, head_dim, nside, block, topn, 0, kUsesTopn, &s) != MOSAIC_OK) return 0;
@@ -267,13 +325,15 @@ size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, i
 
 mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, const float* gates,
                                   const int32_t* sel_idx, const float* dout, int batch, int heads, int head_dim,
-                                  int nside, int block, int topn, int window, float* dq, float* dk, float* dv,
-                                  float* dgates, void* workspace, size_t workspace_bytes, void* stream) {
+                                  int nside, int block, int topn, int window, const void* saved,
+                                  size_t saved_bytes, float* dq, float* dk, float* dv, float* dgates,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(sel_idx); REQUIRE_PTR(dout);
   REQUIRE_PTR(dq); REQUIRE_PTR(dk); REQUIRE_PTR(dv); REQUIRE_PTR(dgates); REQUIRE_PTR(workspace);
   REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
   REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(dout, 16); REQUIRE_ALIGN(dq, 16); REQUIRE_ALIGN(dk, 16);
   REQUIRE_ALIGN(dv, 16); REQUIRE_ALIGN(dgates, 4); REQUIRE_ALIGN(workspace, 256);
+  if (saved) REQUIRE_ALIGN(saved, 256);
   Shape s;
   mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
   if (st != MOSAIC_OK) return st;
@@ -281,6 +341,9 @@ mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, c
   const BwdWorkspace w = bwd_layout(s);
   if (workspace_bytes < w.total)
     return fail(MOSAIC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
+  const Saved sv = saved_layout(s);
+  if (saved && saved_bytes < sv.total)
+    return fail(MOSAIC_ERR_WORKSPACE, "saved buffer of %zu bytes, %zu needed", saved_bytes, sv.total);
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   mosaic::BwdLaunch L;
@@ -304,6 +367,18 @@ mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, c
   double* kbar = reinterpret_cast<double*>(ws + w.kbar);
   float* vbar = reinterpret_cast<float*>(ws + w.vbar);
   float* ocg = reinterpret_cast<float*>(ws + w.ocg);
+  L.save_o = nullptr;
+  L.save_lse = nullptr;
+  if (saved) {   // the training forward's pooled rows, compressed output and branch state
+    const char* sb = static_cast<const char*>(saved);
+    const Workspace fw = layout(s);
+    qbar = reinterpret_cast<double*>(const_cast<char*>(sb + sv.pooled + fw.qbar));
+    kbar = reinterpret_cast<double*>(const_cast<char*>(sb + sv.pooled + fw.kbar));
+    vbar = reinterpret_cast<float*>(const_cast<char*>(sb + sv.pooled + fw.vbar));
+    ocg = reinterpret_cast<float*>(const_cast<char*>(sb + sv.pooled + fw.ocg));
+    L.save_o = reinterpret_cast<const float*>(sb + sv.o);
+    L.save_lse = reinterpret_cast<const float*>(sb + sv.lse);
+  }
   L.qbar = qbar;
   L.kbar = kbar;
   L.vbar = vbar;
@@ -322,13 +397,15 @@ mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, c
   L.inv_off = reinterpret_cast<int32_t*>(ws + w.inv_off);
   L.inv_tmp = reinterpret_cast<int32_t*>(ws + w.inv_tmp);
   L.inv_list = reinterpret_cast<int32_t*>(ws + w.inv_list);
-  // the forward's pooling and compressed branch (its own selection goes to
-  // scratch: the backward uses the caller's)
-  hipError_t e = mosaic::launch_pool(L.q, L.k, L.v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs);
-  if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
-  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, reinterpret_cast<int32_t*>(ws + w.sel), s.slices, s.m,
-                                     s.d, s.topn, hs);
-  if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  if (!saved) {
+    // recompute the forward's pooling and compressed branch (its own
+    // selection goes to scratch: the backward uses the caller's)
+    hipError_t e = mosaic::launch_pool(L.q, L.k, L.v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs);
+    if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
+    e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, reinterpret_cast<int32_t*>(ws + w.sel), s.slices,
+                                       s.m, s.d, s.topn, hs);
+    if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  }
   return hip_status(mosaic::launch_backward(L, hs), "bsa_backward launch");
 }
 

@@ -41,7 +41,7 @@ def test_header_declares_and_library_exports_the_same_symbols():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.mosaic_bsa_abi_version() == 1
+    assert L.mosaic_bsa_abi_version() == 2
     for code, name in _lib.STATUS_NAMES.items():
         assert L.mosaic_status_string(code).decode() == name
     assert L.mosaic_status_string(99).decode() == "MOSAIC_ERR_UNKNOWN"
@@ -110,12 +110,22 @@ def test_python_binding_rejects_bad_tensors_without_launch():
 
 
 def bwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, sel=FAKE, dout=FAKE, batch=1, heads=2, d=64, nside=32, block=64,
-        topn=16, window=256, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, ws=FAKE, ws_bytes=None):
+        topn=16, window=256, saved=None, saved_bytes=0, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, ws=FAKE,
+        ws_bytes=None):
     L = _lib.lib()
     if ws_bytes is None:
         ws_bytes = 1 << 40
     return L.mosaic_bsa_backward(q, k, v, gates, sel, dout, batch, heads, d, nside, block, topn, window,
-                                 dq, dk, dv, dg, ws, ws_bytes, None)
+                                 saved, saved_bytes, dq, dk, dv, dg, ws, ws_bytes, None)
+
+
+def fwd_train(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=64, nside=32, block=64, topn=16,
+              window=256, out=FAKE, sel=FAKE, saved=FAKE, saved_bytes=None):
+    L = _lib.lib()
+    if saved_bytes is None:
+        saved_bytes = 1 << 40
+    return L.mosaic_bsa_forward_train(q, k, v, gates, batch, heads, d, nside, block, topn, window, out, sel,
+                                      saved, saved_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -128,10 +138,34 @@ def bwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, sel=FAKE, dout=FAKE, batch=1, heads=
     (dict(nside=16, block=64), UNSUP),           # m = 48, not a multiple of 64
     (dict(d=48), UNSUP),
     (dict(ws_bytes=1000), WS),
+    (dict(saved=FAKE + 16, saved_bytes=1 << 40), MISAL),
+    (dict(saved=FAKE, saved_bytes=1000), WS),    # a saved state smaller than mosaic_bsa_saved_bytes
 ])
 def test_backward_validation(kw, code):
     assert bwd(**kw) == code
     assert _lib.lib().mosaic_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(gates=None), NULL), (dict(out=None), NULL), (dict(sel=None), NULL),
+    (dict(saved=None), NULL), (dict(saved=FAKE + 64), MISAL), (dict(out=FAKE + 4), MISAL),
+    (dict(saved_bytes=4096), WS), (dict(window=0), SHAPE), (dict(topn=0), SHAPE), (dict(d=16), UNSUP),
+])
+def test_forward_train_validation(kw, code):
+    assert fwd_train(**kw) == code
+    assert _lib.lib().mosaic_last_error().decode() != ""
+
+
+def test_saved_bytes():
+    L = _lib.lib()
+    b, h, d, nside, block = 1, 2, 64, 32, 64
+    n, m, s = 12 * nside * nside, 12 * nside * nside // block, b * h
+    got = L.mosaic_bsa_saved_bytes(b, h, d, nside, block)
+    # float32 branch outputs + float32 log-sum-exps + the forward workspace, in 256-byte sections
+    assert got >= s * n * 2 * d * 4 + s * n * 2 * 4 + L.mosaic_bsa_workspace_bytes(b, h, d, nside, block, 1)
+    assert got < s * n * 2 * d * 4 + s * n * 2 * 4 + L.mosaic_bsa_workspace_bytes(b, h, d, nside, block, 1) + 1024
+    assert L.mosaic_bsa_saved_bytes(b, h, d, nside, 32) == 0      # not a power of four
+    assert L.mosaic_bsa_saved_bytes(b, h, 48, nside, block) == 0  # head_dim
 
 
 def test_backward_workspace_bytes():

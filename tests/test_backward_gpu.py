@@ -72,3 +72,76 @@ def test_backward_correlated_field_head_dim_32():
 def test_backward_block_256():
     # N = 49152, block 256 (m = 192, four 64-query chunks per block), top-4
     _run(BSAConfig("ns64-b256", 64, 1, 1, 64, 256, 4, 300, "fourier", 34))
+
+
+def _saved_views(saved: torch.Tensor, cfg: BSAConfig):
+    """(o [S][N][2][d], lse [S][N][2]) from the training forward's state (layout of
+    mosaic_bsa_saved_bytes: float32 branch outputs, then float32 log2-sum-exps, 256-byte sections)."""
+    s, n, d = cfg.batch * cfg.heads, cfg.n_tokens, cfg.head_dim
+    o_bytes = s * n * 2 * d * 4
+    o = saved[:o_bytes].view(torch.float32).view(s, n, 2, d)
+    lse_off = (o_bytes + 255) // 256 * 256
+    lse = saved[lse_off:lse_off + s * n * 2 * 4].view(torch.float32).view(s, n, 2)
+    return o, lse
+
+
+@pytest.mark.parametrize("cfg", [
+    BSAConfig("ns32-train", 32, 1, 2, 64, 64, 16, 256, "iid", 35),
+    BSAConfig("ns64-b256-train", 64, 1, 1, 64, 256, 4, 300, "fourier", 36),
+    BSAConfig("ns32-d32-train", 32, 1, 1, 32, 64, 8, 100, "fourier", 37),
+], ids=lambda c: c.name)
+def test_training_forward_state_and_backward(cfg):
+    dev = "cuda"
+    q, k, v, g = make_inputs(cfg, device=dev)
+    out0, sel0 = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    out, sel, saved = _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    torch.cuda.synchronize()
+    # the same selection; the same outputs up to float32 rounding of the gated sum
+    assert torch.equal(sel, sel0)
+    diff = float((out - out0).abs().max())
+    log(f"{cfg.name} training forward vs forward: max-abs {diff:.3e}")
+    assert diff <= 1e-6 * float(out0.abs().max())
+
+    # the saved branch outputs and log2-sum-exps against the oracle, slice 0
+    o, lse = _saved_views(saved, cfg)
+    q0, k0, v0 = (to_f64(x)[0, 0] for x in (q, k, v))
+    idx = sel[0, 0].cpu().numpy()
+    o_fg = oracle.fine_selected_branch(q0, k0, v0, idx, cfg.block)
+    o_l = oracle.local_branch(q0, k0, v0, cfg.window)
+    for br, want in ((0, o_fg), (1, o_l)):
+        got = o[0, :, br].double().cpu().numpy()
+        err = float(np.abs(got - want).max())
+        log(f"{cfg.name} saved o[{br}] max-abs {err:.3e}")
+        assert err <= 1e-2
+    # log2-sum-exp of q_t.k_u log2(e)/sqrt(d) over each branch's keys, for sampled queries
+    d = cfg.head_dim
+    rng = np.random.default_rng(cfg.seed)
+    ts = rng.choice(cfg.n_tokens, size=64, replace=False)
+    lo = np.maximum(ts - cfg.window // 2, 0)
+    hi = np.minimum(ts + (cfg.window + 1) // 2, cfg.n_tokens)
+    for j, t in enumerate(ts):
+        blocks = idx[t // cfg.block]
+        keys = (blocks[:, None] * cfg.block + np.arange(cfg.block)).ravel()
+        for br, ks in ((0, keys), (1, np.arange(lo[j], hi[j]))):
+            sc = k0[ks] @ q0[t] / np.sqrt(d)
+            want = (sc.max() + np.log(np.exp(sc - sc.max()).sum())) / np.log(2.0)
+            assert abs(float(lse[0, t, br]) - want) <= 2e-2 + 1e-3 * abs(want), (t, br)
+
+    # backward from the saved state against the float64 oracle
+    gen = torch.Generator(device=dev).manual_seed(2000 + cfg.seed)
+    dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32)
+    dq, dk, dv, dg = _lib.mosaic_bsa_backward(q, k, v, g, sel, dout, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                              saved=saved)
+    torch.cuda.synchronize()
+    ref = oracle.bsa_backward_ref(to_f64(q), to_f64(k), to_f64(v), g.double().cpu().numpy(),
+                                  dout.double().cpu().numpy(), cfg.block, cfg.topn, cfg.window,
+                                  idx=sel.cpu().numpy())
+    for name, t in dict(dq=dq, dk=dk, dv=dv, dgates=dg).items():
+        got = t.double().cpu().numpy()
+        want = ref[name]
+        assert np.all(np.isfinite(got)), name
+        rel_l2 = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+        max_rel = float(np.abs(got - want).max()) / float(np.abs(want).max())
+        log(f"{cfg.name} saved-state {name}: rel-L2 {rel_l2:.3e}, max-abs/max {max_rel:.3e}")
+        assert rel_l2 <= REL_L2, (name, rel_l2)
+        assert max_rel <= MAX_REL, (name, max_rel)
