@@ -182,7 +182,8 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
                "frac_bf16_peak": bf / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                "from": "mosaic_bsa_forward_train state",
                "training_forward_ms": fwd_t_ms, "recompute_ms": bwd_r_ms,
-               "training_step_tokens_per_s": cfg.tokens / ((fwd_t_ms + bwd_ms) * 1e-3)}
+               "training_step_tokens_per_s": cfg.tokens / ((fwd_t_ms + bwd_ms) * 1e-3),
+               "traffic": {"dq": measured_traffic(f"dq_{cfg.name}"), "dkdv": measured_traffic(f"dkdv_{cfg.name}")}}
         del dout, grads, dgates, bws, saved, out_t, sel_t
     res = dict(backward=bwd,
         cfg=cfg, ms=ms, tokens_per_s=cfg.tokens / (ms * 1e-3),
@@ -293,7 +294,7 @@ def main() -> int:
             "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "mfma", "kernel": "bsa_fine (fine_kernel<64>)",
+            "bound": "mfma", "kernel": "bsa_fine (fine_kernel<64, WAVES, false>)",
             "achieved": r["fine_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": r["fine_tflops"] / PEAK_BF16_TFLOPS, "traffic": measured_traffic(f"fine_{c.name}"),
             "flops_per_launch": r["fine_flops"], "ms_per_launch": r["fine_ms"],

@@ -133,6 +133,15 @@ __device__ __forceinline__ void stage_stats(float* buf, const float* stats, long
 
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
 
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2: renumber them so that XCD x runs a contiguous run of tiles.
+// Neighbouring tiles share window rows and mostly the same selected blocks,
+// which then hit in one L2.
+__device__ __forceinline__ long long xcd_contiguous(long long b, long long groups) {
+  const long long q8 = groups / 8, r8 = groups % 8, xcd = b % 8, k = b / 8;
+  return xcd < r8 ? xcd * (q8 + 1) + k : r8 * (q8 + 1) + (xcd - r8) * q8 + k;
+}
+
 struct BwdArgs {
   const uint16_t* q;      // bf16 [S][N][D]
   const uint16_t* k;
@@ -179,8 +188,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ int SelT[64];
   const int N = a.n_tok, B = a.block, n = a.topn;
   const int tiles = N / kTile;
-  const long long slice = blockIdx.x / tiles;
-  const int t0 = (int)(blockIdx.x % tiles) * kTile;
+  const long long tile = xcd_contiguous(blockIdx.x, gridDim.x);
+  const long long slice = tile / tiles;
+  const int t0 = (int)(tile % tiles) * kTile;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int tw = t0 + 32 * w;
@@ -452,8 +462,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(16))) float ST[2][4 * 64];        // per-query lse[64], D[64], g[64]
   const int N = a.n_tok, B = a.block;
   const int tiles = N / kTile;
-  const long long slice = blockIdx.x / tiles;
-  const int u0 = (int)(blockIdx.x % tiles) * kTile;
+  const long long tile = xcd_contiguous(blockIdx.x, gridDim.x);
+  const long long slice = tile / tiles;
+  const int u0 = (int)(tile % tiles) * kTile;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int uw = u0 + 32 * w;

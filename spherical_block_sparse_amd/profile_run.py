@@ -3,9 +3,11 @@
     python -m spherical_block_sparse_amd.profile_run --config ns128 --stage fine --reps 2
     python -m spherical_block_sparse_amd.profile_run --copy-mib 4096 --reps 2
 
---stage pool | select | fine | forward runs that entry point `reps` times on
-the workload's synthetic inputs (the earlier stages run once beforehand to
-produce their inputs).  --copy-mib N copies an N MiB buffer with torch's
+--stage pool | select | fine | forward | train runs that entry point
+`reps` times on the workload's synthetic inputs (the earlier stages run once
+beforehand to produce their inputs); --stage backward runs the training
+forward once and then the backward from its saved state `reps` times, with
+a seeded float32 upstream gradient.  --copy-mib N copies an N MiB buffer with torch's
 elementwise copy kernel `reps` times: N MiB read and N MiB written per call,
 the calibration of the FETCH_SIZE / WRITE_SIZE counters.
 """
@@ -24,7 +26,7 @@ from . import _lib
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="ns128", choices=sorted(CONFIGS))
-    ap.add_argument("--stage", default="fine", choices=["pool", "select", "fine", "forward"])
+    ap.add_argument("--stage", default="fine", choices=["pool", "select", "fine", "forward", "train", "backward"])
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
@@ -44,8 +46,20 @@ def main() -> int:
     qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
     torch.cuda.synchronize()
+    if args.stage == "backward":
+        _, sel_t, saved = _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+        gen = torch.Generator(device="cuda").manual_seed(cfg.seed + 7)
+        dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32)
+        grads = _lib.mosaic_bsa_backward(q, k, v, g, sel_t, dout, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                         saved=saved)
+        torch.cuda.synchronize()
     for _ in range(args.reps):
-        if args.stage == "pool":
+        if args.stage == "backward":
+            _lib.mosaic_bsa_backward(q, k, v, g, sel_t, dout, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                     *grads, saved=saved)
+        elif args.stage == "train":
+            _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+        elif args.stage == "pool":
             _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar)
         elif args.stage == "select":
             _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel)
