@@ -11,8 +11,10 @@ top-n 8, window 1024) is measured in the same run and reported under
 "secondary".  The training forward (mosaic_bsa_forward_train) and the
 backward from its saved state (mosaic_bsa_backward, float32 upstream
 gradient), and the backward that recomputes that state, are timed after each
-forward and reported under "backward"; they are not part of the step.
-Prints one JSON line.
+forward and reported under "backward"; they are not part of the step.  So is
+a stack of encoder layers on the primary workload (512 channels, 4 layers,
+synthetic weights: input projection, BSA, output projection with the
+residual), reported under "encoder_layer".  Prints one JSON line.
 
 Roofline of the dominant kernel (the fine-attention kernel, bf16 MFMA):
 algorithmic FLOPs per launch = sum over queries of 4*d*(n*block + |window(t)|)
@@ -196,6 +198,46 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
     return res
 
 
+def measure_layer(cfg: BSAConfig, channels: int, layers: int, steps: int) -> dict:
+    """A stack of encoder layers (input projection, BSA, output projection with
+    the residual) on the workload's mesh with synthetic weights: ms per layer,
+    and each projection GEMM timed through its stage entry point."""
+    from spherical_block_sparse_amd import make_layer_inputs
+    print(f"[bench] {cfg.name}: encoder layers ({layers} x {channels} channels)", file=sys.stderr, flush=True)
+    x, w_in, w_out = make_layer_inputs(cfg, channels, layers, device="cuda")
+    b, n, h, d = cfg.batch, cfg.n_tokens, cfg.heads, cfg.head_dim
+    ws = torch.empty(_lib.mosaic_bsa_layer_workspace_bytes(b, h, d, channels, cfg.nside, cfg.block, cfg.topn),
+                     dtype=torch.uint8, device="cuda")
+    ys = [torch.empty_like(x), torch.empty_like(x)]
+    sel = torch.empty((b, h, cfg.n_blocks, cfg.topn), dtype=torch.int32, device="cuda")
+
+    def stack():
+        cur = x
+        for li in range(layers):
+            nxt = ys[li % 2]
+            _lib.mosaic_bsa_layer_forward(cur, w_in[li], w_out[li], h, d, cfg.nside, cfg.block, cfg.topn,
+                                          cfg.window, y=nxt, sel_idx=sel, workspace=ws)
+            cur = nxt
+    stack()
+    ms = time_stream(stack, max(2, steps // 5)) / layers
+    q, k, v, g = _lib.mosaic_bsa_layer_in(x, w_in[0], h, d, cfg.nside)
+    attn = torch.randn((b, h, n, d), device="cuda", dtype=torch.float32)
+    lin = lambda: _lib.mosaic_bsa_layer_in(x, w_in[0], h, d, cfg.nside, q, k, v, g)
+    lout = lambda: _lib.mosaic_bsa_layer_out(attn, w_out[0], x, cfg.nside, ys[0])
+    in_ms, out_ms = time_stream(lin, 5), time_stream(lout, 5)
+    m_tok = b * n
+    in_fl = 2.0 * m_tok * channels * (3 * h * d + 3 * h)
+    out_fl = 2.0 * m_tok * (h * d) * channels
+    del x, w_in, w_out, ws, ys, q, k, v, g, attn
+    return {"channels": channels, "layers": layers, "ms_per_layer": ms,
+            "tokens_per_s_per_layer": cfg.tokens / (ms * 1e-3),
+            "in_proj": {"ms": in_ms, "TFLOPs": in_fl / (in_ms * 1e-3) / 1e12,
+                        "frac_bf16_peak": in_fl / (in_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+            "out_proj": {"ms": out_ms, "TFLOPs": out_fl / (out_ms * 1e-3) / 1e12,
+                         "frac_bf16_peak": out_fl / (out_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+            "weights": "synthetic N(0, 1/fan_in), bf16"}
+
+
 def cpu_baseline(cfg: BSAConfig, inputs, budget_s: float) -> dict:
     """The float64 oracle as it stands, on whole (batch, head) slices of the
     same inputs, until `budget_s` seconds of work are done (at least one)."""
@@ -238,6 +280,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the (secondary) backward timing")
+    ap.add_argument("--layer-channels", type=int, default=512, help="encoder-layer width (0: skip the layer timing)")
+    ap.add_argument("--layers", type=int, default=4)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the BSA slices are independent and this build has no "
@@ -256,6 +300,10 @@ def main() -> int:
         cpu = cpu_baseline(cfg, r["inputs"], args.cpu_budget)
     del r["inputs"]
     torch.cuda.empty_cache()
+    layer = None
+    if args.layer_channels:
+        layer = measure_layer(cfg, args.layer_channels, args.layers, args.steps)
+        torch.cuda.empty_cache()
 
     secondary = None
     if args.secondary and args.secondary != args.config:
@@ -311,6 +359,7 @@ def main() -> int:
             "stages_match_forward": r["stages_match_forward"],
         },
         "backward": r["backward"],
+        "encoder_layer": layer,
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 2
+#define MOSAIC_BSA_ABI_VERSION 3
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -118,6 +118,47 @@ mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const
                               const float* o_cg, const int32_t* sel_idx, int batch, int heads,
                               int head_dim, int nside, int block, int topn, int window, float* out,
                               void* stream);
+
+/* ---- Encoder layer --------------------------------------------------------
+ * The papernotes.org ICML2026 notes (关键设计) run several BSA layers at
+ * native HEALPix resolution; they specify neither the projections nor how
+ * the gates are produced.  This library's layer is the plain reading, with
+ * x [batch][N][channels] and y of the same shape, both bf16:
+ *   [q | k | v | z] = x w_inᵀ        w_in  bf16 [3*H*d + 3*H][channels]
+ *       rows h*d + j of each of q, k, v give head h, dimension j;
+ *       row 3*H*d + 3*h + r gives the gate logit of head h, branch r
+ *       (0 compressed, 1 selected, 2 local)
+ *   g = sigmoid(z)
+ *   y = x + merge_heads(BSA(q, k, v, g)) w_outᵀ   w_out bf16 [channels][H*d]
+ * q, k, v, the merged attention output and y are rounded to bf16 (nearest
+ * even); products accumulate in float32.  channels and H*d must be
+ * multiples of 64 (channels <= 16384), else MOSAIC_ERR_UNSUPPORTED.
+ * Alignment: x, y, w_in, w_out, q, k, v, attn 16 bytes; gates 4. */
+
+/* Workspace of mosaic_bsa_layer_forward (q, k, v, gates, the attention
+ * output and the BSA forward's workspace), or 0 for invalid sizes. */
+size_t mosaic_bsa_layer_workspace_bytes(int batch, int heads, int head_dim, int channels, int nside,
+                                        int block, int topn);
+
+/* One encoder layer: input projection, mosaic_bsa_forward's kernels, output
+ * projection with the residual.  sel_idx receives the layer's selection
+ * ([batch][heads][m][topn]); y must not alias x. */
+mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const void* w_out, int batch,
+                                       int heads, int head_dim, int channels, int nside, int block,
+                                       int topn, int window, void* y, int32_t* sel_idx, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* The input projection alone: q, k, v bf16 [batch][heads][N][head_dim] and
+ * gates float32 [batch][heads][N][3] from x and w_in. */
+mosaic_status mosaic_bsa_layer_in(const void* x, const void* w_in, int batch, int heads, int head_dim,
+                                  int channels, int nside, void* q, void* k, void* v, float* gates,
+                                  void* stream);
+
+/* The output projection alone: y = x + merge_heads(attn) w_outᵀ, attn the
+ * float32 [batch][heads][N][head_dim] attention output (rounded to bf16
+ * before the product). */
+mosaic_status mosaic_bsa_layer_out(const float* attn, const void* w_out, const void* x, int batch, int heads,
+                                   int head_dim, int channels, int nside, void* y, void* stream);
 
 /* Bytes of the state mosaic_bsa_forward_train leaves for mosaic_bsa_backward,
  * or 0 when the sizes are invalid or unsupported.  Layout (256-byte aligned

@@ -6,6 +6,6 @@ kernels, declared in ``include/mosaic_bsa.h``); ``_lib`` is the thin ctypes
 binding over it and ``synth`` makes the seeded synthetic inputs.
 """
 
-from .synth import BSAConfig, CONFIGS, make_inputs  # noqa: F401
+from .synth import BSAConfig, CONFIGS, make_inputs, make_layer_inputs  # noqa: F401
 
-__all__ = ["BSAConfig", "CONFIGS", "make_inputs"]
+__all__ = ["BSAConfig", "CONFIGS", "make_inputs", "make_layer_inputs"]

@@ -29,6 +29,7 @@ EXPORTED = (
     "mosaic_bsa_workspace_bytes", "mosaic_bsa_forward", "mosaic_bsa_pool",
     "mosaic_bsa_compress_select", "mosaic_bsa_fine",
     "mosaic_bsa_saved_bytes", "mosaic_bsa_forward_train",
+    "mosaic_bsa_layer_workspace_bytes", "mosaic_bsa_layer_forward", "mosaic_bsa_layer_in", "mosaic_bsa_layer_out",
     "mosaic_bsa_backward_workspace_bytes", "mosaic_bsa_backward",
 )
 
@@ -68,6 +69,14 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
         L.mosaic_bsa_backward_workspace_bytes.restype = S
         L.mosaic_bsa_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.mosaic_bsa_layer_workspace_bytes.restype = S
+        L.mosaic_bsa_layer_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.mosaic_bsa_layer_forward.restype = I
+        L.mosaic_bsa_layer_forward.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, P, P, S, P]
+        L.mosaic_bsa_layer_in.restype = I
+        L.mosaic_bsa_layer_in.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P]
+        L.mosaic_bsa_layer_out.restype = I
+        L.mosaic_bsa_layer_out.argtypes = [P, P, P, I, I, I, I, I, P, P]
         L.mosaic_bsa_saved_bytes.restype = S
         L.mosaic_bsa_saved_bytes.argtypes = [I, I, I, I, I]
         L.mosaic_bsa_forward_train.restype = I
@@ -255,3 +264,68 @@ def mosaic_bsa_backward(q, k, v, gates, sel_idx, dout, nside, block, topn, windo
         _ptr(dv, torch.float32, (b, h, n, d), "dv"), _ptr(dgates, torch.float32, (b, h, n, 3), "dgates"),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return dq, dk, dv, dgates
+
+
+def _layer_dims(x: torch.Tensor, nside: int):
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, N, channels]")
+    b, n, c = x.shape
+    if n != 12 * nside * nside:
+        raise ValueError(f"N = {n} but 12*nside^2 = {12 * nside * nside}")
+    return b, n, c
+
+
+def mosaic_bsa_layer_workspace_bytes(batch, heads, head_dim, channels, nside, block, topn) -> int:
+    return lib().mosaic_bsa_layer_workspace_bytes(batch, heads, head_dim, channels, nside, block, topn)
+
+
+def mosaic_bsa_layer_forward(x, w_in, w_out, heads, head_dim, nside, block, topn, window, y=None, sel_idx=None,
+                             workspace=None, stream=None):
+    """One encoder layer: y [b,N,C] bf16 and sel_idx [b,H,m,topn] from x [b,N,C] bf16,
+    w_in [3*H*d + 3*H, C] and w_out [C, H*d] (bf16)."""
+    b, n, c = _layer_dims(x, nside)
+    m = n // block
+    e = 3 * heads * head_dim + 3 * heads
+    y = torch.empty((b, n, c), dtype=torch.bfloat16, device=x.device) if y is None else y
+    sel_idx = torch.empty((b, heads, m, topn), dtype=torch.int32, device=x.device) if sel_idx is None else sel_idx
+    need = mosaic_bsa_layer_workspace_bytes(b, heads, head_dim, c, nside, block, topn)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or workspace.device.type != "cuda":
+        raise ValueError("workspace must be a 1-D uint8 device tensor")
+    _check(lib().mosaic_bsa_layer_forward(
+        _ptr(x, torch.bfloat16, (b, n, c), "x"), _ptr(w_in, torch.bfloat16, (e, c), "w_in"),
+        _ptr(w_out, torch.bfloat16, (c, heads * head_dim), "w_out"),
+        b, heads, head_dim, c, nside, block, topn, window,
+        _ptr(y, torch.bfloat16, (b, n, c), "y"), _ptr(sel_idx, torch.int32, (b, heads, m, topn), "sel_idx"),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return y, sel_idx
+
+
+def mosaic_bsa_layer_in(x, w_in, heads, head_dim, nside, q=None, k=None, v=None, gates=None, stream=None):
+    """q, k, v [b,H,N,d] bf16 and gates [b,H,N,3] fp32 from x [b,N,C] and w_in."""
+    b, n, c = _layer_dims(x, nside)
+    e = 3 * heads * head_dim + 3 * heads
+    shp = (b, heads, n, head_dim)
+    q = torch.empty(shp, dtype=torch.bfloat16, device=x.device) if q is None else q
+    k = torch.empty(shp, dtype=torch.bfloat16, device=x.device) if k is None else k
+    v = torch.empty(shp, dtype=torch.bfloat16, device=x.device) if v is None else v
+    gates = torch.empty((b, heads, n, 3), dtype=torch.float32, device=x.device) if gates is None else gates
+    _check(lib().mosaic_bsa_layer_in(
+        _ptr(x, torch.bfloat16, (b, n, c), "x"), _ptr(w_in, torch.bfloat16, (e, c), "w_in"),
+        b, heads, head_dim, c, nside,
+        _ptr(q, torch.bfloat16, shp, "q"), _ptr(k, torch.bfloat16, shp, "k"), _ptr(v, torch.bfloat16, shp, "v"),
+        _ptr(gates, torch.float32, (b, heads, n, 3), "gates"), _stream(stream)))
+    return q, k, v, gates
+
+
+def mosaic_bsa_layer_out(attn, w_out, x, nside, y=None, stream=None):
+    """y [b,N,C] bf16 = x + merge_heads(attn) w_outᵀ, attn [b,H,N,d] fp32."""
+    b, n, c = _layer_dims(x, nside)
+    _, heads, _, head_dim = attn.shape
+    y = torch.empty((b, n, c), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _check(lib().mosaic_bsa_layer_out(
+        _ptr(attn, torch.float32, (b, heads, n, head_dim), "attn"),
+        _ptr(w_out, torch.bfloat16, (c, heads * head_dim), "w_out"), _ptr(x, torch.bfloat16, (b, n, c), "x"),
+        b, heads, head_dim, c, nside, _ptr(y, torch.bfloat16, (b, n, c), "y"), _stream(stream)))
+    return y

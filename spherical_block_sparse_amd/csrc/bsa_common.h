@@ -176,6 +176,18 @@ struct BwdLaunch {
   int32_t* inv_list;        // [S][m*topn]
 };
 
+// Encoder layer projections (bsa_layer.hip).  Input: x [batch*N][channels]
+// bf16 times w_in [3*H*d + 3*H][channels] bf16 -> q, k, v bf16 [batch][H][N][d]
+// and gates = sigmoid(logits) float32 [batch][H][N][3].  Output:
+// y = x + merge(attn) w_outᵀ with attn float32 [batch][H][N][d] and w_out
+// [channels][H*d] bf16, y bf16 [batch*N][channels].  channels and H*d are
+// multiples of 64.
+hipError_t launch_layer_in(const uint16_t* x, const uint16_t* w_in, long long batch, int n_tok, int channels,
+                           int heads, int head_dim, uint16_t* q, uint16_t* k, uint16_t* v, float* gates,
+                           hipStream_t stream);
+hipError_t launch_layer_out(const float* attn, const uint16_t* w_out, const uint16_t* x, long long batch,
+                            int n_tok, int channels, int heads, int head_dim, uint16_t* y, hipStream_t stream);
+
 // largest m = N/block the backward's inverted-selection kernel holds in LDS
 constexpr int kIndexMaxBlocks = 16384;
 

@@ -1,0 +1,283 @@
+// The BSA encoder layer around the attention operator: input projections to
+// per-head q, k, v and branch gates, and the output projection with the
+// residual.
+//
+// Source: papernotes.org ICML2026 notes on "(Sparse) Attention to the
+// Details", 关键设计: the encoder runs several BSA layers at native HEALPix
+// resolution, and BSA mixes its three branches with per-token gates g_CG,
+// g_FG, g_L.  The pages give neither the projections nor the gate
+// parametrisation; the layer here is the plain reading:
+//   [q | k | v | z] = x W_inᵀ,  g = sigmoid(z)  (one gate per head and branch)
+//   y = x + merge_heads(BSA(q, k, v, g)) W_outᵀ
+// with bf16 activations between the steps (q, k, v, the merged attention
+// output and y are rounded to bf16 once, round-to-nearest-even).
+//
+// Both projections are one GEMM kernel, D[m][n] = sum_k A[m][k] B[n][k]
+// (A: tokens x K, B: features x K, both with K contiguous), with
+// v_mfma_f32_16x16x32_bf16:
+//   * a workgroup owns a 128-token x 128-feature tile, four waves in 2 x 2,
+//     each 64 x 64 = 4 x 4 MFMA tiles (64 accumulator registers);
+//   * K streams through LDS in 64-wide chunks, double-buffered: bf16 rows
+//     arrive by direct global->LDS loads into XOR-swizzled [64][64] tiles;
+//     the float32 attention output of the output projection is loaded into
+//     registers one chunk ahead, rounded to bf16 and written to LDS;
+//   * the MFMA computes the transposed tile (features x tokens), so each
+//     lane ends with four consecutive features of one token: the epilogue
+//     stores 8 contiguous bytes per lane (the head split of q, k, v, the
+//     sigmoid of the gate logits, or x + the projection);
+//   * workgroups are renumbered so each XCD runs a contiguous run of tiles:
+//     the feature tiles of one token tile then share its rows in one L2.
+#include "bsa_common.h"
+
+#include <math.h>
+
+namespace mosaic {
+namespace {
+
+constexpr int kGT = 128;   // tokens and features per workgroup tile
+constexpr int kGK = 64;    // K per staged chunk
+constexpr int kGWaves = 4;
+
+__device__ const uint4 kZero16L = {0u, 0u, 0u, 0u};
+
+// 16-byte chunk swizzle of a 64-element (128-byte) row, period 16 rows
+__device__ __forceinline__ int gswz(int row) { return 2 * ((row >> 1) & 3) + ((row >> 3) & 1); }
+
+// operand of rows 16*rt .. +15 of a staged [128][64] tile (two swizzled
+// [64][64] halves): lane lr + 16*lg holds row 16*rt + lr, k = 32*kk + 8*lg .. +7
+__device__ __forceinline__ bf16x8 tile_operand(const uint16_t* buf, int rt, int kk) {
+  const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
+  const int row = 16 * rt + lr;
+  return *reinterpret_cast<const bf16x8*>(buf + row * kGK + 8 * ((4 * kk + lg) ^ gswz(row)));
+}
+
+// direct loads of rows r0 .. r0+127, k0 .. k0+63 of a [rows][K] bf16 matrix
+// into a staged tile; rows >= `rows` read as zeros.  Wave w issues 1 KB loads
+// w, w+4, w+8, w+12 (8 rows of 128 bytes each).
+__device__ __forceinline__ void stage_bf16(uint16_t* buf, const uint16_t* base, long long r0, long long rows,
+                                           int K, int k0, int w) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int grp = w + kGWaves * i;
+    const int row = 8 * grp + lane / 8;
+    const int lc = (lane % 8) ^ gswz(row);
+    const long long r = r0 + row;
+    const void* src = r < rows ? (const void*)(base + r * K + k0 + 8 * lc) : (const void*)&kZero16L;
+    dma_global(buf + grp * 512, src);
+  }
+}
+
+struct GemmArgs {
+  const uint16_t* a;       // bf16 [M][K] (input projection: x)
+  const float* a_heads;    // float32 [b][H][N][d] (output projection: the attention output)
+  const uint16_t* b;       // bf16 [F][K] weights
+  long long M;             // tokens b*N
+  int F;                   // output features
+  int K;
+  int n_tok, heads, head_dim;
+  // input projection outputs
+  uint16_t* q;             // bf16 [b][H][N][d]
+  uint16_t* k;
+  uint16_t* v;
+  float* gates;            // float32 [b][H][N][3]
+  // output projection
+  const uint16_t* x;       // bf16 [M][F] residual
+  uint16_t* y;             // bf16 [M][F]
+  int m_tiles, f_tiles;
+};
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// OUT false: input projection (A = x via direct loads, head-split epilogue);
+// OUT true: output projection (A = float32 attention output, residual epilogue)
+template <bool OUT>
+__global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGT * kGK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGT * kGK];
+  const long long tiles = (long long)p.m_tiles * p.f_tiles;
+  long long logical;
+  {
+    const long long b = blockIdx.x, q8 = tiles / 8, r8 = tiles % 8, xcd = b % 8, kq = b / 8;
+    logical = xcd < r8 ? xcd * (q8 + 1) + kq : r8 * (q8 + 1) + (xcd - r8) * q8 + kq;
+  }
+  const long long m0 = (logical / p.f_tiles) * kGT;
+  const int f0 = (int)(logical % p.f_tiles) * kGT;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
+  const int wm = w & 1, wf = w >> 1;   // the wave's 64-token and 64-feature quarter
+  const int nk = p.K / kGK;
+
+  // OUT: the float32 attention output of chunk c, rows m0 .. m0+127: thread
+  // x handles row x/2, 32 of its 64 k values (8 float4), k = 32*(x%2) + 4*i
+  const int ar = threadIdx.x / 2, ah = threadIdx.x % 2;
+  float4 areg[8];
+  auto load_a32 = [&](int c) __attribute__((always_inline)) {
+    const long long m = m0 + ar;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = c * kGK + 32 * ah + 4 * i;          // feature h*d + j of the merged heads
+      const int h = kk / p.head_dim, j = kk % p.head_dim;
+      if (m < p.M) {
+        const long long bi = m / p.n_tok, t = m % p.n_tok;
+        areg[i] = *reinterpret_cast<const float4*>(
+            p.a_heads + (((bi * p.heads + h) * (long long)p.n_tok + t) * p.head_dim + j));
+      } else {
+        areg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  auto store_a32 = [&](uint16_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {   // two float4 = one 16-byte chunk of 8 bf16
+      const int kc = 32 * ah + 4 * i;  // k within the chunk, a multiple of 8
+      ushort4 lo, hi;
+      lo.x = bf16_rne(areg[i].x); lo.y = bf16_rne(areg[i].y); lo.z = bf16_rne(areg[i].z); lo.w = bf16_rne(areg[i].w);
+      hi.x = bf16_rne(areg[i + 1].x); hi.y = bf16_rne(areg[i + 1].y);
+      hi.z = bf16_rne(areg[i + 1].z); hi.w = bf16_rne(areg[i + 1].w);
+      uint16_t* dst = buf + ar * kGK + 8 * ((kc / 8) ^ gswz(ar));
+      *reinterpret_cast<ushort4*>(dst) = lo;
+      *reinterpret_cast<ushort4*>(dst + 4) = hi;
+    }
+  };
+  auto stage = [&](int c, int s) __attribute__((always_inline)) {
+    if constexpr (!OUT) stage_bf16(As[s], p.a, m0, p.M, p.K, c * kGK, w);
+    stage_bf16(Bs[s], p.b, f0, p.F, p.K, c * kGK, w);
+  };
+
+  floatx4 acc[4][4];   // [feature tile][token tile]: features 16*ft + 4*lg + i of token 16*mt + lr
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[ft][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (OUT) {
+    load_a32(0);
+    store_a32(As[0]);
+  }
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads have landed
+  __syncthreads();
+  for (int c = 0; c < nk; ++c) {
+    const int s = c & 1;
+    if (c + 1 < nk) {
+      stage(c + 1, s ^ 1);
+      if constexpr (OUT) load_a32(c + 1);
+    }
+    const uint16_t* a_t = As[s] + wm * 64 * kGK;
+    const uint16_t* b_t = Bs[s] + wf * 64 * kGK;
+#pragma unroll
+    for (int kk = 0; kk < kGK / 32; ++kk) {
+      bf16x8 bo[4], ao[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bo[t] = tile_operand(b_t, t, kk);
+        ao[t] = tile_operand(a_t, t, kk);
+      }
+#pragma unroll
+      for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[ft][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo[ft], ao[mt], acc[ft][mt], 0, 0, 0);
+    }
+    // buffer s^1 was last read in chunk c-1, before the barrier that ended it
+    if constexpr (OUT) {
+      if (c + 1 < nk) store_a32(As[s ^ 1]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds features f = f0 + 64*wf + 16*ft + 4*lg + i of token
+  // m = m0 + 64*wm + 16*mt + lr
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const long long m = m0 + 64 * wm + 16 * mt + lr;
+    if (m >= p.M) continue;
+    const long long bi = m / p.n_tok, t = m % p.n_tok;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft) {
+      const int f = f0 + 64 * wf + 16 * ft + 4 * lg;
+      if (f >= p.F) continue;
+      const floatx4 r = acc[ft][mt];
+      if constexpr (OUT) {
+        const ushort4 xr = *reinterpret_cast<const ushort4*>(p.x + m * p.F + f);
+        ushort4 o;
+        o.x = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.x << 16) + r[0]);
+        o.y = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.y << 16) + r[1]);
+        o.z = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.z << 16) + r[2]);
+        o.w = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.w << 16) + r[3]);
+        *reinterpret_cast<ushort4*>(p.y + m * p.F + f) = o;
+      } else {
+        const int hd = p.heads * p.head_dim;
+        if (f < 3 * hd) {   // four features of one head of one of q, k, v
+          const int which = f / hd, h = (f % hd) / p.head_dim, j = f % p.head_dim;
+          uint16_t* dst = which == 0 ? p.q : (which == 1 ? p.k : p.v);
+          ushort4 o;
+          o.x = bf16_rne(r[0]); o.y = bf16_rne(r[1]); o.z = bf16_rne(r[2]); o.w = bf16_rne(r[3]);
+          *reinterpret_cast<ushort4*>(dst + ((bi * p.heads + h) * (long long)p.n_tok + t) * p.head_dim + j) = o;
+        } else {            // gate logits: feature 3*hd + 3*h + branch
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int gi = f + i - 3 * hd;
+            if (gi >= 3 * p.heads) break;
+            const int h = gi / 3, br = gi % 3;
+            p.gates[((bi * p.heads + h) * (long long)p.n_tok + t) * 3 + br] = 1.f / (1.f + __expf(-r[i]));
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm(GemmArgs p, bool out, hipStream_t stream) {
+  p.m_tiles = (int)((p.M + kGT - 1) / kGT);
+  p.f_tiles = (p.F + kGT - 1) / kGT;
+  const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
+  if (out)
+    hipLaunchKernelGGL(layer_gemm_kernel<true>, grid, dim3(64 * kGWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL(layer_gemm_kernel<false>, grid, dim3(64 * kGWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_layer_in(const uint16_t* x, const uint16_t* w_in, long long batch, int n_tok, int channels,
+                           int heads, int head_dim, uint16_t* q, uint16_t* k, uint16_t* v, float* gates,
+                           hipStream_t stream) {
+  GemmArgs p = {};
+  p.a = x;
+  p.b = w_in;
+  p.M = batch * n_tok;
+  p.F = 3 * heads * head_dim + 3 * heads;
+  p.K = channels;
+  p.n_tok = n_tok;
+  p.heads = heads;
+  p.head_dim = head_dim;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gates = gates;
+  return launch_gemm(p, false, stream);
+}
+
+hipError_t launch_layer_out(const float* attn, const uint16_t* w_out, const uint16_t* x, long long batch,
+                            int n_tok, int channels, int heads, int head_dim, uint16_t* y, hipStream_t stream) {
+  GemmArgs p = {};
+  p.a_heads = attn;
+  p.b = w_out;
+  p.M = batch * n_tok;
+  p.F = channels;
+  p.K = heads * head_dim;
+  p.n_tok = n_tok;
+  p.heads = heads;
+  p.head_dim = head_dim;
+  p.x = x;
+  p.y = y;
+  return launch_gemm(p, true, stream);
+}
+
+}  // namespace mosaic

@@ -163,6 +163,37 @@ mosaic_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// encoder layer: limits of the projection kernels and the workspace
+mosaic_status check_layer(const Shape& s, int heads, int channels) {
+  if (channels < 64 || channels % 64 || channels > 16384)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "channels %d: the projections need a multiple of 64 in [64, 16384]",
+                channels);
+  if ((heads * s.d) % 64)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "heads*head_dim = %d: the output projection needs a multiple of 64",
+                heads * s.d);
+  return MOSAIC_OK;
+}
+
+struct LayerWorkspace {
+  size_t q, k, v, gates, attn, bsa, total;
+};
+
+LayerWorkspace layer_layout(const Shape& s) {
+  const size_t e = (size_t)s.slices * s.n_tok * s.d;
+  LayerWorkspace w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t r = o; o += align256(bytes); return r; };
+  w.q = take(e * sizeof(uint16_t));
+  w.k = take(e * sizeof(uint16_t));
+  w.v = take(e * sizeof(uint16_t));
+  w.gates = take((size_t)s.slices * s.n_tok * 3 * sizeof(float));
+  w.attn = take(e * sizeof(float));
+  w.bsa = take(layout(s).total);
+  w.total = o;
+  return w;
+}
+
+
 #define REQUIRE_PTR(p) \
   if (!(p)) return fail(MOSAIC_ERR_NULL_POINTER, "%s is NULL", #p)
 #define REQUIRE_ALIGN(p, a) \
@@ -273,6 +304,93 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
                           s.block, s.topn, s.window, hs);
   return hip_status(e, "bsa_fine launch");
+}
+
+// ---------------------------------------------------------------------------
+// encoder layer
+
+
+size_t mosaic_bsa_layer_workspace_bytes(int batch, int heads, int head_dim, int channels, int nside, int block,
+                                        int topn) {
+  Shape s;
+  if (check_shape(batch, heads, head_dim, nside, block, topn, 0, kUsesTopn, &s) != MOSAIC_OK) return 0;
+  if (check_layer(s, heads, channels) != MOSAIC_OK) return 0;
+  return layer_layout(s).total;
+}
+
+mosaic_status mosaic_bsa_layer_in(const void* x, const void* w_in, int batch, int heads, int head_dim,
+                                  int channels, int nside, void* q, void* k, void* v, float* gates,
+                                  void* stream) {
+  REQUIRE_PTR(x); REQUIRE_PTR(w_in); REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates);
+  REQUIRE_ALIGN(x, 16); REQUIRE_ALIGN(w_in, 16); REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16);
+  REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, 16, 0, 0, 0, &s);
+  if (st != MOSAIC_OK) return st;
+  if ((st = check_layer(s, heads, channels)) != MOSAIC_OK) return st;
+  return hip_status(mosaic::launch_layer_in(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_in),
+                                            batch, s.n_tok, channels, heads, s.d, static_cast<uint16_t*>(q),
+                                            static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), gates,
+                                            static_cast<hipStream_t>(stream)),
+                    "layer input projection launch");
+}
+
+mosaic_status mosaic_bsa_layer_out(const float* attn, const void* w_out, const void* x, int batch, int heads,
+                                   int head_dim, int channels, int nside, void* y, void* stream) {
+  REQUIRE_PTR(attn); REQUIRE_PTR(w_out); REQUIRE_PTR(x); REQUIRE_PTR(y);
+  REQUIRE_ALIGN(attn, 16); REQUIRE_ALIGN(w_out, 16); REQUIRE_ALIGN(x, 16); REQUIRE_ALIGN(y, 16);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, 16, 0, 0, 0, &s);
+  if (st != MOSAIC_OK) return st;
+  if ((st = check_layer(s, heads, channels)) != MOSAIC_OK) return st;
+  return hip_status(mosaic::launch_layer_out(attn, static_cast<const uint16_t*>(w_out),
+                                             static_cast<const uint16_t*>(x), batch, s.n_tok, channels, heads, s.d,
+                                             static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream)),
+                    "layer output projection launch");
+}
+
+mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const void* w_out, int batch, int heads,
+                                       int head_dim, int channels, int nside, int block, int topn, int window,
+                                       void* y, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  REQUIRE_PTR(x); REQUIRE_PTR(w_in); REQUIRE_PTR(w_out); REQUIRE_PTR(y); REQUIRE_PTR(sel_idx);
+  REQUIRE_PTR(workspace);
+  REQUIRE_ALIGN(x, 16); REQUIRE_ALIGN(w_in, 16); REQUIRE_ALIGN(w_out, 16); REQUIRE_ALIGN(y, 16);
+  REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(workspace, 256);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
+  if (st != MOSAIC_OK) return st;
+  if ((st = check_layer(s, heads, channels)) != MOSAIC_OK) return st;
+  const LayerWorkspace lw = layer_layout(s);
+  if (workspace_bytes < lw.total)
+    return fail(MOSAIC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, lw.total);
+  if (x == y) return fail(MOSAIC_ERR_BAD_SHAPE, "y must not alias x");
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* q = reinterpret_cast<uint16_t*>(ws + lw.q);
+  uint16_t* k = reinterpret_cast<uint16_t*>(ws + lw.k);
+  uint16_t* v = reinterpret_cast<uint16_t*>(ws + lw.v);
+  float* gates = reinterpret_cast<float*>(ws + lw.gates);
+  float* attn = reinterpret_cast<float*>(ws + lw.attn);
+  char* bws = ws + lw.bsa;
+  const Workspace w = layout(s);
+  double* qbar = reinterpret_cast<double*>(bws + w.qbar);
+  double* kbar = reinterpret_cast<double*>(bws + w.kbar);
+  float* vbar = reinterpret_cast<float*>(bws + w.vbar);
+  float* ocg = reinterpret_cast<float*>(bws + w.ocg);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = mosaic::launch_layer_in(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_in), batch,
+                                         s.n_tok, channels, heads, s.d, q, k, v, gates, hs);
+  if (e != hipSuccess) return hip_status(e, "layer input projection launch");
+  e = mosaic::launch_pool(q, k, v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  e = mosaic::launch_fine(q, k, v, gates, ocg, sel_idx, attn, s.slices, s.n_tok, s.d, s.block, s.topn, s.window, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_fine launch");
+  return hip_status(mosaic::launch_layer_out(attn, static_cast<const uint16_t*>(w_out),
+                                             static_cast<const uint16_t*>(x), batch, s.n_tok, channels, heads, s.d,
+                                             static_cast<uint16_t*>(y), hs),
+                    "layer output projection launch");
 }
 
 size_t mosaic_bsa_saved_bytes(int batch, int heads, int head_dim, int nside, int block) {

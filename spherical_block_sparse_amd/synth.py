@@ -196,3 +196,36 @@ def make_inputs(cfg: BSAConfig, device="cpu", dtype=torch.bfloat16, seed: int | 
 def to_f64(x: torch.Tensor) -> np.ndarray:
     """Exact widening of a (bf16 / fp32) tensor to a float64 numpy array on the host."""
     return x.detach().to("cpu").to(torch.float64).numpy()
+
+
+def make_layer_inputs(cfg: BSAConfig, channels: int, layers: int = 1, device="cpu", seed: int | None = None):
+    """Return (x, w_in, w_out) for an encoder layer on ``cfg``'s mesh.
+
+    x: [b, N, channels] bf16, the config's field ("iid": N(0,1); "fourier":
+    the cosine-mode field above with ``channels`` channels) from the first
+    stream of seed + 1000.  w_in: [layers, 3*H*d + 3*H, channels] and w_out:
+    [layers, channels, H*d], bf16, i.i.d. N(0, 1/fan_in) from the second and
+    third streams (fan_in = channels and H*d)."""
+    seeds = _stream_seeds((cfg.seed if seed is None else seed) + 1000)
+    b, n = cfg.batch, cfg.n_tokens
+    hd = cfg.heads * cfg.head_dim
+    e = 3 * hd + 3 * cfg.heads
+    gen = _generator(device, seeds[0])
+    x = torch.empty((b, n, channels), dtype=torch.bfloat16, device=device)
+    u = None
+    if cfg.field == "fourier":
+        u = torch.from_numpy(pix2vec_nest(cfg.nside)).to(device=device, dtype=torch.float32)
+    for bi in range(b):
+        if cfg.field == "iid":
+            x[bi].copy_(torch.randn((n, channels), generator=gen, device=device, dtype=torch.float32))
+        elif cfg.field == "fourier":
+            x[bi].copy_(_fourier_field(u, channels, gen))
+        else:
+            raise ValueError(cfg.field)
+    gen = _generator(device, seeds[1])
+    w_in = (torch.randn((layers, e, channels), generator=gen, device=device, dtype=torch.float32)
+            / math.sqrt(channels)).to(torch.bfloat16)
+    gen = _generator(device, seeds[2])
+    w_out = (torch.randn((layers, channels, hd), generator=gen, device=device, dtype=torch.float32)
+             / math.sqrt(hd)).to(torch.bfloat16)
+    return x, w_in, w_out

@@ -41,7 +41,7 @@ def test_header_declares_and_library_exports_the_same_symbols():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.mosaic_bsa_abi_version() == 2
+    assert L.mosaic_bsa_abi_version() == 3
     for code, name in _lib.STATUS_NAMES.items():
         assert L.mosaic_status_string(code).decode() == name
     assert L.mosaic_status_string(99).decode() == "MOSAIC_ERR_UNKNOWN"
@@ -178,3 +178,50 @@ def test_backward_workspace_bytes():
     # the largest section is the bf16 copy of dout plus the per-query statistics
     n, s = 12 * 32 * 32, 2
     assert L.mosaic_bsa_backward_workspace_bytes(1, 2, 64, 32, 64, 16) >= s * n * 64 * 2 + 2 * s * n * 12
+
+
+def layer(x=FAKE, w_in=FAKE, w_out=FAKE, batch=1, heads=2, d=64, channels=128, nside=32, block=64, topn=16,
+          window=256, y=FAKE + 4096, sel=FAKE, ws=FAKE, ws_bytes=None):
+    L = _lib.lib()
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return L.mosaic_bsa_layer_forward(x, w_in, w_out, batch, heads, d, channels, nside, block, topn, window,
+                                      y, sel, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w_in=None), NULL), (dict(w_out=None), NULL), (dict(y=None), NULL),
+    (dict(sel=None), NULL), (dict(ws=None), NULL),
+    (dict(x=FAKE + 8), MISAL), (dict(w_in=FAKE + 2), MISAL), (dict(y=FAKE + 4), MISAL), (dict(ws=FAKE + 64), MISAL),
+    (dict(channels=96), UNSUP), (dict(channels=32), UNSUP), (dict(channels=16384 + 64), UNSUP),
+    (dict(heads=1, d=32), UNSUP),                # H*d = 32 is not a multiple of 64
+    (dict(topn=0), SHAPE), (dict(window=0), SHAPE), (dict(block=32), SHAPE),
+    (dict(ws_bytes=4096), WS),
+    (dict(y=FAKE), SHAPE),                       # y aliases x
+])
+def test_layer_validation(kw, code):
+    assert layer(**kw) == code
+    assert _lib.lib().mosaic_last_error().decode() != ""
+
+
+def test_layer_stage_validation():
+    L = _lib.lib()
+    assert L.mosaic_bsa_layer_in(None, FAKE, 1, 2, 64, 128, 32, FAKE, FAKE, FAKE, FAKE, None) == NULL
+    assert L.mosaic_bsa_layer_in(FAKE, FAKE, 1, 2, 64, 100, 32, FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+    assert L.mosaic_bsa_layer_in(FAKE, FAKE, 1, 2, 64, 128, 32, FAKE + 8, FAKE, FAKE, FAKE, None) == MISAL
+    assert L.mosaic_bsa_layer_in(FAKE, FAKE, 1, 2, 64, 128, 3, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.mosaic_bsa_layer_out(FAKE, FAKE, None, 1, 2, 64, 128, 32, FAKE, None) == NULL
+    assert L.mosaic_bsa_layer_out(FAKE, FAKE, FAKE, 1, 2, 64, 128, 32, FAKE + 2, None) == MISAL
+    assert L.mosaic_bsa_layer_out(FAKE, FAKE, FAKE, 1, 1, 32, 128, 32, FAKE, None) == UNSUP
+
+
+def test_layer_workspace_bytes():
+    L = _lib.lib()
+    b, h, d, c, nside, block, topn = 1, 2, 64, 128, 32, 64, 16
+    n = 12 * nside * nside
+    got = L.mosaic_bsa_layer_workspace_bytes(b, h, d, c, nside, block, topn)
+    # q, k, v bf16 + gates + float32 attention output + the forward workspace
+    floor = 3 * b * h * n * d * 2 + b * h * n * 3 * 4 + b * h * n * d * 4 + \
+        L.mosaic_bsa_workspace_bytes(b, h, d, nside, block, topn)
+    assert floor <= got < floor + 8 * 256
+    assert L.mosaic_bsa_layer_workspace_bytes(b, h, d, 100, nside, block, topn) == 0
