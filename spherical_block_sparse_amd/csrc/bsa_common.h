@@ -132,11 +132,14 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
                                   int topn, hipStream_t stream);
 
 // save_o / save_lse non-null: also write each query's normalised selected and
-// local branch outputs (float32 [S][N][2][D]) and their log2-sum-exp ([S][N][2])
+// local branch outputs (float32 [S][N][2][D]) and their log2-sum-exp
+// ([S][N][2]).  out_merged non-null (with `heads`, S = batch*heads): write
+// out in bf16 as [batch][N][heads][D] there instead of `out`.
 hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gates,
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
-                       hipStream_t stream, float* save_o = nullptr, float* save_lse = nullptr);
+                       hipStream_t stream, float* save_o = nullptr, float* save_lse = nullptr,
+                       uint16_t* out_merged = nullptr, int heads = 1);
 
 // Everything the backward launches read and write (device pointers; the
 // workspace buffers are carved by the C-ABI entry point).
@@ -187,6 +190,10 @@ hipError_t launch_layer_in(const uint16_t* x, const uint16_t* w_in, long long ba
                            hipStream_t stream);
 hipError_t launch_layer_out(const float* attn, const uint16_t* w_out, const uint16_t* x, long long batch,
                             int n_tok, int channels, int heads, int head_dim, uint16_t* y, hipStream_t stream);
+// the same from the attention output already merged and in bf16, [batch*N][H*d]
+hipError_t launch_layer_out_merged(const uint16_t* attn_merged, const uint16_t* w_out, const uint16_t* x,
+                                   long long batch, int n_tok, int channels, int heads, int head_dim, uint16_t* y,
+                                   hipStream_t stream);
 
 // largest m = N/block the backward's inverted-selection kernel holds in LDS
 constexpr int kIndexMaxBlocks = 16384;

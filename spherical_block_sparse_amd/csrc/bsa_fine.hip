@@ -47,7 +47,9 @@
 //   * epilogue: out = g0·o_CG[t/block] + g1·o_FG + g2·o_L, float32.  The
 //     SAVE instantiation (training forward) also stores o_FG, o_L (float32)
 //     and their log2-sum-exp, which the backward reads instead of
-//     recomputing both branches.
+//     recomputing both branches; the MERGED instantiation (encoder layer)
+//     writes out in bf16 with the heads side by side, [b][N][H][D], the
+//     layout the output projection reads.
 // Roofline: bf16 matrix work 4*d*(n*block + W) per query, HBM traffic at
 // least q, k, v once plus gates, o_CG and out.
 #include "bsa_common.h"
@@ -67,6 +69,8 @@ struct FineArgs {
   float* out;
   float* save_o;      // [S][N][2][D] o_FG, o_L (normalised), SAVE only
   float* save_lse;    // [S][N][2] their log2-sum-exp (log2 units of S*log2(e)/sqrt(d)), SAVE only
+  uint16_t* out_merged;   // bf16 [b][N][H][D] in place of out, MERGED only
+  int heads;
   int n_tok;
   int block;
   int topn;
@@ -289,7 +293,9 @@ __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
 // this wave are outstanding (lgkm and exp counters not waited on)
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
 
-template <int D, int WAVES, bool SAVE>
+enum FineMode { kPlain = 0, kSave = 1, kMerged = 2 };
+
+template <int D, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void fine_kernel(FineArgs a) {
   constexpr int KK = Tile<D>::KK, DT = Tile<D>::DT;
   constexpr int T = 32 * WAVES;           // queries per workgroup
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   auto finish_selected = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if constexpr (SAVE) save_branch(s, 0);
+      if constexpr (MODE == kSave) save_branch(s, 0);
       const int tq = tw + 16 * s + lr;
       const float* g = a.gates + ((size_t)slice * N + tq) * 3;
       const float g0 = g[0], g1 = g[1] / br[s].l[0];
@@ -558,10 +564,15 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   // gated sum: pre + g_L * o_L
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    if constexpr (SAVE) save_branch(s, 1);
+    if constexpr (MODE == kSave) save_branch(s, 1);
     const int tq = tw + 16 * s + lr;
     const float g2 = a.gates[((size_t)slice * N + tq) * 3 + 2] / br[s].l[0];
     float* dst = a.out + ((size_t)slice * N + tq) * D;
+    uint16_t* dstb = nullptr;
+    if constexpr (MODE == kMerged) {
+      const long long bi = slice / a.heads, h = slice % a.heads;
+      dstb = a.out_merged + (((size_t)bi * N + tq) * a.heads + h) * D;
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       float4 r = pre[s][dt];
@@ -569,7 +580,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       r.y += g2 * br[s].o[dt][1];
       r.z += g2 * br[s].o[dt][2];
       r.w += g2 * br[s].o[dt][3];
-      *reinterpret_cast<float4*>(dst + dt * 16 + 4 * lg) = r;
+      if constexpr (MODE == kMerged) {
+        ushort4 o;
+        o.x = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r.x));
+        o.y = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r.y));
+        o.z = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r.z));
+        o.w = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r.w));
+        *reinterpret_cast<ushort4*>(dstb + dt * 16 + 4 * lg) = o;
+      } else {
+        *reinterpret_cast<float4*>(dst + dt * 16 + 4 * lg) = r;
+      }
     }
   }
 }
@@ -582,9 +602,11 @@ hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
   a.groups = slices * a.tiles;
   dim3 grid((unsigned)a.groups);
   if (a.save_o)
-    hipLaunchKernelGGL((fine_kernel<D, WAVES, true>), grid, dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((fine_kernel<D, WAVES, kSave>), grid, dim3(64 * WAVES), 0, stream, a);
+  else if (a.out_merged)
+    hipLaunchKernelGGL((fine_kernel<D, WAVES, kMerged>), grid, dim3(64 * WAVES), 0, stream, a);
   else
-    hipLaunchKernelGGL((fine_kernel<D, WAVES, false>), grid, dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((fine_kernel<D, WAVES, kPlain>), grid, dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -593,7 +615,7 @@ hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
 hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gates,
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
-                       hipStream_t stream, float* save_o, float* save_lse) {
+                       hipStream_t stream, float* save_o, float* save_lse, uint16_t* out_merged, int heads) {
   FineArgs a;
   a.q = q;
   a.k = k;
@@ -604,6 +626,8 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.out = out;
   a.save_o = save_o;
   a.save_lse = save_lse;
+  a.out_merged = out_merged;
+  a.heads = heads;
   a.n_tok = n_tok;
   a.block = block;
   a.topn = topn;

@@ -19,8 +19,10 @@
 //     each 64 x 64 = 4 x 4 MFMA tiles (64 accumulator registers);
 //   * K streams through LDS in 64-wide chunks, double-buffered: bf16 rows
 //     arrive by direct global->LDS loads into XOR-swizzled [64][64] tiles;
-//     the float32 attention output of the output projection is loaded into
-//     registers one chunk ahead, rounded to bf16 and written to LDS;
+//     within the layer the attention output arrives already in bf16 with the
+//     heads side by side (the fine kernel's merged mode); the stage entry
+//     point's float32 [b][H][N][d] input is instead loaded into registers
+//     one chunk ahead, rounded to bf16 and written to LDS;
 //   * the MFMA computes the transposed tile (features x tokens), so each
 //     lane ends with four consecutive features of one token: the epilogue
 //     stores 8 contiguous bytes per lane (the head split of q, k, v, the
@@ -92,8 +94,9 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 }
 
 // OUT false: input projection (A = x via direct loads, head-split epilogue);
-// OUT true: output projection (A = float32 attention output, residual epilogue)
-template <bool OUT>
+// OUT true: output projection (residual epilogue), A either bf16 [M][K] via
+// direct loads or (A32) the float32 [b][H][N][d] attention output
+template <bool OUT, bool A32>
 __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kGT * kGK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGT * kGK];
@@ -109,24 +112,27 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int wm = w & 1, wf = w >> 1;   // the wave's 64-token and 64-feature quarter
   const int nk = p.K / kGK;
+  // the tile's first token is batch element bi0, position t0 (one division
+  // per workgroup); a tile of 128 tokens spans at most two batch elements
+  // (N >= 192)
+  const long long bi0 = m0 / p.n_tok;
+  const int t0 = (int)(m0 - bi0 * p.n_tok);
 
   // OUT: the float32 attention output of chunk c, rows m0 .. m0+127: thread
   // x handles row x/2, 32 of its 64 k values (8 float4), k = 32*(x%2) + 4*i
   const int ar = threadIdx.x / 2, ah = threadIdx.x % 2;
   float4 areg[8];
+  const bool a_ok = m0 + ar < p.M;
+  const long long a_row = (t0 + ar < p.n_tok) ? bi0 * p.heads * (long long)p.n_tok + t0 + ar
+                                               : (bi0 + 1) * p.heads * (long long)p.n_tok + t0 + ar - p.n_tok;
   auto load_a32 = [&](int c) __attribute__((always_inline)) {
-    const long long m = m0 + ar;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int kk = c * kGK + 32 * ah + 4 * i;          // feature h*d + j of the merged heads
       const int h = kk / p.head_dim, j = kk % p.head_dim;
-      if (m < p.M) {
-        const long long bi = m / p.n_tok, t = m % p.n_tok;
-        areg[i] = *reinterpret_cast<const float4*>(
-            p.a_heads + (((bi * p.heads + h) * (long long)p.n_tok + t) * p.head_dim + j));
-      } else {
-        areg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      areg[i] = a_ok ? *reinterpret_cast<const float4*>(
+                           p.a_heads + ((a_row + (long long)h * p.n_tok) * p.head_dim + j))
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto store_a32 = [&](uint16_t* buf) __attribute__((always_inline)) {
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
     }
   };
   auto stage = [&](int c, int s) __attribute__((always_inline)) {
-    if constexpr (!OUT) stage_bf16(As[s], p.a, m0, p.M, p.K, c * kGK, w);
+    if constexpr (!A32) stage_bf16(As[s], p.a, m0, p.M, p.K, c * kGK, w);
     stage_bf16(Bs[s], p.b, f0, p.F, p.K, c * kGK, w);
   };
 
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[ft][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (OUT) {
+  if constexpr (A32) {
     load_a32(0);
     store_a32(As[0]);
   }
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
     const int s = c & 1;
     if (c + 1 < nk) {
       stage(c + 1, s ^ 1);
-      if constexpr (OUT) load_a32(c + 1);
+      if constexpr (A32) load_a32(c + 1);
     }
     const uint16_t* a_t = As[s] + wm * 64 * kGK;
     const uint16_t* b_t = Bs[s] + wf * 64 * kGK;
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
           acc[ft][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo[ft], ao[mt], acc[ft][mt], 0, 0, 0);
     }
     // buffer s^1 was last read in chunk c-1, before the barrier that ended it
-    if constexpr (OUT) {
+    if constexpr (A32) {
       if (c + 1 < nk) store_a32(As[s ^ 1]);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -191,12 +197,29 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
   }
 
   // epilogue: lane holds features f = f0 + 64*wf + 16*ft + 4*lg + i of token
-  // m = m0 + 64*wm + 16*mt + lr
+  // m = m0 + 64*wm + 16*mt + lr.
+  // the wave's 16-feature groups lie inside one head (head_dim is 32 or 64):
+  // which of q, k, v, the head and the first dimension of group ft
+  const int hd = p.heads * p.head_dim;
+  int g_which[4], g_head[4], g_j0[4];
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft) {
+    const int fg = __builtin_amdgcn_readfirstlane(f0 + 64 * wf + 16 * ft);
+    g_which[ft] = fg / hd;
+    g_head[ft] = (fg % hd) / p.head_dim;
+    g_j0[ft] = fg % p.head_dim;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const long long m = m0 + 64 * wm + 16 * mt + lr;
+    const int row = 64 * wm + 16 * mt + lr;
+    const long long m = m0 + row;
     if (m >= p.M) continue;
-    const long long bi = m / p.n_tok, t = m % p.n_tok;
+    int t = t0 + row;
+    long long bi = bi0;
+    if (t >= p.n_tok) {
+      t -= p.n_tok;
+      bi += 1;
+    }
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft) {
       const int f = f0 + 64 * wf + 16 * ft + 4 * lg;
@@ -211,9 +234,8 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
         o.w = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.w << 16) + r[3]);
         *reinterpret_cast<ushort4*>(p.y + m * p.F + f) = o;
       } else {
-        const int hd = p.heads * p.head_dim;
-        if (f < 3 * hd) {   // four features of one head of one of q, k, v
-          const int which = f / hd, h = (f % hd) / p.head_dim, j = f % p.head_dim;
+        if (g_which[ft] < 3) {   // four features of one head of one of q, k, v
+          const int which = g_which[ft], h = g_head[ft], j = g_j0[ft] + 4 * lg;
           uint16_t* dst = which == 0 ? p.q : (which == 1 ? p.k : p.v);
           ushort4 o;
           o.x = bf16_rne(r[0]); o.y = bf16_rne(r[1]); o.z = bf16_rne(r[2]); o.w = bf16_rne(r[3]);
@@ -232,14 +254,16 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
   }
 }
 
-hipError_t launch_gemm(GemmArgs p, bool out, hipStream_t stream) {
+hipError_t launch_gemm(GemmArgs p, bool out, bool a32, hipStream_t stream) {
   p.m_tiles = (int)((p.M + kGT - 1) / kGT);
   p.f_tiles = (p.F + kGT - 1) / kGT;
   const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
-  if (out)
-    hipLaunchKernelGGL(layer_gemm_kernel<true>, grid, dim3(64 * kGWaves), 0, stream, p);
+  if (!out)
+    hipLaunchKernelGGL((layer_gemm_kernel<false, false>), grid, dim3(64 * kGWaves), 0, stream, p);
+  else if (a32)
+    hipLaunchKernelGGL((layer_gemm_kernel<true, true>), grid, dim3(64 * kGWaves), 0, stream, p);
   else
-    hipLaunchKernelGGL(layer_gemm_kernel<false>, grid, dim3(64 * kGWaves), 0, stream, p);
+    hipLaunchKernelGGL((layer_gemm_kernel<true, false>), grid, dim3(64 * kGWaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -261,7 +285,7 @@ hipError_t launch_layer_in(const uint16_t* x, const uint16_t* w_in, long long ba
   p.k = k;
   p.v = v;
   p.gates = gates;
-  return launch_gemm(p, false, stream);
+  return launch_gemm(p, false, false, stream);
 }
 
 hipError_t launch_layer_out(const float* attn, const uint16_t* w_out, const uint16_t* x, long long batch,
@@ -277,7 +301,24 @@ hipError_t launch_layer_out(const float* attn, const uint16_t* w_out, const uint
   p.head_dim = head_dim;
   p.x = x;
   p.y = y;
-  return launch_gemm(p, true, stream);
+  return launch_gemm(p, true, true, stream);
+}
+
+hipError_t launch_layer_out_merged(const uint16_t* attn_merged, const uint16_t* w_out, const uint16_t* x,
+                                   long long batch, int n_tok, int channels, int heads, int head_dim, uint16_t* y,
+                                   hipStream_t stream) {
+  GemmArgs p = {};
+  p.a = attn_merged;
+  p.b = w_out;
+  p.M = batch * n_tok;
+  p.F = channels;
+  p.K = heads * head_dim;
+  p.n_tok = n_tok;
+  p.heads = heads;
+  p.head_dim = head_dim;
+  p.x = x;
+  p.y = y;
+  return launch_gemm(p, true, false, stream);
 }
 
 }  // namespace mosaic

@@ -187,7 +187,7 @@ LayerWorkspace layer_layout(const Shape& s) {
   w.k = take(e * sizeof(uint16_t));
   w.v = take(e * sizeof(uint16_t));
   w.gates = take((size_t)s.slices * s.n_tok * 3 * sizeof(float));
-  w.attn = take(e * sizeof(float));
+  w.attn = take(e * sizeof(uint16_t));   // bf16 [b][N][H][d], the heads side by side
   w.bsa = take(layout(s).total);
   w.total = o;
   return w;
@@ -370,7 +370,7 @@ mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const vo
   uint16_t* k = reinterpret_cast<uint16_t*>(ws + lw.k);
   uint16_t* v = reinterpret_cast<uint16_t*>(ws + lw.v);
   float* gates = reinterpret_cast<float*>(ws + lw.gates);
-  float* attn = reinterpret_cast<float*>(ws + lw.attn);
+  uint16_t* attn = reinterpret_cast<uint16_t*>(ws + lw.attn);
   char* bws = ws + lw.bsa;
   const Workspace w = layout(s);
   double* qbar = reinterpret_cast<double*>(bws + w.qbar);
@@ -385,11 +385,12 @@ mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const vo
   if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
   e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
-  e = mosaic::launch_fine(q, k, v, gates, ocg, sel_idx, attn, s.slices, s.n_tok, s.d, s.block, s.topn, s.window, hs);
+  e = mosaic::launch_fine(q, k, v, gates, ocg, sel_idx, nullptr, s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
+                          hs, nullptr, nullptr, attn, heads);
   if (e != hipSuccess) return hip_status(e, "bsa_fine launch");
-  return hip_status(mosaic::launch_layer_out(attn, static_cast<const uint16_t*>(w_out),
-                                             static_cast<const uint16_t*>(x), batch, s.n_tok, channels, heads, s.d,
-                                             static_cast<uint16_t*>(y), hs),
+  return hip_status(mosaic::launch_layer_out_merged(attn, static_cast<const uint16_t*>(w_out),
+                                                    static_cast<const uint16_t*>(x), batch, s.n_tok, channels, heads,
+                                                    s.d, static_cast<uint16_t*>(y), hs),
                     "layer output projection launch");
 }
 

@@ -94,13 +94,18 @@ def test_layer_forward(cfg, channels):
     x, w_in, w_out = make_layer_inputs(cfg, channels, device="cuda")
     y, sel = _lib.mosaic_bsa_layer_forward(x, w_in[0], w_out[0], cfg.heads, cfg.head_dim, cfg.nside, cfg.block,
                                            cfg.topn, cfg.window)
-    # the layer equals its stages run one after another (same kernels, same bits)
+    # the layer equals its stages run one after another: the same selection;
+    # y up to the rounding of the attention output, which the layer takes
+    # straight to bf16 inside the fine kernel
     q, k, v, g = _lib.mosaic_bsa_layer_in(x, w_in[0], cfg.heads, cfg.head_dim, cfg.nside)
     attn, sel2 = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
     y2 = _lib.mosaic_bsa_layer_out(attn, w_out[0], x, cfg.nside)
     torch.cuda.synchronize()
     assert torch.equal(sel, sel2)
-    assert torch.equal(y, y2)
+    same = float((y == y2).float().mean())
+    log(f"{cfg.name} layer vs stages: {same:.5f} of y equal")
+    assert same >= 0.999
+    assert float((y.float() - y2.float()).abs().max()) <= 2.0 ** -7 * float(y2.float().abs().max())
 
     ref = oracle.layer_ref(to_f64(x), to_f64(w_in[0]), to_f64(w_out[0]), cfg.heads, cfg.head_dim, cfg.block,
                            cfg.topn, cfg.window, idx=sel.cpu().numpy())
