@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 3
+#define MOSAIC_BSA_ABI_VERSION 4
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -118,6 +118,19 @@ mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const
                               const float* o_cg, const int32_t* sel_idx, int batch, int heads,
                               int head_dim, int nside, int block, int topn, int window, float* out,
                               void* stream);
+
+/* ---- HEALPix coarsening ---------------------------------------------------
+ * A field on the NESTED pixels at nside taken to nside / 2^levels
+ * (papernotes.org ICML2026 notes, 关键设计 › HEALPix + NESTED: the children of
+ * pixel p are 4p .. 4p+3, so a coarse pixel's 4^levels descendants are one
+ * contiguous run of rows; the encoder downsamples to a coarser grid).  The
+ * coarse value is the mean of the descendants, summed in float64.
+ *   x  in : bf16 bits [batch][12*nside^2][channels]
+ *   y  out: float32 [batch][12*(nside>>levels)^2][channels]
+ * channels a multiple of 8; levels >= 1 with nside >> levels >= 1.
+ * Alignment: x and y 16 bytes. */
+mosaic_status mosaic_healpix_coarsen(const void* x, int batch, int channels, int nside, int levels, float* y,
+                                     void* stream);
 
 /* ---- Encoder layer --------------------------------------------------------
  * The papernotes.org ICML2026 notes (关键设计) run several BSA layers at

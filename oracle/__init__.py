@@ -52,4 +52,4 @@ from .bsa_backward import (  # noqa: F401
     bsa_backward_ref,
 )
 from .layer import round_bf16, layer_in_ref, layer_out_ref, layer_ref  # noqa: F401
-from .healpix import npix, nest_children, nest_parent, descendants  # noqa: F401
+from .healpix import npix, nest_children, nest_parent, descendants, coarsen  # noqa: F401

@@ -44,3 +44,20 @@ def descendants(p: int, levels: int) -> list[int]:
             nxt.extend(nest_children(c))
         cur = nxt
     return sorted(cur)
+
+
+def coarsen(x, nside: int, levels: int):
+    """A field on the NESTED pixels at ``nside`` (x [..., 12*nside^2, C])
+    taken to ``nside / 2^levels``: each coarse pixel's value is the mean of
+    its ``levels``-fold descendants (children rule applied ``levels`` times).
+    Plain loop over coarse pixels, float64."""
+    import numpy as np
+
+    x = np.asarray(x, dtype=np.float64)
+    if nside % (1 << levels):
+        raise ValueError("nside must be divisible by 2^levels")
+    coarse = npix(nside >> levels)
+    out = np.empty(x.shape[:-2] + (coarse, x.shape[-1]))
+    for p in range(coarse):
+        out[..., p, :] = x[..., descendants(p, levels), :].mean(axis=-2)
+    return out

@@ -30,6 +30,7 @@ EXPORTED = (
     "mosaic_bsa_compress_select", "mosaic_bsa_fine",
     "mosaic_bsa_saved_bytes", "mosaic_bsa_forward_train",
     "mosaic_bsa_layer_workspace_bytes", "mosaic_bsa_layer_forward", "mosaic_bsa_layer_in", "mosaic_bsa_layer_out",
+    "mosaic_healpix_coarsen",
     "mosaic_bsa_backward_workspace_bytes", "mosaic_bsa_backward",
 )
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
         L.mosaic_bsa_backward_workspace_bytes.restype = S
         L.mosaic_bsa_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.mosaic_healpix_coarsen.restype = I
+        L.mosaic_healpix_coarsen.argtypes = [P, I, I, I, I, P, P]
         L.mosaic_bsa_layer_workspace_bytes.restype = S
         L.mosaic_bsa_layer_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.mosaic_bsa_layer_forward.restype = I
@@ -328,4 +331,14 @@ def mosaic_bsa_layer_out(attn, w_out, x, nside, y=None, stream=None):
         _ptr(attn, torch.float32, (b, heads, n, head_dim), "attn"),
         _ptr(w_out, torch.bfloat16, (c, heads * head_dim), "w_out"), _ptr(x, torch.bfloat16, (b, n, c), "x"),
         b, heads, head_dim, c, nside, _ptr(y, torch.bfloat16, (b, n, c), "y"), _stream(stream)))
+    return y
+
+
+def mosaic_healpix_coarsen(x, nside, levels, y=None, stream=None):
+    """y [b, 12*(nside>>levels)^2, C] fp32: mean of each coarse pixel's descendants, x [b, N, C] bf16."""
+    b, n, c = _layer_dims(x, nside)
+    nc = 12 * (nside >> levels) ** 2
+    y = torch.empty((b, nc, c), dtype=torch.float32, device=x.device) if y is None else y
+    _check(lib().mosaic_healpix_coarsen(_ptr(x, torch.bfloat16, (b, n, c), "x"), b, c, nside, levels,
+                                        _ptr(y, torch.float32, (b, nc, c), "y"), _stream(stream)))
     return y

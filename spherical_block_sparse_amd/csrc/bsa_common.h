@@ -195,6 +195,12 @@ hipError_t launch_layer_out_merged(const uint16_t* attn_merged, const uint16_t* 
                                    long long batch, int n_tok, int channels, int heads, int head_dim, uint16_t* y,
                                    hipStream_t stream);
 
+// HEALPix NESTED coarsening (healpix_coarsen.hip): y [batch][N/4^levels][C]
+// float32 = mean of each run of 4^levels rows of x [batch][N][C] bf16;
+// C a multiple of 8.
+hipError_t launch_coarsen(const uint16_t* x, float* y, long long batch, int n_tok, int channels, int levels,
+                          hipStream_t stream);
+
 // largest m = N/block the backward's inverted-selection kernel holds in LDS
 constexpr int kIndexMaxBlocks = 16384;
 

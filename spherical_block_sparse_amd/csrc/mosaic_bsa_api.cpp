@@ -307,6 +307,29 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
 }
 
 // ---------------------------------------------------------------------------
+// HEALPix coarsening
+
+mosaic_status mosaic_healpix_coarsen(const void* x, int batch, int channels, int nside, int levels, float* y,
+                                     void* stream) {
+  REQUIRE_PTR(x); REQUIRE_PTR(y);
+  REQUIRE_ALIGN(x, 16); REQUIRE_ALIGN(y, 16);
+  if (batch < 1) return fail(MOSAIC_ERR_BAD_SHAPE, "batch (%d) must be >= 1", batch);
+  if (nside < 1 || (nside & (nside - 1)))
+    return fail(MOSAIC_ERR_BAD_SHAPE, "nside (%d) must be a power of two >= 1", nside);
+  if (nside > 8192) return fail(MOSAIC_ERR_UNSUPPORTED, "nside %d: N = 12*nside^2 must fit in int32", nside);
+  if (levels < 1 || (nside >> levels) < 1 || ((nside >> levels) << levels) != nside)
+    return fail(MOSAIC_ERR_BAD_SHAPE, "levels (%d) must be >= 1 with nside / 2^levels >= 1", levels);
+  if (channels < 8 || channels % 8)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "channels %d: the kernel needs a multiple of 8", channels);
+  const long long n_tok = 12LL * nside * nside;
+  if ((long long)batch * n_tok * channels / 8 > 0x7fffffffLL * 256LL)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "batch*N*channels too large for one launch");
+  return hip_status(mosaic::launch_coarsen(static_cast<const uint16_t*>(x), y, batch, (int)n_tok, channels, levels,
+                                           static_cast<hipStream_t>(stream)),
+                    "healpix_coarsen launch");
+}
+
+// ---------------------------------------------------------------------------
 // encoder layer
 
 

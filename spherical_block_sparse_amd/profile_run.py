@@ -7,7 +7,8 @@
 `reps` times on the workload's synthetic inputs (the earlier stages run once
 beforehand to produce their inputs); --stage backward runs the training
 forward once and then the backward from its saved state `reps` times, with
-a seeded float32 upstream gradient.  --copy-mib N copies an N MiB buffer with torch's
+a seeded float32 upstream gradient.  --order ring lays the same field out in
+RING (iso-latitude) token order.  --copy-mib N copies an N MiB buffer with torch's
 elementwise copy kernel `reps` times: N MiB read and N MiB written per call,
 the calibration of the FETCH_SIZE / WRITE_SIZE counters.
 """
@@ -29,6 +30,8 @@ def main() -> int:
     ap.add_argument("--stage", default="fine", choices=["pool", "select", "fine", "forward", "train", "backward"])
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--order", default="nested", choices=["nested", "ring"],
+                    help="token order of the inputs (ring: the same field laid out by iso-latitude rings)")
     args = ap.parse_args()
 
     if args.copy_mib:
@@ -43,6 +46,10 @@ def main() -> int:
 
     cfg = CONFIGS[args.config]
     q, k, v, g = make_inputs(cfg, device="cuda", dtype=torch.bfloat16)
+    if args.order == "ring":
+        from .locality_study import permute_tokens
+        from .synth import nest_ring_order
+        q, k, v, g = permute_tokens([q, k, v, g], nest_ring_order(cfg.nside))
     qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
     torch.cuda.synchronize()

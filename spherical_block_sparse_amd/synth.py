@@ -103,12 +103,10 @@ def _compact_even_bits(v: np.ndarray) -> np.ndarray:
     return v
 
 
-def pix2vec_nest(nside: int) -> np.ndarray:
-    """Unit vectors of the centres of all 12*nside^2 NESTED pixels, [N, 3] f64.
-
-    The in-face coordinates (ix, iy) are the even and odd bits of the index
-    within the base face; ring number and azimuth follow from the face's
-    position (polar caps above/below |z| = 2/3, equatorial belt between)."""
+def _nest_ring_coords(nside: int):
+    """Ring number jr (1 .. 4*nside-1, north to south), pixel-in-ring jp
+    (1-based, eastward), pixels in the ring nr/4 (nr) and the belt shift of
+    every NESTED pixel."""
     if nside < 1 or nside & (nside - 1):
         raise ValueError("nside must be a power of two")
     npface = nside * nside
@@ -122,12 +120,33 @@ def pix2vec_nest(nside: int) -> np.ndarray:
     south = jr > 3 * nside
     belt = ~(north | south)
     nr = np.where(north, jr, np.where(south, 4 * nside - jr, nside))
-    cap_z = 1.0 - nr.astype(np.float64) ** 2 / (3.0 * npface)
-    z = np.where(north, cap_z, np.where(south, -cap_z, (2 * nside - jr) * (2.0 / (3.0 * nside))))
     kshift = np.where(belt, (jr - nside) & 1, 0)
     jp = (_JPLL[face] * nr + ix - iy + 1 + kshift) // 2
     jp = np.where(jp > 4 * nside, jp - 4 * nside, jp)
     jp = np.where(jp < 1, jp + 4 * nside, jp)
+    return jr, jp, nr, kshift
+
+
+def nest_ring_order(nside: int) -> np.ndarray:
+    """NESTED indices of the pixels in RING order (iso-latitude rings north to
+    south, each from azimuth 0 eastward): the layout of a latitude-longitude
+    raster on the same mesh, used to compare block locality with NESTED."""
+    jr, jp, _, _ = _nest_ring_coords(nside)
+    return np.lexsort((jp, jr))
+
+
+def pix2vec_nest(nside: int) -> np.ndarray:
+    """Unit vectors of the centres of all 12*nside^2 NESTED pixels, [N, 3] f64.
+
+    The in-face coordinates (ix, iy) are the even and odd bits of the index
+    within the base face; ring number and azimuth follow from the face's
+    position (polar caps above/below |z| = 2/3, equatorial belt between)."""
+    jr, jp, nr, kshift = _nest_ring_coords(nside)
+    npface = nside * nside
+    north = jr < nside
+    south = jr > 3 * nside
+    cap_z = 1.0 - nr.astype(np.float64) ** 2 / (3.0 * npface)
+    z = np.where(north, cap_z, np.where(south, -cap_z, (2 * nside - jr) * (2.0 / (3.0 * nside))))
     phi = (jp - (kshift + 1) * 0.5) * (np.pi / (2.0 * nr))
     sth = np.sqrt((1.0 - z) * (1.0 + z))
     return np.stack([sth * np.cos(phi), sth * np.sin(phi), z], axis=1)

@@ -41,7 +41,7 @@ def test_header_declares_and_library_exports_the_same_symbols():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.mosaic_bsa_abi_version() == 3
+    assert L.mosaic_bsa_abi_version() == 4
     for code, name in _lib.STATUS_NAMES.items():
         assert L.mosaic_status_string(code).decode() == name
     assert L.mosaic_status_string(99).decode() == "MOSAIC_ERR_UNKNOWN"
@@ -225,3 +225,18 @@ def test_layer_workspace_bytes():
         L.mosaic_bsa_workspace_bytes(b, h, d, nside, block, topn)
     assert floor <= got < floor + 8 * 256
     assert L.mosaic_bsa_layer_workspace_bytes(b, h, d, 100, nside, block, topn) == 0
+
+
+def test_coarsen_validation():
+    L = _lib.lib()
+    f = L.mosaic_healpix_coarsen
+    assert f(None, 1, 64, 32, 1, FAKE, None) == NULL
+    assert f(FAKE, 1, 64, 32, 1, None, None) == NULL
+    assert f(FAKE + 8, 1, 64, 32, 1, FAKE, None) == MISAL
+    assert f(FAKE, 1, 64, 32, 1, FAKE + 4, None) == MISAL
+    assert f(FAKE, 0, 64, 32, 1, FAKE, None) == SHAPE
+    assert f(FAKE, 1, 64, 24, 1, FAKE, None) == SHAPE      # nside not a power of two
+    assert f(FAKE, 1, 64, 32, 0, FAKE, None) == SHAPE      # levels < 1
+    assert f(FAKE, 1, 64, 32, 6, FAKE, None) == SHAPE      # nside / 2^6 < 1
+    assert f(FAKE, 1, 60, 32, 1, FAKE, None) == UNSUP      # channels not a multiple of 8
+    assert _lib.lib().mosaic_last_error().decode() != ""

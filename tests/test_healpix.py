@@ -91,3 +91,40 @@ def test_children_lie_inside_parent(nside):
 def test_centres_distinct():
     v = pix2vec_nest(8)
     assert np.unique(np.round(v, 10), axis=0).shape[0] == v.shape[0]
+
+
+def test_coarsen_pins():
+    from oracle import coarsen, npix, pool_mean
+    r = np.random.default_rng(7)
+    nside = 8
+    x = r.standard_normal((2, npix(nside), 5))
+    # one level twice equals two levels at once (means of equal-size groups)
+    np.testing.assert_allclose(coarsen(coarsen(x, nside, 1), nside // 2, 1), coarsen(x, nside, 2), rtol=1e-12, atol=1e-15)
+    # the global mean is kept
+    np.testing.assert_allclose(coarsen(x, nside, 3).mean(axis=1), x.mean(axis=1), rtol=1e-12)
+    # a field constant on the coarse pixels comes back unchanged
+    c = r.integers(-64, 64, (npix(nside // 4), 5)) / 8.0   # dyadic: the sums are exact
+    np.testing.assert_array_equal(coarsen(np.repeat(c, 16, axis=0), nside, 2), c)
+    # equals the BSA oracle's block mean with block 4^levels (reshape-mean, written separately)
+    np.testing.assert_allclose(coarsen(x[0], nside, 2), pool_mean(x[0], 16), rtol=1e-12, atol=1e-15)
+    # levels 0 is the identity
+    np.testing.assert_array_equal(coarsen(x, nside, 0), x)
+
+
+def test_ring_order_textbook_values():
+    from spherical_block_sparse_amd.synth import nest_ring_order
+    # at Nside 1 the two schemes number the 12 base pixels alike
+    np.testing.assert_array_equal(nest_ring_order(1), np.arange(12))
+    # Nside 2: the polar ring is the top corner (child 3) of base pixels 0..3,
+    # the next ring alternates children 2 and 1; the south polar ring is child 0 of 8..11
+    o = nest_ring_order(2)
+    np.testing.assert_array_equal(o[:12], [3, 7, 11, 15, 2, 1, 6, 5, 10, 9, 14, 13])
+    np.testing.assert_array_equal(o[-4:], [32, 36, 40, 44])
+    for nside in (4, 16):
+        o = nest_ring_order(nside)
+        assert sorted(o.tolist()) == list(range(healpix.npix(nside)))
+        v = pix2vec_nest(nside)[o]
+        assert np.all(np.diff(v[:, 2]) <= 1e-12)              # north to south
+        phi = np.mod(np.arctan2(v[:, 1], v[:, 0]), 2 * np.pi)
+        same_ring = np.abs(np.diff(v[:, 2])) < 1e-12
+        assert np.all(np.diff(phi)[same_ring] > 0)            # eastward inside a ring
