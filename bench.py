@@ -14,7 +14,9 @@ gradient), and the backward that recomputes that state, are timed after each
 forward and reported under "backward"; they are not part of the step.  So is
 a stack of encoder layers on the primary workload (512 channels, 4 layers,
 synthetic weights: input projection, BSA, output projection with the
-residual), reported under "encoder_layer".  Prints one JSON line.
+residual, plus one level of HEALPix coarsening of its input), reported
+under "encoder_layer", and the lat-lon -> HEALPix interpolation (0.25-degree
+grid onto Nside 256), reported under "interpolation".  Prints one JSON line.
 
 Roofline of the dominant kernel (the fine-attention kernel, bf16 MFMA):
 algorithmic FLOPs per launch = sum over queries of 4*d*(n*block + |window(t)|)
@@ -225,6 +227,12 @@ def measure_layer(cfg: BSAConfig, channels: int, layers: int, steps: int) -> dic
     lin = lambda: _lib.mosaic_bsa_layer_in(x, w_in[0], h, d, cfg.nside, q, k, v, g)
     lout = lambda: _lib.mosaic_bsa_layer_out(attn, w_out[0], x, cfg.nside, ys[0])
     in_ms, out_ms = time_stream(lin, 5), time_stream(lout, 5)
+    # HEALPix coarsening of the layer input by one level (Nside 128 -> 64)
+    xc = _lib.mosaic_healpix_coarsen(x, cfg.nside, 1)
+    co = lambda: _lib.mosaic_healpix_coarsen(x, cfg.nside, 1, y=xc)
+    co_ms = time_stream(co, 5)
+    co_bytes = float(x.numel() * 2 + xc.numel() * 4)
+    del xc
     m_tok = b * n
     in_fl = 2.0 * m_tok * channels * (3 * h * d + 3 * h)
     out_fl = 2.0 * m_tok * (h * d) * channels
@@ -235,7 +243,30 @@ def measure_layer(cfg: BSAConfig, channels: int, layers: int, steps: int) -> dic
                         "frac_bf16_peak": in_fl / (in_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
             "out_proj": {"ms": out_ms, "TFLOPs": out_fl / (out_ms * 1e-3) / 1e12,
                          "frac_bf16_peak": out_fl / (out_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-            "weights": "synthetic N(0, 1/fan_in), bf16"}
+            "weights": "synthetic N(0, 1/fan_in), bf16",
+            "coarsen_1_level": {"ms": co_ms, "bytes": co_bytes, "GBs": co_bytes / (co_ms * 1e-3) / 1e9,
+                                "frac_hbm_peak": co_bytes / (co_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+
+
+def measure_interp(steps: int) -> dict:
+    """The lat-lon -> HEALPix interpolation: the 0.25-degree grid (721 x 1440)
+    onto Nside 256 for 2 members x 16 heads (d = dv = 64, a 4 x 4 stencil)."""
+    from spherical_block_sparse_amd.synth import make_interp_inputs
+    print("[bench] interpolation 721x1440 -> Nside 256, 32 slices", file=sys.stderr, flush=True)
+    s_, n_lat, n_lon, nside = 32, 721, 1440, 256
+    k, v, w_q, nbr, rel = make_interp_inputs(nside, n_lat, n_lon, s_, device="cuda", seed=nside)
+    out = _lib.mosaic_interp_attention(k, v, w_q, nbr, rel)
+    ws = torch.empty(_lib.mosaic_interp_workspace_bytes(s_, n_lat * n_lon), dtype=torch.uint8, device="cuda")
+    fn = lambda: _lib.mosaic_interp_attention(k, v, w_q, nbr, rel, out=out, workspace=ws)
+    ms = time_stream(fn, max(3, steps // 2))
+    n_src, n_dst, kk = n_lat * n_lon, nbr.shape[0], nbr.shape[1]
+    # each source row once (k, v), the stencil once, each output once
+    byts = float(s_ * n_src * (64 + 64) * 2 + n_dst * kk * 16 + s_ * n_dst * 64 * 4)
+    del k, v, w_q, nbr, rel, out, ws
+    return {"workload": "0.25-degree lat-lon (721 x 1440) -> HEALPix Nside 256, 2 members x 16 heads, "
+                        "d = dv = 64, 4 x 4 stencil", "ms": ms, "targets_per_s": s_ * n_dst / (ms * 1e-3),
+            "algorithmic_bytes": byts, "GBs": byts / (ms * 1e-3) / 1e9,
+            "frac_hbm_peak": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
 def cpu_baseline(cfg: BSAConfig, inputs, budget_s: float) -> dict:
@@ -282,6 +313,7 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true", help="skip the (secondary) backward timing")
     ap.add_argument("--layer-channels", type=int, default=512, help="encoder-layer width (0: skip the layer timing)")
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--no-interp", action="store_true", help="skip the interpolation timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the BSA slices are independent and this build has no "
@@ -303,6 +335,10 @@ def main() -> int:
     layer = None
     if args.layer_channels:
         layer = measure_layer(cfg, args.layer_channels, args.layers, args.steps)
+        torch.cuda.empty_cache()
+    interp = None
+    if not args.no_interp:
+        interp = measure_interp(args.steps)
         torch.cuda.empty_cache()
 
     secondary = None
@@ -360,6 +396,7 @@ def main() -> int:
         },
         "backward": r["backward"],
         "encoder_layer": layer,
+        "interpolation": interp,
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

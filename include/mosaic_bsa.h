@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 4
+#define MOSAIC_BSA_ABI_VERSION 5
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -131,6 +131,26 @@ mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const
  * Alignment: x and y 16 bytes. */
 mosaic_status mosaic_healpix_coarsen(const void* x, int batch, int channels, int nside, int levels, float* y,
                                      void* stream);
+
+/* ---- Lat-lon -> HEALPix cross-attention interpolation ---------------------
+ * papernotes.org ICML2026 notes, 关键设计 › HEALPix + NESTED: each HEALPix
+ * target i attends over its neighbouring source points j with the relative
+ * positions as queries, o_i = sum_{j in N_i} softmax_j(q_ij^T k_j/sqrt(d)) v_j;
+ * here q_ij = w_q p_ij (this library's reading).
+ *   k        in : bf16 bits [slices][n_src][d]     source keys
+ *   v        in : bf16 bits [slices][n_src][dv]    source values (dv = 64)
+ *   w_q      in : float32 [d][3]                  query map of the relative position
+ *   nbr      in : int32 [n_dst][n_nbr]            source indices of each target
+ *                 (1 <= n_nbr <= 16; values clamped into [0, n_src))
+ *   rel      in : float32 [n_dst][n_nbr][3]       relative positions p_ij
+ *   out      out: float32 [slices][n_dst][dv]
+ *   workspace   : at least mosaic_interp_workspace_bytes(slices, n_src)
+ * d a multiple of 8 in [8, 256].  Alignment: k, v, out 16 bytes, workspace
+ * 256, the rest 4. */
+size_t mosaic_interp_workspace_bytes(int slices, int n_src);
+mosaic_status mosaic_interp_attention(const void* k, const void* v, const float* w_q, const int32_t* nbr,
+                                      const float* rel, int slices, int n_src, int n_dst, int n_nbr, int d, int dv,
+                                      float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Encoder layer --------------------------------------------------------
  * The papernotes.org ICML2026 notes (关键设计) run several BSA layers at

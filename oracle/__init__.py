@@ -1,5 +1,6 @@
 """Float64 CPU oracle for the MOSAIC mesh-aligned block-sparse attention (BSA)
-forward pass, its gradient, and the encoder layer around it.
+forward pass, its gradient, the encoder layer around it, HEALPix coarsening
+and the lat-lon -> HEALPix cross-attention interpolation.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
 only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -23,7 +24,7 @@ reading is listed in the module docstring of ``oracle.bsa``.
 
 Parity status: every function here is pinned by ``tests/test_oracle.py`` /
 ``tests/test_oracle_backward.py`` / ``tests/test_oracle_layer.py`` /
-``tests/test_healpix.py`` against
+``tests/test_oracle_interp.py`` / ``tests/test_healpix.py`` against
 finite differences, an independent autograd derivation, closed forms, library routines (torch's
 float64 scaled_dot_product_attention), brute force and invariants.  No
 function is "parity unpinned".
@@ -52,4 +53,5 @@ from .bsa_backward import (  # noqa: F401
     bsa_backward_ref,
 )
 from .layer import round_bf16, layer_in_ref, layer_out_ref, layer_ref  # noqa: F401
+from .interp import interp_attention, interp_attention_ref  # noqa: F401
 from .healpix import npix, nest_children, nest_parent, descendants, coarsen  # noqa: F401

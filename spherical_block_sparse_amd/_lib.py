@@ -30,7 +30,7 @@ EXPORTED = (
     "mosaic_bsa_compress_select", "mosaic_bsa_fine",
     "mosaic_bsa_saved_bytes", "mosaic_bsa_forward_train",
     "mosaic_bsa_layer_workspace_bytes", "mosaic_bsa_layer_forward", "mosaic_bsa_layer_in", "mosaic_bsa_layer_out",
-    "mosaic_healpix_coarsen",
+    "mosaic_healpix_coarsen", "mosaic_interp_workspace_bytes", "mosaic_interp_attention",
     "mosaic_bsa_backward_workspace_bytes", "mosaic_bsa_backward",
 )
 
@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
         L.mosaic_bsa_backward_workspace_bytes.restype = S
         L.mosaic_bsa_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.mosaic_interp_workspace_bytes.restype = S
+        L.mosaic_interp_workspace_bytes.argtypes = [I, I]
+        L.mosaic_interp_attention.restype = I
+        L.mosaic_interp_attention.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, S, P]
         L.mosaic_healpix_coarsen.restype = I
         L.mosaic_healpix_coarsen.argtypes = [P, I, I, I, I, P, P]
         L.mosaic_bsa_layer_workspace_bytes.restype = S
@@ -342,3 +346,25 @@ def mosaic_healpix_coarsen(x, nside, levels, y=None, stream=None):
     _check(lib().mosaic_healpix_coarsen(_ptr(x, torch.bfloat16, (b, n, c), "x"), b, c, nside, levels,
                                         _ptr(y, torch.float32, (b, nc, c), "y"), _stream(stream)))
     return y
+
+
+def mosaic_interp_workspace_bytes(slices, n_src) -> int:
+    return lib().mosaic_interp_workspace_bytes(slices, n_src)
+
+
+def mosaic_interp_attention(k, v, w_q, nbr, rel, out=None, workspace=None, stream=None):
+    """out [S, n_dst, 64] fp32: cross-attention of each target over its neighbours (k, v bf16
+    [S, n_src, d] / [S, n_src, 64], w_q [d, 3] fp32, nbr [n_dst, K] int32, rel [n_dst, K, 3] fp32)."""
+    s, n_src, d = k.shape
+    dv = v.shape[-1]
+    n_dst, n_nbr = nbr.shape
+    out = torch.empty((s, n_dst, dv), dtype=torch.float32, device=k.device) if out is None else out
+    need = mosaic_interp_workspace_bytes(s, n_src)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    _check(lib().mosaic_interp_attention(
+        _ptr(k, torch.bfloat16, (s, n_src, d), "k"), _ptr(v, torch.bfloat16, (s, n_src, dv), "v"),
+        _ptr(w_q, torch.float32, (d, 3), "w_q"), _ptr(nbr, torch.int32, (n_dst, n_nbr), "nbr"),
+        _ptr(rel, torch.float32, (n_dst, n_nbr, 3), "rel"), s, n_src, n_dst, n_nbr, d, dv,
+        _ptr(out, torch.float32, (s, n_dst, dv), "out"), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out

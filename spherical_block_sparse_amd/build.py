@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmosaic_bsa.so")
 
 SOURCES = ["bsa_pool.hip", "bsa_compress_select.hip", "bsa_fine.hip", "bsa_backward.hip", "bsa_layer.hip",
-           "healpix_coarsen.hip", "mosaic_bsa_api.cpp"]
+           "healpix_coarsen.hip", "healpix_interp.hip", "mosaic_bsa_api.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

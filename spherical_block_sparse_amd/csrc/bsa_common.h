@@ -201,6 +201,14 @@ hipError_t launch_layer_out_merged(const uint16_t* attn_merged, const uint16_t* 
 hipError_t launch_coarsen(const uint16_t* x, float* y, long long batch, int n_tok, int channels, int levels,
                           hipStream_t stream);
 
+// Lat-lon -> HEALPix cross-attention interpolation (healpix_interp.hip):
+// k [S][n_src][d], v [S][n_src][64] bf16; w_q [d][3]; nbr [n_dst][n_nbr]
+// (n_nbr <= 16), rel [n_dst][n_nbr][3]; out [S][n_dst][64] float32;
+// kappa: workspace of S*n_src float4.
+hipError_t launch_interp(const uint16_t* k, const uint16_t* v, const float* w_q, const int32_t* nbr,
+                         const float* rel, long long slices, int n_src, int n_dst, int n_nbr, int d, float* out,
+                         float4* kappa, hipStream_t stream);
+
 // largest m = N/block the backward's inverted-selection kernel holds in LDS
 constexpr int kIndexMaxBlocks = 16384;
 

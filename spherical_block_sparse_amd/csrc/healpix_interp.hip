@@ -1,0 +1,134 @@
+// Lat-lon -> HEALPix cross-attention interpolation.
+//
+// Source: papernotes.org ICML2026 notes, 关键设计 › HEALPix + NESTED: for each
+// HEALPix target i, the relative positions p_ij of its neighbouring source
+// points are the queries and the source features the keys and values,
+// o_i = sum_{j in N_i} softmax_j(q_ij^T k_j / sqrt(d)) v_j, with q_ij a
+// linear map W_q p_ij of the 3-vector p_ij (this library's reading).
+//
+// Since q_ij^T k_j = p_ij^T (W_q^T k_j), the scores need only the 3-vector
+// kappa_j = W_q^T k_j / sqrt(d) of each source point, formed once:
+//   * kappa_kernel: eight lanes per source row (a wave reads eight whole
+//     rows), W_q in LDS, float32 dot products of the bf16 row summed across
+//     the eight lanes; HBM-bound (d*2 bytes read, 16 written);
+//   * interp_kernel: one 16-lane group per target.  Lane l holds neighbour l
+//     (index, relative position, kappa -> score); max and sum over the group
+//     by shuffles; then lane l accumulates output dims 4l .. 4l+3 over the
+//     neighbours, each neighbour's v row read by the 16 lanes as one
+//     contiguous 128-byte line, all 16 rows in flight at once.  Targets in NESTED order share most of
+//     their stencils, so the gathered rows hit in L2; the workgroup order is
+//     XCD-contiguous.  HBM-bound.
+#include "bsa_common.h"
+
+#include <math.h>
+
+namespace mosaic {
+namespace {
+
+__global__ __launch_bounds__(256) void kappa_kernel(const uint16_t* k, const float* w_q, float4* kappa, long long rows,
+                                                    int d, float inv_sqrt_d) {
+  __shared__ float W[256 * 3];
+  for (int e = threadIdx.x; e < 3 * d; e += 256) W[e] = w_q[e];
+  __syncthreads();
+  // 8 lanes per row, each taking 16-byte pieces 8*e, 8*e + 64, ... of it, so
+  // a wave reads 8 consecutive rows as one contiguous span
+  const long long row = (long long)blockIdx.x * 32 + threadIdx.x / 8;
+  const int e = threadIdx.x % 8;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+  if (row < rows) {
+    const uint16_t* src = k + row * d;
+    for (int c = 8 * e; c < d; c += 64) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src + c);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = __builtin_bit_cast(float, i & 1 ? (w[i / 2] & 0xffff0000u) : (w[i / 2] << 16));
+        const float* wr = W + 3 * (c + i);   // w_q[d][3], row c + i
+        a0 = fmaf(wr[0], x, a0);
+        a1 = fmaf(wr[1], x, a1);
+        a2 = fmaf(wr[2], x, a2);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    a0 += __shfl_xor(a0, o, 8);
+    a1 += __shfl_xor(a1, o, 8);
+    a2 += __shfl_xor(a2, o, 8);
+  }
+  if (row < rows && e == 0) kappa[row] = make_float4(a0 * inv_sqrt_d, a1 * inv_sqrt_d, a2 * inv_sqrt_d, 0.f);
+}
+
+__global__ __launch_bounds__(256) void interp_kernel(const float4* kappa, const uint16_t* v, const int32_t* nbr,
+                                                     const float* rel, float* out, long long groups, int n_src,
+                                                     int n_dst, int n_nbr) {
+  constexpr int DV = 64;
+  long long logical;
+  {
+    const long long g = gridDim.x, b = blockIdx.x, q8 = g / 8, r8 = g % 8, xcd = b % 8, kq = b / 8;
+    logical = xcd < r8 ? xcd * (q8 + 1) + kq : r8 * (q8 + 1) + (xcd - r8) * q8 + kq;
+  }
+  const long long item = logical * 16 + threadIdx.x / 16;   // (slice, target)
+  if (item >= groups) return;                                // whole 16-lane groups leave together
+  const long long s = item / n_dst;
+  const int i = (int)(item - s * n_dst);
+  const int l = threadIdx.x % 16;
+
+  int j = 0;
+  float score = -INFINITY;
+  if (l < n_nbr) {
+    j = nbr[(long long)i * n_nbr + l];
+    j = j < 0 ? 0 : (j >= n_src ? n_src - 1 : j);
+    const float* p = rel + ((long long)i * n_nbr + l) * 3;
+    const float4 kp = kappa[s * n_src + j];
+    score = p[0] * kp.x + p[1] * kp.y + p[2] * kp.z;
+  }
+  float mx = score;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+  const float e = l < n_nbr ? __expf(score - mx) : 0.f;
+  float sum = e;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 16);
+  const float pw = e / sum;
+
+  // all 16 rows are loaded before any is used (a lane past n_nbr has index 0
+  // and weight 0), so the group waits for one round of L2 latency, not 16
+  const uint16_t* vs = v + s * (long long)n_src * DV + 4 * l;
+  ushort4 rows[16];
+  float pjs[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int jn = __shfl(j, jj, 16);
+    pjs[jj] = __shfl(pw, jj, 16);
+    rows[jj] = *reinterpret_cast<const ushort4*>(vs + (long long)jn * DV);
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const ushort4 b = rows[jj];
+    acc.x = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.x << 16), acc.x);
+    acc.y = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.y << 16), acc.y);
+    acc.z = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.z << 16), acc.z);
+    acc.w = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.w << 16), acc.w);
+  }
+  *reinterpret_cast<float4*>(out + item * DV + 4 * l) = acc;
+}
+
+}  // namespace
+
+hipError_t launch_interp(const uint16_t* k, const uint16_t* v, const float* w_q, const int32_t* nbr,
+                         const float* rel, long long slices, int n_src, int n_dst, int n_nbr, int d, float* out,
+                         float4* kappa, hipStream_t stream) {
+  const long long rows = slices * n_src;
+  hipLaunchKernelGGL(kappa_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, k, w_q, kappa, rows, d,
+                     (float)(1.0 / sqrt((double)d)));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long groups = slices * n_dst;
+  hipLaunchKernelGGL(interp_kernel, dim3((unsigned)((groups + 15) / 16)), dim3(256), 0, stream, kappa, v, nbr, rel,
+                     out, groups, n_src, n_dst, n_nbr);
+  return hipGetLastError();
+}
+
+}  // namespace mosaic

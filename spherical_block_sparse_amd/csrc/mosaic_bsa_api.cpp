@@ -330,6 +330,38 @@ mosaic_status mosaic_healpix_coarsen(const void* x, int batch, int channels, int
 }
 
 // ---------------------------------------------------------------------------
+// lat-lon -> HEALPix interpolation
+
+size_t mosaic_interp_workspace_bytes(int slices, int n_src) {
+  if (slices < 1 || n_src < 1) return 0;
+  return align256((size_t)slices * n_src * 4 * sizeof(float));
+}
+
+mosaic_status mosaic_interp_attention(const void* k, const void* v, const float* w_q, const int32_t* nbr,
+                                      const float* rel, int slices, int n_src, int n_dst, int n_nbr, int d, int dv,
+                                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(w_q); REQUIRE_PTR(nbr); REQUIRE_PTR(rel); REQUIRE_PTR(out);
+  REQUIRE_PTR(workspace);
+  REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(w_q, 4); REQUIRE_ALIGN(nbr, 4); REQUIRE_ALIGN(rel, 4);
+  REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(workspace, 256);
+  if (slices < 1 || n_src < 1 || n_dst < 1)
+    return fail(MOSAIC_ERR_BAD_SHAPE, "slices (%d), n_src (%d) and n_dst (%d) must be >= 1", slices, n_src, n_dst);
+  if (n_nbr < 1 || n_nbr > 16)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "n_nbr %d: the kernel takes 1 .. 16 neighbours per target", n_nbr);
+  if (d < 8 || d > 256 || d % 8) return fail(MOSAIC_ERR_UNSUPPORTED, "d %d: a multiple of 8 in [8, 256]", d);
+  if (dv != 64) return fail(MOSAIC_ERR_UNSUPPORTED, "dv %d: the kernel takes 64 value channels", dv);
+  if ((long long)slices * n_src / 32 > 0x7fffffffLL || (long long)slices * n_dst / 16 > 0x7fffffffLL)
+    return fail(MOSAIC_ERR_UNSUPPORTED, "slices*n_src or slices*n_dst too large for one launch");
+  const size_t need = mosaic_interp_workspace_bytes(slices, n_src);
+  if (workspace_bytes < need)
+    return fail(MOSAIC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(mosaic::launch_interp(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), w_q, nbr,
+                                          rel, slices, n_src, n_dst, n_nbr, d, out, static_cast<float4*>(workspace),
+                                          static_cast<hipStream_t>(stream)),
+                    "interpolation launch");
+}
+
+// ---------------------------------------------------------------------------
 // encoder layer
 
 

@@ -248,3 +248,62 @@ def make_layer_inputs(cfg: BSAConfig, channels: int, layers: int = 1, device="cp
     w_out = (torch.randn((layers, channels, hd), generator=gen, device=device, dtype=torch.float32)
              / math.sqrt(hd)).to(torch.bfloat16)
     return x, w_in, w_out
+
+
+# --------------------------------------------------------------------------
+# lat-lon source grid and its stencil around HEALPix targets
+# --------------------------------------------------------------------------
+
+def latlon_vectors(n_lat: int, n_lon: int) -> np.ndarray:
+    """Unit vectors of a regular latitude-longitude grid with both poles:
+    row r at latitude 90 - 180*r/(n_lat-1) degrees, column c at longitude
+    360*c/n_lon; [n_lat*n_lon, 3], row-major."""
+    lat = np.radians(90.0 - 180.0 * np.arange(n_lat) / (n_lat - 1))
+    lon = np.radians(360.0 * np.arange(n_lon) / n_lon)
+    cl = np.cos(lat)[:, None]
+    return np.stack([np.broadcast_to(cl * np.cos(lon)[None, :], (n_lat, n_lon)),
+                     np.broadcast_to(cl * np.sin(lon)[None, :], (n_lat, n_lon)),
+                     np.broadcast_to(np.sin(lat)[:, None], (n_lat, n_lon))], axis=-1).reshape(-1, 3)
+
+
+def latlon_stencil(nside: int, n_lat: int, n_lon: int):
+    """The source neighbourhood of every HEALPix NESTED pixel on a lat-lon
+    grid: the 4 x 4 grid points around the pixel centre (rows r0-1 .. r0+2
+    clamped at the poles, columns c0-1 .. c0+2 wrapped in longitude, with
+    (r0, c0) the grid cell holding the centre), and each one's position
+    relative to the centre, (u_j - u_i) / spacing with the grid spacing in
+    radians.  Returns nbr [N, 16] int32 and rel [N, 16, 3] float32."""
+    u = pix2vec_nest(nside)
+    lat = np.degrees(np.arcsin(np.clip(u[:, 2], -1.0, 1.0)))
+    lon = np.mod(np.degrees(np.arctan2(u[:, 1], u[:, 0])), 360.0)
+    dlat, dlon = 180.0 / (n_lat - 1), 360.0 / n_lon
+    r0 = np.minimum(np.floor((90.0 - lat) / dlat).astype(np.int64), n_lat - 2)
+    c0 = np.floor(lon / dlon).astype(np.int64) % n_lon
+    rows = np.clip(r0[:, None] + np.arange(-1, 3)[None, :], 0, n_lat - 1)        # [N, 4]
+    cols = (c0[:, None] + np.arange(-1, 3)[None, :]) % n_lon                      # [N, 4]
+    nbr = (rows[:, :, None] * n_lon + cols[:, None, :]).reshape(-1, 16)
+    src = latlon_vectors(n_lat, n_lon)
+    rel = (src[nbr] - u[:, None, :]) / np.radians(dlat)
+    return nbr.astype(np.int32), rel.astype(np.float32)
+
+
+def make_interp_inputs(nside: int, n_lat: int, n_lon: int, slices: int, d: int = 64, dv: int = 64,
+                       device="cpu", seed: int = 0):
+    """Source keys and values on the lat-lon grid (smooth cosine-mode fields
+    of the grid points' unit vectors, bf16 [slices, n_src, d] and
+    [slices, n_src, dv]), the relative-position query weights w_q [d, 3]
+    (float32, N(0, 1)), and the stencil of ``latlon_stencil``."""
+    seeds = _stream_seeds(seed + 2000)
+    u = torch.from_numpy(latlon_vectors(n_lat, n_lon)).to(device=device, dtype=torch.float32)
+    n_src = u.shape[0]
+    out = []
+    for s, ch in zip(seeds[:2], (d, dv)):
+        gen = _generator(device, s)
+        t = torch.empty((slices, n_src, ch), dtype=torch.bfloat16, device=device)
+        for i in range(slices):
+            t[i].copy_(_fourier_field(u, ch, gen))
+        out.append(t)
+    gen = _generator(device, seeds[2])
+    w_q = torch.randn((d, 3), generator=gen, device=device, dtype=torch.float32)
+    nbr, rel = latlon_stencil(nside, n_lat, n_lon)
+    return out[0], out[1], w_q, torch.from_numpy(nbr).to(device), torch.from_numpy(rel).to(device)

@@ -41,7 +41,7 @@ def test_header_declares_and_library_exports_the_same_symbols():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.mosaic_bsa_abi_version() == 4
+    assert L.mosaic_bsa_abi_version() == 5
     for code, name in _lib.STATUS_NAMES.items():
         assert L.mosaic_status_string(code).decode() == name
     assert L.mosaic_status_string(99).decode() == "MOSAIC_ERR_UNKNOWN"
@@ -240,3 +240,27 @@ def test_coarsen_validation():
     assert f(FAKE, 1, 64, 32, 6, FAKE, None) == SHAPE      # nside / 2^6 < 1
     assert f(FAKE, 1, 60, 32, 1, FAKE, None) == UNSUP      # channels not a multiple of 8
     assert _lib.lib().mosaic_last_error().decode() != ""
+
+
+def test_interp_validation():
+    L = _lib.lib()
+    f = L.mosaic_interp_attention
+
+    def call(k=FAKE, v=FAKE, w=FAKE, nbr=FAKE, rel=FAKE, s=2, n_src=1000, n_dst=500, K=16, d=64, dv=64,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return f(k, v, w, nbr, rel, s, n_src, n_dst, K, d, dv, out, ws, ws_bytes, None)
+    assert call(k=None) == NULL
+    assert call(rel=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(k=FAKE + 8) == MISAL
+    assert call(out=FAKE + 4) == MISAL
+    assert call(ws=FAKE + 128) == MISAL
+    assert call(s=0) == SHAPE
+    assert call(n_dst=0) == SHAPE
+    assert call(K=0) == UNSUP
+    assert call(K=17) == UNSUP
+    assert call(d=60) == UNSUP
+    assert call(dv=32) == UNSUP
+    assert call(ws_bytes=100) == WS
+    assert L.mosaic_interp_workspace_bytes(2, 1000) >= 2 * 1000 * 16
+    assert L.mosaic_interp_workspace_bytes(0, 1000) == 0
