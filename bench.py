@@ -378,7 +378,7 @@ def main() -> int:
             "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "mfma", "kernel": "bsa_fine (fine_kernel<64, WAVES, false>)",
+            "bound": "mfma", "kernel": "bsa_fine (fine_kernel<64, WAVES, kPlain>)",
             "achieved": r["fine_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": r["fine_tflops"] / PEAK_BF16_TFLOPS, "traffic": measured_traffic(f"fine_{c.name}"),
             "flops_per_launch": r["fine_flops"], "ms_per_launch": r["fine_ms"],
