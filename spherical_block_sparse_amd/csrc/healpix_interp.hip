@@ -15,7 +15,8 @@
 //     (index, relative position, kappa -> score); max and sum over the group
 //     by shuffles; then lane l accumulates output dims 4l .. 4l+3 over the
 //     neighbours, each neighbour's v row read by the 16 lanes as one
-//     contiguous 128-byte line, all 16 rows in flight at once.  Targets in NESTED order share most of
+//     contiguous 128-byte line, all 16 rows in flight at once and issued
+//     as soon as the indices are known.  Targets in NESTED order share most of
 //     their stencils, so the gathered rows hit in L2; the workgroup order is
 //     XCD-contiguous.  HBM-bound.
 #include "bsa_common.h"
@@ -75,10 +76,20 @@ __global__ __launch_bounds__(256) void interp_kernel(const float4* kappa, const 
   const int l = threadIdx.x % 16;
 
   int j = 0;
-  float score = -INFINITY;
   if (l < n_nbr) {
     j = nbr[(long long)i * n_nbr + l];
     j = j < 0 ? 0 : (j >= n_src ? n_src - 1 : j);
+  }
+  // the 16 value rows depend only on the indices: they are all issued before
+  // the scores are formed, so their latency overlaps the kappa gather (a
+  // lane past n_nbr has index 0 and, below, weight 0)
+  const uint16_t* vs = v + s * (long long)n_src * DV + 4 * l;
+  ushort4 rows[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) rows[jj] = *reinterpret_cast<const ushort4*>(vs + (long long)__shfl(j, jj, 16) * DV);
+
+  float score = -INFINITY;
+  if (l < n_nbr) {
     const float* p = rel + ((long long)i * n_nbr + l) * 3;
     const float4 kp = kappa[s * n_src + j];
     score = p[0] * kp.x + p[1] * kp.y + p[2] * kp.z;
@@ -92,25 +103,15 @@ __global__ __launch_bounds__(256) void interp_kernel(const float4* kappa, const 
   for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 16);
   const float pw = e / sum;
 
-  // all 16 rows are loaded before any is used (a lane past n_nbr has index 0
-  // and weight 0), so the group waits for one round of L2 latency, not 16
-  const uint16_t* vs = v + s * (long long)n_src * DV + 4 * l;
-  ushort4 rows[16];
-  float pjs[16];
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const int jn = __shfl(j, jj, 16);
-    pjs[jj] = __shfl(pw, jj, 16);
-    rows[jj] = *reinterpret_cast<const ushort4*>(vs + (long long)jn * DV);
-  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
+    const float pj = __shfl(pw, jj, 16);
     const ushort4 b = rows[jj];
-    acc.x = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.x << 16), acc.x);
-    acc.y = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.y << 16), acc.y);
-    acc.z = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.z << 16), acc.z);
-    acc.w = fmaf(pjs[jj], __builtin_bit_cast(float, (uint32_t)b.w << 16), acc.w);
+    acc.x = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.x << 16), acc.x);
+    acc.y = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.y << 16), acc.y);
+    acc.z = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.z << 16), acc.z);
+    acc.w = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.w << 16), acc.w);
   }
   *reinterpret_cast<float4*>(out + item * DV + 4 * l) = acc;
 }
