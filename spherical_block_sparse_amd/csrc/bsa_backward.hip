@@ -102,6 +102,9 @@ __device__ __forceinline__ bf16x8 global_operand(const uint16_t* base, long long
 
 __device__ const uint4 kZero16B = {0u, 0u, 0u, 0u};
 
+// x rounded to the nearest bf16 value (ties to even), as float
+__device__ __forceinline__ float bf16_round(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
+
 // Stage rows r0 .. r0+63 of a [N][D] bf16 tensor (rows >= r0+valid read as
 // zeros) into a swizzled LDS tile; each wave issues its share of the loads.
 template <int D>
@@ -350,17 +353,26 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
       for (int s = 0; s < 2; ++s) {
         const int t = tw + 16 * s + lr;
         const float inv_l = 1.f / st[s].l[0];
-        float dg = 0.f;
+        // dg = dO·o (the gate gradient) with dO in float32; D = g (dO_b·o)
+        // with the bf16 dO_b that dP = dO_b V^T uses, so that sum_u dS_u
+        // stays zero up to rounding (otherwise dO's rounding error, times
+        // the mean key, lands in every dQ)
+        float dg = 0.f, dgb = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const float4 d4 = *reinterpret_cast<const float4*>(dofs + (size_t)t * D + dt * 16 + 4 * lg);
           dg += d4.x * st[s].o[dt][0] + d4.y * st[s].o[dt][1] + d4.z * st[s].o[dt][2] + d4.w * st[s].o[dt][3];
+          dgb += bf16_round(d4.x) * st[s].o[dt][0] + bf16_round(d4.y) * st[s].o[dt][1] +
+                 bf16_round(d4.z) * st[s].o[dt][2] + bf16_round(d4.w) * st[s].o[dt][3];
         }
         dg *= inv_l;
         dg += __shfl_xor(dg, 16);
         dg += __shfl_xor(dg, 32);
+        dgb *= inv_l;
+        dgb += __shfl_xor(dgb, 16);
+        dgb += __shfl_xor(dgb, 32);
         lse[s] = st[s].m * c + log2f(st[s].l[0]);
-        dsub[s] = g[s] * dg;
+        dsub[s] = g[s] * dgb;
         if (lg == 0) {
           float* sp = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N + t;
           sp[0] = lse[s];
@@ -685,15 +697,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
     if (a.save_o) {   // dg_br = dO·o_br for the selected (0) and local (1) branches
 #pragma unroll
       for (int br = 0; br < 2; ++br) {
+        // e = dO·o_br for the gate gradient; eb = dO_b·o_br (bf16 dO, as dP
+        // uses it) for D, so that the logit gradients of a row sum to zero
         const float4 ob = *reinterpret_cast<const float4*>(a.save_o + (row * 2 + br) * D + 4 * c4);
         float e = d4.x * ob.x + d4.y * ob.y + d4.z * ob.z + d4.w * ob.w;
+        float eb = bf16_round(d4.x) * ob.x + bf16_round(d4.y) * ob.y + bf16_round(d4.z) * ob.z +
+                   bf16_round(d4.w) * ob.w;
 #pragma unroll
-        for (int sh = 1; sh < C4; sh <<= 1) e += __shfl_xor(e, sh);
+        for (int sh = 1; sh < C4; sh <<= 1) {
+          e += __shfl_xor(e, sh);
+          eb += __shfl_xor(eb, sh);
+        }
         if (c4 == 0) {
           const float gb = a.gates[row * 3 + 1 + br];
           float* sp = a.stats + ((size_t)br * a.slices + slice) * 3 * a.n_tok + t;
           sp[0] = a.save_lse[row * 2 + br];
-          sp[a.n_tok] = gb * e;
+          sp[a.n_tok] = gb * eb;
           sp[2 * (size_t)a.n_tok] = gb;
           a.dgates[row * 3 + 1 + br] = e;
         }
