@@ -42,8 +42,10 @@ constexpr int kGWaves = 4;
 
 __device__ const uint4 kZero16L = {0u, 0u, 0u, 0u};
 
-// 16-byte chunk swizzle of a 64-element (128-byte) row, period 16 rows
-__device__ __forceinline__ int gswz(int row) { return 2 * ((row >> 1) & 3) + ((row >> 3) & 1); }
+// 16-byte chunk swizzle of a 64-element (128-byte) row: the 8 lanes that one
+// LDS cycle serves read 8 consecutive rows at the same logical chunk, which
+// land on 8 different bank groups
+__device__ __forceinline__ int gswz(int row) { return row & 7; }
 
 // operand of rows 16*rt .. +15 of a staged [128][64] tile (two swizzled
 // [64][64] halves): lane lr + 16*lg holds row 16*rt + lr, k = 32*kk + 8*lg .. +7
@@ -53,15 +55,16 @@ __device__ __forceinline__ bf16x8 tile_operand(const uint16_t* buf, int rt, int 
   return *reinterpret_cast<const bf16x8*>(buf + row * kGK + 8 * ((4 * kk + lg) ^ gswz(row)));
 }
 
-// direct loads of rows r0 .. r0+127, k0 .. k0+63 of a [rows][K] bf16 matrix
-// into a staged tile; rows >= `rows` read as zeros.  Wave w issues 1 KB loads
-// w, w+4, w+8, w+12 (8 rows of 128 bytes each).
+// direct loads of rows r0 .. r0+NROWS-1, k0 .. k0+63 of a [rows][K] bf16
+// matrix into a staged tile; rows >= `rows` read as zeros.  Each 1 KB load
+// covers 8 rows of 128 bytes; wave w of WAVES issues loads w, w+WAVES, ...
+template <int NROWS = kGT, int WAVES = kGWaves>
 __device__ __forceinline__ void stage_bf16(uint16_t* buf, const uint16_t* base, long long r0, long long rows,
                                            int K, int k0, int w) {
   const int lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int grp = w + kGWaves * i;
+  for (int i = 0; i < NROWS / 8 / WAVES; ++i) {
+    const int grp = w + WAVES * i;
     const int row = 8 * grp + lane / 8;
     const int lc = (lane % 8) ^ gswz(row);
     const long long r = r0 + row;
@@ -91,6 +94,163 @@ struct GemmArgs {
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Epilogue of a wave's 64 x 64 tile: lane holds features
+// f = f0 + 64*wf + 16*ft + 4*lg + i of token m = m0 + 64*wm + 16*mt + lr;
+// the tile's first token is batch element bi0, position t0.
+template <bool OUT>
+__device__ __forceinline__ void epilogue(const GemmArgs p, const floatx4 (&acc)[4][4], long long m0, int f0,
+                                         long long bi0, int t0, int wm, int wf) {
+  const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
+  // the wave's 16-feature groups lie inside one head (head_dim is 32 or 64):
+  // which of q, k, v, the head and the first dimension of group ft
+  const int hd = p.heads * p.head_dim;
+  int g_which[4], g_head[4], g_j0[4];
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft) {
+    const int fg = __builtin_amdgcn_readfirstlane(f0 + 64 * wf + 16 * ft);
+    g_which[ft] = fg / hd;
+    g_head[ft] = (fg % hd) / p.head_dim;
+    g_j0[ft] = fg % p.head_dim;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int row = 64 * wm + 16 * mt + lr;
+    const long long m = m0 + row;
+    if (m >= p.M) continue;
+    int t = t0 + row;
+    long long bi = bi0;
+    while (t >= p.n_tok) {   // a tile spans at most three batch elements (N >= 192)
+      t -= p.n_tok;
+      bi += 1;
+    }
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft) {
+      const int f = f0 + 64 * wf + 16 * ft + 4 * lg;
+      if (f >= p.F) continue;
+      const floatx4 r = acc[ft][mt];
+      if constexpr (OUT) {
+        const ushort4 xr = *reinterpret_cast<const ushort4*>(p.x + m * p.F + f);
+        ushort4 o;
+        o.x = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.x << 16) + r[0]);
+        o.y = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.y << 16) + r[1]);
+        o.z = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.z << 16) + r[2]);
+        o.w = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.w << 16) + r[3]);
+        *reinterpret_cast<ushort4*>(p.y + m * p.F + f) = o;
+      } else {
+        if (g_which[ft] < 3) {   // four features of one head of one of q, k, v
+          const int which = g_which[ft], h = g_head[ft], j = g_j0[ft] + 4 * lg;
+          uint16_t* dst = which == 0 ? p.q : (which == 1 ? p.k : p.v);
+          ushort4 o;
+          o.x = bf16_rne(r[0]); o.y = bf16_rne(r[1]); o.z = bf16_rne(r[2]); o.w = bf16_rne(r[3]);
+          *reinterpret_cast<ushort4*>(dst + ((bi * p.heads + h) * (long long)p.n_tok + t) * p.head_dim + j) = o;
+        } else {            // gate logits: feature 3*hd + 3*h + branch
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int gi = f + i - 3 * hd;
+            if (gi >= 3 * p.heads) break;
+            const int h = gi / 3, br = gi % 3;
+            p.gates[((bi * p.heads + h) * (long long)p.n_tok + t) * 3 + br] =
+                __builtin_amdgcn_rcpf(1.f + __expf(-r[i]));
+          }
+        }
+      }
+    }
+  }
+}
+
+// Epilogue through LDS: the wave's 64 x 64 float32 tile goes to its own LDS
+// region (rows padded by 16 bytes against bank conflicts), then is read back
+// a token row at a time, so every global store writes whole 128-byte runs
+// (a head's 64 dims of q, k or v, or 64 channels of y) instead of 32-byte
+// pieces of four different lines.  Gate-logit features keep the direct path.
+template <bool OUT>
+__device__ __forceinline__ void epilogue_staged(const GemmArgs p, const floatx4 (&acc)[4][4], long long m0, int f0,
+                                                long long bi0, int t0, int wm, int wf, float* lds) {
+  const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
+  const int fw = f0 + 64 * wf;   // the wave's first feature, uniform
+  const int hd = p.heads * p.head_dim;
+  if (fw >= p.F) return;
+  if (!OUT && fw >= 3 * hd) {   // gate logits
+    epilogue<false>(p, acc, m0, f0, bi0, t0, wm, wf);
+    return;
+  }
+  constexpr int RS = 64 + 4;   // floats per staged row
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+      *reinterpret_cast<floatx4*>(lds + (16 * mt + lr) * RS + 16 * ft + 4 * lg) = acc[ft][mt];
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const int cl = lane % 16;             // 16-byte piece (4 features) of the row
+  const int fl = fw + 4 * cl;           // this lane's first feature
+  const bool f_ok = fl < p.F;
+  // the wave's first token: batch element bw, position tw (a tile spans at
+  // most two batch elements per wave: 64 rows, N >= 192)
+  const long long mw = m0 + 64 * wm;
+  long long bw = bi0;
+  int tw = t0 + 64 * wm;
+  if (tw >= p.n_tok) {
+    tw -= p.n_tok;
+    bw += 1;
+  }
+  // per-row global pointers: rows before the batch boundary, and after it
+  const uint16_t* xrow = nullptr;
+  uint16_t* row0 = nullptr;
+  uint16_t* row1 = nullptr;
+  int step = 0;
+  if constexpr (OUT) {
+    xrow = p.x + mw * p.F + fl;
+    row0 = p.y + mw * p.F + fl;
+    step = p.F;
+  } else {
+    const int which = fw / hd, h = (fl % hd) / p.head_dim, j = fl % p.head_dim;
+    uint16_t* dst = which == 0 ? p.q : (which == 1 ? p.k : p.v);
+    row0 = dst + ((bw * p.heads + h) * (long long)p.n_tok + tw) * p.head_dim + j;
+    row1 = dst + ((bw + 1) * p.heads + h) * (long long)p.n_tok * p.head_dim + j;
+    step = p.head_dim;
+  }
+  const int split = p.n_tok - tw;       // rows from here on belong to batch element bw + 1
+  const int r0 = lane / 16;             // first row of this lane; rows r0, r0 + 4, ...
+  const long long rows_left = p.M - mw; // rows of the wave that exist
+  if (OUT || split >= 64) {             // one batch element: pointers advance by 4 rows
+    const uint16_t* xp = xrow + (long long)r0 * step;
+    uint16_t* yp = row0 + (long long)r0 * step;
+    const long long adv = 4LL * step;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + r0;
+      if (row < rows_left && f_ok) {
+        const floatx4 r = *reinterpret_cast<const floatx4*>(lds + row * RS + 4 * cl);
+        ushort4 o;
+        if constexpr (OUT) {
+          const ushort4 xr = *reinterpret_cast<const ushort4*>(xp);
+          o.x = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.x << 16) + r[0]);
+          o.y = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.y << 16) + r[1]);
+          o.z = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.z << 16) + r[2]);
+          o.w = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.w << 16) + r[3]);
+        } else {
+          o.x = bf16_rne(r[0]); o.y = bf16_rne(r[1]); o.z = bf16_rne(r[2]); o.w = bf16_rne(r[3]);
+        }
+        *reinterpret_cast<ushort4*>(yp) = o;
+      }
+      if constexpr (OUT) xp += adv;
+      yp += adv;
+    }
+    return;
+  }
+  // a tile that crosses into the next batch element (q, k, v only)
+  for (int i = 0; i < 16; ++i) {
+    const int row = 4 * i + r0;
+    if (row >= rows_left || !f_ok) continue;
+    const floatx4 r = *reinterpret_cast<const floatx4*>(lds + row * RS + 4 * cl);
+    uint16_t* d = row < split ? row0 + (long long)row * step : row1 + (long long)(row - split) * step;
+    ushort4 o;
+    o.x = bf16_rne(r[0]); o.y = bf16_rne(r[1]); o.z = bf16_rne(r[2]); o.w = bf16_rne(r[3]);
+    *reinterpret_cast<ushort4*>(d) = o;
+  }
 }
 
 // OUT false: input projection (A = x via direct loads, head-split epilogue);
@@ -196,74 +356,134 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // epilogue: lane holds features f = f0 + 64*wf + 16*ft + 4*lg + i of token
-  // m = m0 + 64*wm + 16*mt + lr.
-  // the wave's 16-feature groups lie inside one head (head_dim is 32 or 64):
-  // which of q, k, v, the head and the first dimension of group ft
-  const int hd = p.heads * p.head_dim;
-  int g_which[4], g_head[4], g_j0[4];
+  epilogue<OUT>(p, acc, m0, f0, bi0, t0, wm, wf);
+}
+
+// Both operands bf16 (input projection, and the output projection inside the
+// layer): 256-token x 128-feature tiles, 8 waves in 4 x 2 (each 64 x 64, two
+// per SIMD, one workgroup per CU), three LDS stages (144 KB): chunk c+2 loads
+// while c is computed, so two chunks of loads are in flight per CU.  With
+// K = 512 a tile is only 8 chunks long, and the doubled tile and deeper
+// pipeline keep the matrix cores fed where the 128 x 128, two-stage tile
+// waits on its loads.
+constexpr int kBT = 256;
+constexpr int kBWaves = 8;
+
+template <bool OUT>
+__global__ __launch_bounds__(64 * kBWaves) void layer_gemm_big_kernel(GemmArgs p) {
+  // three A stages (256 x 64) then three B stages (128 x 64), one array so
+  // that the epilogue can reuse all of it
+  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * kBT * kGK + 3 * kGT * kGK];
+  auto As = [&](int st) __attribute__((always_inline)) { return smem + st * kBT * kGK; };
+  auto Bs = [&](int st) __attribute__((always_inline)) { return smem + 3 * kBT * kGK + st * kGT * kGK; };
+  const long long tiles = (long long)p.m_tiles * p.f_tiles;
+  long long logical;
+  {
+    const long long b = blockIdx.x, q8 = tiles / 8, r8 = tiles % 8, xcd = b % 8, kq = b / 8;
+    logical = xcd < r8 ? xcd * (q8 + 1) + kq : r8 * (q8 + 1) + (xcd - r8) * q8 + kq;
+  }
+  const long long m0 = (logical / p.f_tiles) * kBT;
+  const int f0 = (int)(logical % p.f_tiles) * kGT;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = w & 3, wf = w >> 2;   // the wave's 64-token and 64-feature part
+  const int nk = p.K / kGK;
+  const long long bi0 = m0 / p.n_tok;
+  const int t0 = (int)(m0 - bi0 * p.n_tok);
+  // loads per wave and chunk: (256 + 128) rows / 8 rows per load / 8 waves
+  constexpr int kLoadsA = kBT / 8 / kBWaves, kLoadsB = kGT / 8 / kBWaves;
+  constexpr int kLoads = kLoadsA + kLoadsB;
+  // per-lane source pointers of the wave's loads, formed once: load i covers
+  // rows 8*(w + 8i) .. +7, the lane one 16-byte piece of one row.  Rows past
+  // the matrix are clamped to its last row: they only feed accumulator rows
+  // or columns that the epilogue never stores.  A chunk then only adds its
+  // k offset.
+  const int lane = threadIdx.x % kWave;
+  const uint16_t* srcA[kLoadsA];
+  const uint16_t* srcB[kLoadsB];
 #pragma unroll
-  for (int ft = 0; ft < 4; ++ft) {
-    const int fg = __builtin_amdgcn_readfirstlane(f0 + 64 * wf + 16 * ft);
-    g_which[ft] = fg / hd;
-    g_head[ft] = (fg % hd) / p.head_dim;
-    g_j0[ft] = fg % p.head_dim;
+  for (int i = 0; i < kLoadsA; ++i) {
+    const int row = 8 * (w + kBWaves * i) + lane / 8;
+    const long long r = m0 + row < p.M ? m0 + row : p.M - 1;
+    srcA[i] = p.a + r * p.K + 8 * ((lane % 8) ^ gswz(row));
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = 64 * wm + 16 * mt + lr;
-    const long long m = m0 + row;
-    if (m >= p.M) continue;
-    int t = t0 + row;
-    long long bi = bi0;
-    if (t >= p.n_tok) {
-      t -= p.n_tok;
-      bi += 1;
-    }
+  for (int i = 0; i < kLoadsB; ++i) {
+    const int row = 8 * (w + kBWaves * i) + lane / 8;
+    const long long r = f0 + row < p.F ? f0 + row : p.F - 1;
+    srcB[i] = p.b + r * p.K + 8 * ((lane % 8) ^ gswz(row));
+  }
+  const int lds_wave = lds_addr(smem) + w * 1024;   // the wave's first 1 KB slot
+  auto stage = [&](int c, int s) __attribute__((always_inline)) {
+    const int k0 = c * kGK;
+    const int a_base = __builtin_amdgcn_readfirstlane(lds_wave + s * (kBT * kGK * 2));
+    const int b_base = __builtin_amdgcn_readfirstlane(lds_wave + 3 * (kBT * kGK * 2) + s * (kGT * kGK * 2));
+    static_for<0, kLoadsA>([&](auto i) __attribute__((always_inline)) {
+      dma_global_at<decltype(i)::value * kBWaves * 1024>(a_base, srcA[decltype(i)::value] + k0);
+    });
+    static_for<0, kLoadsB>([&](auto i) __attribute__((always_inline)) {
+      dma_global_at<decltype(i)::value * kBWaves * 1024>(b_base, srcB[decltype(i)::value] + k0);
+    });
+  };
+  floatx4 acc[4][4];
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft) {
-      const int f = f0 + 64 * wf + 16 * ft + 4 * lg;
-      if (f >= p.F) continue;
-      const floatx4 r = acc[ft][mt];
-      if constexpr (OUT) {
-        const ushort4 xr = *reinterpret_cast<const ushort4*>(p.x + m * p.F + f);
-        ushort4 o;
-        o.x = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.x << 16) + r[0]);
-        o.y = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.y << 16) + r[1]);
-        o.z = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.z << 16) + r[2]);
-        o.w = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.w << 16) + r[3]);
-        *reinterpret_cast<ushort4*>(p.y + m * p.F + f) = o;
-      } else {
-        if (g_which[ft] < 3) {   // four features of one head of one of q, k, v
-          const int which = g_which[ft], h = g_head[ft], j = g_j0[ft] + 4 * lg;
-          uint16_t* dst = which == 0 ? p.q : (which == 1 ? p.k : p.v);
-          ushort4 o;
-          o.x = bf16_rne(r[0]); o.y = bf16_rne(r[1]); o.z = bf16_rne(r[2]); o.w = bf16_rne(r[3]);
-          *reinterpret_cast<ushort4*>(dst + ((bi * p.heads + h) * (long long)p.n_tok + t) * p.head_dim + j) = o;
-        } else {            // gate logits: feature 3*hd + 3*h + branch
+  for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int gi = f + i - 3 * hd;
-            if (gi >= 3 * p.heads) break;
-            const int h = gi / 3, br = gi % 3;
-            p.gates[((bi * p.heads + h) * (long long)p.n_tok + t) * 3 + br] = 1.f / (1.f + __expf(-r[i]));
-          }
-        }
+    for (int mt = 0; mt < 4; ++mt) acc[ft][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  stage(0, 0);
+  if (nk > 1) {
+    stage(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);   // chunk 0 has landed (loads complete in order)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+  __syncthreads();
+  int s = 0;
+  for (int c = 0; c < nk; ++c) {
+    // buffer (c+2)%3 was last read in chunk c-1, before the barrier that ended it
+    if (c + 2 < nk) stage(c + 2, s == 0 ? 2 : s - 1);
+    const uint16_t* a_t = As(s) + wm * 64 * kGK;
+    const uint16_t* b_t = Bs(s) + wf * 64 * kGK;
+#pragma unroll
+    for (int kk = 0; kk < kGK / 32; ++kk) {
+      bf16x8 bo[4], ao[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bo[t] = tile_operand(b_t, t, kk);
+        ao[t] = tile_operand(a_t, t, kk);
       }
+#pragma unroll
+      for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[ft][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo[ft], ao[mt], acc[ft][mt], 0, 0, 0);
     }
+    if (c + 2 < nk)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);   // chunk c+1 has landed, c+2 may be in flight
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    s = s == 2 ? 0 : s + 1;
   }
+  // the staging buffers are free (every wave passed the last barrier): each
+  // wave takes a 64 x 68 float region of them (8 x 17 KB of the 144 KB)
+  epilogue_staged<OUT>(p, acc, m0, f0, bi0, t0, wm, wf, reinterpret_cast<float*>(smem) + w * 64 * (64 + 4));
 }
 
 hipError_t launch_gemm(GemmArgs p, bool out, bool a32, hipStream_t stream) {
-  p.m_tiles = (int)((p.M + kGT - 1) / kGT);
   p.f_tiles = (p.F + kGT - 1) / kGT;
-  const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
-  if (!out)
-    hipLaunchKernelGGL((layer_gemm_kernel<false, false>), grid, dim3(64 * kGWaves), 0, stream, p);
-  else if (a32)
+  if (a32) {
+    p.m_tiles = (int)((p.M + kGT - 1) / kGT);
+    const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
     hipLaunchKernelGGL((layer_gemm_kernel<true, true>), grid, dim3(64 * kGWaves), 0, stream, p);
+    return hipGetLastError();
+  }
+  p.m_tiles = (int)((p.M + kBT - 1) / kBT);
+  const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
+  if (out)
+    hipLaunchKernelGGL(layer_gemm_big_kernel<true>, grid, dim3(64 * kBWaves), 0, stream, p);
   else
-    hipLaunchKernelGGL((layer_gemm_kernel<true, false>), grid, dim3(64 * kGWaves), 0, stream, p);
+    hipLaunchKernelGGL(layer_gemm_big_kernel<false>, grid, dim3(64 * kBWaves), 0, stream, p);
   return hipGetLastError();
 }
 

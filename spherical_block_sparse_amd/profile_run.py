@@ -3,7 +3,8 @@
     python -m spherical_block_sparse_amd.profile_run --config ns128 --stage fine --reps 2
     python -m spherical_block_sparse_amd.profile_run --copy-mib 4096 --reps 2
 
---stage pool | select | fine | forward | train runs that entry point
+--stage pool | select | fine | forward | train | layer_in | layer runs that
+entry point (the layer stages with 512 channels)
 `reps` times on the workload's synthetic inputs (the earlier stages run once
 beforehand to produce their inputs); --stage backward runs the training
 forward once and then the backward from its saved state `reps` times, with
@@ -27,7 +28,8 @@ from . import _lib
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="ns128", choices=sorted(CONFIGS))
-    ap.add_argument("--stage", default="fine", choices=["pool", "select", "fine", "forward", "train", "backward"])
+    ap.add_argument("--stage", default="fine",
+                    choices=["pool", "select", "fine", "forward", "train", "backward", "layer_in", "layer"])
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--copy-mib", type=int, default=0)
     ap.add_argument("--order", default="nested", choices=["nested", "ring"],
@@ -45,6 +47,18 @@ def main() -> int:
         return 0
 
     cfg = CONFIGS[args.config]
+    if args.stage in ("layer_in", "layer"):   # the encoder layer of 512 channels on the workload's mesh
+        from . import make_layer_inputs
+        x, w_in, w_out = make_layer_inputs(cfg, 512, device="cuda")
+        for _ in range(args.reps):
+            if args.stage == "layer_in":
+                _lib.mosaic_bsa_layer_in(x, w_in[0], cfg.heads, cfg.head_dim, cfg.nside)
+            else:
+                _lib.mosaic_bsa_layer_forward(x, w_in[0], w_out[0], cfg.heads, cfg.head_dim, cfg.nside, cfg.block,
+                                              cfg.topn, cfg.window)
+        torch.cuda.synchronize()
+        print(f"{args.stage} {cfg.name} x {args.reps} done", flush=True)
+        return 0
     q, k, v, g = make_inputs(cfg, device="cuda", dtype=torch.bfloat16)
     if args.order == "ring":
         from .locality_study import permute_tokens
