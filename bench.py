@@ -141,11 +141,13 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
     kbar = torch.empty_like(qbar)
     vbar = torch.empty((b, h, m, d), dtype=torch.float32, device=dev)
     o_cg = torch.empty_like(vbar)
+    knorm = torch.empty((b, h, m), dtype=torch.float32, device=dev)
     sel2 = torch.empty_like(sel)
     out2 = torch.empty_like(out)
-    pool = lambda: _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar)
+    pool = lambda: _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar, knorm=knorm)
     cs = lambda: _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel2)
-    fine = lambda: _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel2, cfg.nside, cfg.block, cfg.topn, cfg.window, out2)
+    fine = lambda: _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel2, cfg.nside, cfg.block, cfg.topn, cfg.window, out2,
+                                        knorm=knorm)
     pool(); cs(); fine()
     kt = max(3, steps // 2)
     pool_ms = time_stream(pool, kt)

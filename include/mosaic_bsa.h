@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 5
+#define MOSAIC_BSA_ABI_VERSION 6
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -73,8 +73,9 @@ const char* mosaic_status_string(int status);
 const char* mosaic_last_error(void);
 
 /* Bytes of device workspace mosaic_bsa_forward needs: pooled q̄, k̄ (float64),
- * pooled v̄ and o_CG (float32), each [batch][heads][m][head_dim], 256-byte
- * aligned sections.  Returns 0 if the shape is invalid or unsupported. */
+ * pooled v̄ and o_CG (float32), each [batch][heads][m][head_dim], then the
+ * largest key norm of each block (float32 [batch][heads][m]), 256-byte aligned
+ * sections.  Returns 0 if the shape is invalid or unsupported. */
 size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn);
 
 /* The whole BSA forward pass (pool -> compressed + selection -> selected and
@@ -93,10 +94,12 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
 /* Pooling only: q̄, k̄ (float64) and v̄ (float32), [batch][heads][m][head_dim],
  * the mean of each block's `block` consecutive NESTED tokens (the block
  * summaries of the BSA item; the mean is this library's reading of the
- * unspecified pooling). */
+ * unspecified pooling).  knorm (may be NULL): float32 [batch][heads][m], the
+ * largest key norm max_t |k_t| of each block (float32 sums of squares); not
+ * part of the method, it lets mosaic_bsa_fine bound scores in advance. */
 mosaic_status mosaic_bsa_pool(const void* q, const void* k, const void* v, int batch, int heads,
                               int head_dim, int nside, int block, double* qbar, double* kbar,
-                              float* vbar, void* stream);
+                              float* vbar, float* knorm, void* stream);
 
 /* Compressed branch and top-n selection from pooled tensors: o_cg
  * [batch][heads][m][head_dim] float32 = sum_j softmax_j(q̄_i·k̄_j/sqrt(d)) v̄_j,
@@ -113,11 +116,16 @@ mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar,
  * valid block indices per row, each in [0, m); order is irrelevant):
  * out = g_CG·o_cg[t/block] + g_FG·o_FG + g_L·o_L.  bf16 products with
  * float32 accumulation; attention weights are rounded to bf16 before they
- * multiply v. */
+ * multiply v.  knorm (may be NULL): mosaic_bsa_pool's largest key norm per
+ * block.  With it, queries whose scores it bounds closely enough use the
+ * bound c·|q|·knorm as the fixed softmax reference in place of a running
+ * maximum (the same softmax up to rounding).  A knorm that understates a
+ * norm by a factor f lets weights grow to 2^((f-1)·bound): pass the pool's
+ * own output. */
 mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const float* gates,
-                              const float* o_cg, const int32_t* sel_idx, int batch, int heads,
-                              int head_dim, int nside, int block, int topn, int window, float* out,
-                              void* stream);
+                              const float* o_cg, const int32_t* sel_idx, const float* knorm, int batch,
+                              int heads, int head_dim, int nside, int block, int topn, int window,
+                              float* out, void* stream);
 
 /* ---- HEALPix coarsening ---------------------------------------------------
  * A field on the NESTED pixels at nside taken to nside / 2^levels
@@ -198,7 +206,7 @@ mosaic_status mosaic_bsa_layer_out(const float* attn, const void* w_out, const v
  * sections): float32 o_FG_t, o_L_t [batch][heads][N][2][head_dim] (each
  * normalised), float32 [batch][heads][N][2] their base-2 log-sum-exp of
  * q_t·k_u·log2(e)/sqrt(d), then the forward workspace of
- * mosaic_bsa_workspace_bytes (q̄, k̄, v̄, o_CG). */
+ * mosaic_bsa_workspace_bytes (q̄, k̄, v̄, o_CG, largest key norm per block). */
 size_t mosaic_bsa_saved_bytes(int batch, int heads, int head_dim, int nside, int block);
 
 /* mosaic_bsa_forward for training: the same sel_idx and out (up to float32

@@ -63,11 +63,11 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_forward.restype = I
         L.mosaic_bsa_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, P, S, P]
         L.mosaic_bsa_pool.restype = I
-        L.mosaic_bsa_pool.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P]
+        L.mosaic_bsa_pool.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P]
         L.mosaic_bsa_compress_select.restype = I
         L.mosaic_bsa_compress_select.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
         L.mosaic_bsa_fine.restype = I
-        L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+        L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
         L.mosaic_bsa_backward_workspace_bytes.restype = S
         L.mosaic_bsa_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.mosaic_interp_workspace_bytes.restype = S
@@ -169,8 +169,9 @@ def mosaic_bsa_forward(q, k, v, gates, nside, block, topn, window, out=None, sel
     return out, sel_idx
 
 
-def mosaic_bsa_pool(q, k, v, nside, block, qbar=None, kbar=None, vbar=None, stream=None):
-    """q̄, k̄ (float64) and v̄ (float32), [b,H,m,d]: block means."""
+def mosaic_bsa_pool(q, k, v, nside, block, qbar=None, kbar=None, vbar=None, knorm=None, stream=None):
+    """q̄, k̄ (float64) and v̄ (float32), [b,H,m,d]: block means.  knorm, if given (float32
+    [b,H,m]), receives each block's largest key norm."""
     b, h, n, d = _dims(q, nside)
     m = n // block
     qbar = torch.empty((b, h, m, d), dtype=torch.float64, device=q.device) if qbar is None else qbar
@@ -180,7 +181,8 @@ def mosaic_bsa_pool(q, k, v, nside, block, qbar=None, kbar=None, vbar=None, stre
         _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
         _ptr(v, torch.bfloat16, (b, h, n, d), "v"), b, h, d, nside, block,
         _ptr(qbar, torch.float64, (b, h, m, d), "qbar"), _ptr(kbar, torch.float64, (b, h, m, d), "kbar"),
-        _ptr(vbar, torch.float32, (b, h, m, d), "vbar"), _stream(stream)))
+        _ptr(vbar, torch.float32, (b, h, m, d), "vbar"),
+        None if knorm is None else _ptr(knorm, torch.float32, (b, h, m), "knorm"), _stream(stream)))
     return qbar, kbar, vbar
 
 
@@ -199,8 +201,10 @@ def mosaic_bsa_compress_select(qbar, kbar, vbar, nside, block, topn, o_cg=None, 
     return o_cg, sel_idx
 
 
-def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, out=None, stream=None):
-    """out [b,H,N,d] fp32: gated sum of o_cg with the selected and local fine branches."""
+def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, out=None, knorm=None,
+                    stream=None):
+    """out [b,H,N,d] fp32: gated sum of o_cg with the selected and local fine branches.  knorm: the
+    pool's largest key norm per block (float32 [b,H,m]), or None for the running-maximum softmax."""
     b, h, n, d = _dims(q, nside)
     m = n // block
     out = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device) if out is None else out
@@ -208,6 +212,7 @@ def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, o
         _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
         _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
         _ptr(o_cg, torch.float32, (b, h, m, d), "o_cg"), _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"),
+        None if knorm is None else _ptr(knorm, torch.float32, (b, h, m), "knorm"),
         b, h, d, nside, block, topn, window, _ptr(out, torch.float32, (b, h, n, d), "out"), _stream(stream)))
     return out
 

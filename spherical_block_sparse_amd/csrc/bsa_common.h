@@ -123,14 +123,17 @@ __device__ __forceinline__ int32x4 slice_rsrc(const void* base, int bytes) {
 }
 
 
+// knorm non-null: also write the largest key norm max_t |k_t| of each block, float32 [slices][m]
 hipError_t launch_pool(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* qbar,
                        double* kbar, float* vbar, long long slices, int n_tok, int head_dim,
-                       int block, hipStream_t stream);
+                       int block, hipStream_t stream, float* knorm = nullptr);
 
 hipError_t launch_compress_select(const double* qbar, const double* kbar, const float* vbar,
                                   float* o_cg, int32_t* sel, long long slices, int m, int head_dim,
                                   int topn, hipStream_t stream);
 
+// knorm non-null (the pool's largest key norm per block): waves whose scores
+// it bounds tightly enough skip the running maximum of the online softmax.
 // save_o / save_lse non-null: also write each query's normalised selected and
 // local branch outputs (float32 [S][N][2][D]) and their log2-sum-exp
 // ([S][N][2]).  out_merged non-null (with `heads`, S = batch*heads): write
@@ -138,8 +141,8 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
 hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gates,
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
-                       hipStream_t stream, float* save_o = nullptr, float* save_lse = nullptr,
-                       uint16_t* out_merged = nullptr, int heads = 1);
+                       hipStream_t stream, const float* knorm = nullptr, float* save_o = nullptr,
+                       float* save_lse = nullptr, uint16_t* out_merged = nullptr, int heads = 1);
 
 // Everything the backward launches read and write (device pointers; the
 // workspace buffers are carved by the C-ABI entry point).

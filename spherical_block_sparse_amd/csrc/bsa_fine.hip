@@ -31,7 +31,11 @@
 //     32*jj + 16*h + 4*g + r/4, column 16*dt + 4*(r%4).
 //   * softmax in base 2 with log2(e)/sqrt(d) folded into the scores; the
 //     running reference max only moves when a score exceeds it by more than
-//     2^8 (weights stay <= 256), so O is rescaled on few chunks; the
+//     2^8 (weights stay <= 256), so O is rescaled on few chunks.  Given the
+//     pool's largest key norm per key block, a query's scores over a
+//     branch's blocks are bounded by c*|q|*max|k|; when those bounds are small
+//     enough for every query of a wave, the bounds serve as fixed
+//     references and the running maximum is skipped altogether.  The
 //     denominator is the same MFMA with an all-ones A operand (sum of the
 //     rounded weights, so each output is an exact convex combination of the
 //     weights actually applied).
@@ -66,6 +70,7 @@ struct FineArgs {
   const float* gates;
   const float* o_cg;
   const int32_t* sel;
+  const float* knorm; // largest key norm of each key block [S][m], or null
   float* out;
   float* save_o;      // [S][N][2][D] o_FG, o_L (normalised), SAVE only
   float* save_lse;    // [S][N][2] their log2-sum-exp (log2 units of S*log2(e)/sqrt(d)), SAVE only
@@ -86,6 +91,11 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 
 constexpr float kLazy = 8.0f;
+// Largest score bound M (log2 units) for which the running maximum is
+// skipped.  The best key's weight is then at least 2^-2M = 2^-96: it, the
+// denominator and its products with v elements above 2^-30 stay normal
+// float32 and bf16 numbers, 30 binades above the smallest.
+constexpr float kBoundMax = 48.0f;
 
 
 // transposing 8-byte LDS read (ds_read_b64_tr_b16)
@@ -188,35 +198,39 @@ __device__ __forceinline__ void qk_chunk(const uint16_t* Ks, const bf16x8 (&qf)[
 // query's reference and the wave votes, so the common case needs no
 // exchange between lanes; only when some score grew does the wave form the
 // queries' maxima across their four lanes and rescale (a scalar branch; any
-// query may move its reference: alpha <= 1 is always exact).
-template <int D, bool ALL>
+// query may move its reference: alpha <= 1 is always exact).  A bounded
+// wave's references are fixed upper bounds of its scores, so it skips all
+// of this.
+template <int D, bool ALL, bool BOUNDED>
 __device__ __forceinline__ void softmax_chunk(floatx4 (&acc)[2][4], Branch<D> (&br)[2], bf16x8 (&pb)[2][2],
                                               const bool (&act)[2], float c, float lazy_raw) {
   constexpr int DT = Tile<D>::DT;
-  float mx[2];   // this lane's maximum of each sub-tile's scores
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float a = fmaxf(acc[s][0][0], acc[s][0][1]);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = (kt == 0 ? 2 : 0); i < 4; i += 2) a = fmaxf(a, fmaxf(acc[s][kt][i], acc[s][kt][i + 1]));
-    mx[s] = a;
-  }
-  const bool grow = (ALL || act[0]) && mx[0] > br[0].m + lazy_raw;
-  const bool grow1 = (ALL || act[1]) && mx[1] > br[1].m + lazy_raw;
-  if (__ballot(grow || grow1)) {
+  if constexpr (!BOUNDED) {   // bounded references never move
+    float mx[2];   // this lane's maximum of each sub-tile's scores
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (!(ALL || act[s])) continue;
-      float row = fmaxf(mx[s], __shfl_xor(mx[s], 16));
-      row = fmaxf(row, __shfl_xor(row, 32));
-      const float mnew = fmaxf(br[s].m, row);
-      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((br[s].m - mnew) * c);
-      br[s].m = mnew;
-      br[s].l *= alpha;
+      float a = fmaxf(acc[s][0][0], acc[s][0][1]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) br[s].o[dt] *= alpha;
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = (kt == 0 ? 2 : 0); i < 4; i += 2) a = fmaxf(a, fmaxf(acc[s][kt][i], acc[s][kt][i + 1]));
+      mx[s] = a;
+    }
+    const bool grow = (ALL || act[0]) && mx[0] > br[0].m + lazy_raw;
+    const bool grow1 = (ALL || act[1]) && mx[1] > br[1].m + lazy_raw;
+    if (__ballot(grow || grow1)) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (!(ALL || act[s])) continue;
+        float row = fmaxf(mx[s], __shfl_xor(mx[s], 16));
+        row = fmaxf(row, __shfl_xor(row, 32));
+        const float mnew = fmaxf(br[s].m, row);
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((br[s].m - mnew) * c);
+        br[s].m = mnew;
+        br[s].l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) br[s].o[dt] *= alpha;
+      }
     }
   }
 #pragma unroll
@@ -235,7 +249,7 @@ __device__ __forceinline__ void softmax_chunk(floatx4 (&acc)[2][4], Branch<D> (&
 // case).  With MASK, chunk key kappa is valid for this lane's query of
 // sub-tile s iff lo[s] <= kappa < lo[s] + span[s] (span >= 0); otherwise
 // every key is valid.
-template <int D, bool MASK>
+template <int D, bool MASK, bool BOUNDED>
 __device__ __forceinline__ void attend_full(const uint16_t* Ks, const uint16_t* Vs,
                                             const bf16x8 (&qf)[2][Tile<D>::KK], Branch<D> (&br)[2],
                                             float c, float lazy_raw, const int (&lo)[2], const int (&span)[2]) {
@@ -253,13 +267,13 @@ __device__ __forceinline__ void attend_full(const uint16_t* Ks, const uint16_t* 
         for (int i = 0; i < 4; ++i)
           if ((unsigned)(16 * kt + 4 * lg + i - lo[s]) >= (unsigned)span[s]) acc[s][kt][i] = -INFINITY;
   }
-  softmax_chunk<D, true>(acc, br, pb, act, c, lazy_raw);
+  softmax_chunk<D, true, BOUNDED>(acc, br, pb, act, c, lazy_raw);
   pv_chunk<D, true>(Vs, pb, br, act);
 }
 
 // One staged 64-key chunk in general form: act[s] says whether sub-tile s
 // takes part, msk[s] whether its scores need valid(s, kappa).
-template <int D, typename V>
+template <int D, bool BOUNDED, typename V>
 __device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t* Vs,
                                              const bf16x8 (&qf)[2][Tile<D>::KK], Branch<D> (&br)[2],
                                              const bool (&act)[2], const bool (&msk)[2], float c,
@@ -278,7 +292,7 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* Ks, const uint16_t*
         for (int i = 0; i < 4; ++i)
           if (!valid(s, 16 * kt + 4 * lg + i)) acc[s][kt][i] = -INFINITY;
     }
-  softmax_chunk<D, false>(acc, br, pb, act, c, lazy_raw);
+  softmax_chunk<D, false, BOUNDED>(acc, br, pb, act, c, lazy_raw);
   pv_chunk<D, false>(Vs, pb, br, act);
 }
 
@@ -366,6 +380,45 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     __syncthreads();
   }
 
+  // Score bounds from the largest key norm of each key block: a query's
+  // scaled scores over a set of blocks lie within +-M, M = c*|q|*max|k|
+  // (Cauchy-Schwarz).  When every such bound of the wave's queries is at
+  // most kBoundMax, each branch's reference is its bound from the start:
+  // weights stay at or below about 1, the best one at or above 2^-2M, and
+  // no running maximum or rescaling is needed.  Otherwise the lazy running
+  // maximum is used.
+  float m_sel[2] = {0.f, 0.f}, m_loc[2] = {0.f, 0.f};
+  bool bounded = false;
+  if (a.knorm) {
+    const float* kn = a.knorm + (size_t)slice * m;
+    bool ok = true;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float q2 = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = static_cast<float>(qf[s][kk][e]);
+          q2 = fmaf(x, x, q2);
+        }
+      q2 += __shfl_xor(q2, 16);
+      q2 += __shfl_xor(q2, 32);
+      const float qn = sqrtf(q2);
+      const int ts = tw + 16 * s;   // the sub-tile's query range is uniform
+      float ks = 0.f, kl = 0.f;
+      for (int gi = (ts >> lb) - blk0; gi <= ((ts + 15) >> lb) - blk0; ++gi)
+        for (int j = 0; j < n; ++j) ks = fmaxf(ks, kn[SelT[gi * n + j]]);
+      const int ulo = max(0, ts - lo_off);
+      const int uhi = (int)min((long long)N, (long long)ts + 15 + hi_off);
+      for (int bl = ulo >> lb; bl <= (uhi - 1) >> lb; ++bl) kl = fmaxf(kl, kn[bl]);
+      m_sel[s] = c * qn * ks;
+      m_loc[s] = c * qn * kl;
+      ok = ok && m_sel[s] <= kBoundMax && m_loc[s] <= kBoundMax;
+    }
+    bounded = !__ballot(!ok);
+  }
+
   auto token_of = [&](int ci, int kappa) __attribute__((always_inline)) -> int {
     if (ci < c_sel) {
       const int gi = ci / cpg;
@@ -451,7 +504,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
 
   Branch<D> br[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) branch_init(br[s]);
+  for (int s = 0; s < 2; ++s) {
+    branch_init(br[s]);
+    if (bounded) br[s].m = m_sel[s] / c;
+  }
   float4 pre[2][DT];   // g_CG*o_CG + g_FG*o_FG, formed when the selected branch ends
 
   // SAVE: the branch's normalised output and log2-sum-exp m*c + log2(l) of
@@ -489,9 +545,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   };
 
   const float lazy_raw = kLazy / c;
-  auto step_selected = [&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
+  // BND (std::true_type or std::false_type): whether the wave's references
+  // are its score bounds; the chunk code is compiled for each case
+  auto step_selected = [&](int ci, const uint16_t* kb, const uint16_t* vb, auto BND) __attribute__((always_inline)) {
+    constexpr bool bnd = decltype(BND)::value;
     if (B >= T && nB - ci * 64 >= 64) {   // one group: chunk ci starts at virtual key 64*ci
-      attend_full<D, false>(kb, vb, qf, br, c, lazy_raw, kNoRange, kNoRange);
+      attend_full<D, false, bnd>(kb, vb, qf, br, c, lazy_raw, kNoRange, kNoRange);
       return;
     }
     const int gi = groups == 1 ? 0 : ci / cpg;
@@ -502,9 +561,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       act[s] = B >= T || (tw + 16 * s) / B == blk0 + gi;
       msk[s] = nB - vc0 < 64;
     }
-    attend_chunk<D>(kb, vb, qf, br, act, msk, c, lazy_raw, [&](int, int kappa) { return vc0 + kappa < nB; });
+    attend_chunk<D, bnd>(kb, vb, qf, br, act, msk, c, lazy_raw, [&](int, int kappa) { return vc0 + kappa < nB; });
   };
-  auto step_local = [&](int ci, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
+  auto step_local = [&](int ci, const uint16_t* kb, const uint16_t* vb, auto BND) __attribute__((always_inline)) {
+    constexpr bool bnd = decltype(BND)::value;
     const int u0 = wlo + (ci - c_sel) * 64;
     bool act[2], msk[2];
 #pragma unroll
@@ -518,7 +578,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       msk[s] = !(u0 >= ilo && u0 + 64 <= ihi);
     }
     if (act[0] && act[1] && !msk[0] && !msk[1]) {
-      attend_full<D, false>(kb, vb, qf, br, c, lazy_raw, kNoRange, kNoRange);
+      attend_full<D, false, bnd>(kb, vb, qf, br, c, lazy_raw, kNoRange, kNoRange);
       return;
     }
     if (act[0] && act[1]) {   // edge of the windows: this lane's query keeps [lo, lo + span)
@@ -529,10 +589,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         lo[s] = t - lo_off - u0;
         span[s] = max(0, (int)min((long long)N, (long long)t + hi_off) - u0 - lo[s]);
       }
-      attend_full<D, true>(kb, vb, qf, br, c, lazy_raw, lo, span);
+      attend_full<D, true, bnd>(kb, vb, qf, br, c, lazy_raw, lo, span);
       return;
     }
-    attend_chunk<D>(kb, vb, qf, br, act, msk, c, lazy_raw, [&](int s, int kappa) {
+    attend_chunk<D, bnd>(kb, vb, qf, br, act, msk, c, lazy_raw, [&](int s, int kappa) {
       const int u = u0 + kappa, t = tw + 16 * s + lr;
       return u >= t - lo_off && u < t + hi_off && u < N;
     });
@@ -540,26 +600,36 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // Chunks [c0, c1) double-buffered: the loads of chunk ci+1 run while chunk
   // ci is computed; each barrier follows the wave's wait for its own loads.
-  auto run = [&](int c0, int c1, auto step) __attribute__((always_inline)) {
+  auto run = [&](int c0, int c1, auto step, auto BND) __attribute__((always_inline)) {
     if (c0 >= c1) return;
     issue(c0, P0);
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     for (int ci = c0; ci < c1; ci += 2) {
       if (ci + 1 < c1) issue(ci + 1, P1);
-      step(ci, Kb0, Vb0);
+      step(ci, Kb0, Vb0, BND);
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       __syncthreads();
       if (ci + 1 >= c1) break;
       if (ci + 2 < c1) issue(ci + 2, P0);
-      step(ci + 1, Kb1, Vb1);
+      step(ci + 1, Kb1, Vb1, BND);
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       __syncthreads();
     }
   };
-  run(0, c_sel, step_selected);
-  finish_selected();
-  run(c_sel, c_all, step_local);
+  auto branches = [&](auto BND) __attribute__((always_inline)) {
+    run(0, c_sel, step_selected, BND);
+    finish_selected();
+    if constexpr (decltype(BND)::value) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) br[s].m = m_loc[s] / c;
+    }
+    run(c_sel, c_all, step_local, BND);
+  };
+  if (bounded)
+    branches(std::true_type{});
+  else
+    branches(std::false_type{});
 
   // gated sum: pre + g_L * o_L
 #pragma unroll
@@ -615,7 +685,8 @@ hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
 hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gates,
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
-                       hipStream_t stream, float* save_o, float* save_lse, uint16_t* out_merged, int heads) {
+                       hipStream_t stream, const float* knorm, float* save_o, float* save_lse,
+                       uint16_t* out_merged, int heads) {
   FineArgs a;
   a.q = q;
   a.k = k;
@@ -623,6 +694,7 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.gates = gates;
   a.o_cg = o_cg;
   a.sel = sel;
+  a.knorm = knorm;
   a.out = out;
   a.save_o = save_o;
   a.save_lse = save_lse;

@@ -15,6 +15,12 @@
 // cross-lane reduction is needed.  Sums are float64: exact for bf16 inputs
 // (8-bit significands, at most a few thousand terms), and block = 4^k makes
 // the final scaling exact.  HBM-bound: 6*D bytes read per token.
+//
+// The key workgroups can also write each block's largest key norm
+// max_t |k_t| (float32 [slices][m]).  It is not part of the method: the
+// fine-attention kernel turns it into an upper bound on a query's scores
+// over a set of blocks (Cauchy-Schwarz: q.k <= |q| |k|) and then needs no
+// running maximum.
 #include "bsa_common.h"
 
 namespace mosaic {
@@ -24,6 +30,7 @@ struct PoolArgs {
   const uint16_t* src[3];
   double* dst64[2];   // q̄, k̄
   float* dst32;       // v̄
+  float* knorm;       // largest key norm of each block, or null
   long long total_blocks;   // slices * m
   long long wgs_per_tensor;
   int block;
@@ -47,21 +54,60 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0;
 
-  const int rows = a.block;
-  for (int r0 = 0; r0 < rows; r0 += 8) {
-    u32x4 w[8];
+  // NORM: also track the largest squared key norm.  Lane c holds channels
+  // 8c .. 8c+7 of a row, so a row's |k|^2 is a sum over the row's TPR
+  // lanes: each lane forms its 8-channel partials of 8 rows, and a
+  // butterfly over the TPR lanes (each step hands half of the rows to the
+  // partner and adds the partner's share of the other half) leaves every
+  // lane with whole sums of 8/TPR of them.
+  auto sweep = [&](auto NORM) __attribute__((always_inline)) {
+    float nmax = 0.f;
+    for (int r0 = 0; r0 < a.block; r0 += 8) {
+      u32x4 w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = __builtin_nontemporal_load(p + (size_t)(r0 + u) * TPR);
+      for (int u = 0; u < 8; ++u) w[u] = __builtin_nontemporal_load(p + (size_t)(r0 + u) * TPR);
+      float ss[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t x[4] = {w[u][0], w[u][1], w[u][2], w[u][3]};
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t x[4] = {w[u][0], w[u][1], w[u][2], w[u][3]};
+        ss[u] = 0.f;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        acc[2 * h] += (double)__uint_as_float(x[h] << 16);
-        acc[2 * h + 1] += (double)__uint_as_float(x[h] & 0xffff0000u);
+        for (int h = 0; h < 4; ++h) {
+          const float lo = __uint_as_float(x[h] << 16), hi = __uint_as_float(x[h] & 0xffff0000u);
+          acc[2 * h] += (double)lo;
+          acc[2 * h + 1] += (double)hi;
+          if constexpr (decltype(NORM)::value) ss[u] = fmaf(hi, hi, fmaf(lo, lo, ss[u]));
+        }
+      }
+      if constexpr (decltype(NORM)::value) {
+        static_for<0, 3>([&](auto st) __attribute__((always_inline)) {
+          constexpr int off = TPR >> (1 + decltype(st)::value), half = 4 >> decltype(st)::value;
+          if constexpr (off >= 1) {
+            const bool upper = (c & off) != 0;
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+              const float send = upper ? ss[i] : ss[i + half];
+              const float keep = upper ? ss[i + half] : ss[i];
+              ss[i] = keep + __shfl_xor(send, off);
+            }
+          }
+        });
+        constexpr int left = 8 / TPR;   // whole row sums now held by each lane
+#pragma unroll
+        for (int i = 0; i < left; ++i) nmax = fmaxf(nmax, ss[i]);
       }
     }
-  }
+    if constexpr (decltype(NORM)::value) {
+      // the TPR lanes of a block are consecutive and TPR-aligned
+#pragma unroll
+      for (int off = 1; off < TPR; off *= 2) nmax = fmaxf(nmax, __shfl_xor(nmax, off));
+      if (c == 0) a.knorm[gb] = sqrtf(nmax);
+    }
+  };
+  if (tensor == 1 && a.knorm)
+    sweep(std::true_type{});
+  else
+    sweep(std::false_type{});
 
   const size_t o = (size_t)gb * D + c * 8;
   if (tensor < 2) {
@@ -82,7 +128,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 
 hipError_t launch_pool(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* qbar,
                        double* kbar, float* vbar, long long slices, int n_tok, int head_dim,
-                       int block, hipStream_t stream) {
+                       int block, hipStream_t stream, float* knorm) {
   PoolArgs a;
   a.src[0] = q;
   a.src[1] = k;
@@ -90,6 +136,7 @@ hipError_t launch_pool(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.dst64[0] = qbar;
   a.dst64[1] = kbar;
   a.dst32 = vbar;
+  a.knorm = knorm;
   a.total_blocks = slices * (long long)(n_tok / block);
   a.block = block;
   a.inv_block = 1.0 / (double)block;

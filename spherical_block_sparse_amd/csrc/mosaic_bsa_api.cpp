@@ -83,7 +83,7 @@ mosaic_status check_shape(int batch, int heads, int head_dim, int nside, int blo
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Workspace {
-  size_t qbar, kbar, vbar, ocg, total;
+  size_t qbar, kbar, vbar, ocg, knorm, total;
 };
 
 Workspace layout(const Shape& s) {
@@ -93,7 +93,8 @@ Workspace layout(const Shape& s) {
   w.kbar = w.qbar + align256(e * sizeof(double));
   w.vbar = w.kbar + align256(e * sizeof(double));
   w.ocg = w.vbar + align256(e * sizeof(float));
-  w.total = w.ocg + align256(e * sizeof(float));
+  w.knorm = w.ocg + align256(e * sizeof(float));
+  w.total = w.knorm + align256((size_t)s.slices * s.m * sizeof(float));
   return w;
 }
 
@@ -228,17 +229,17 @@ size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside,
 
 mosaic_status mosaic_bsa_pool(const void* q, const void* k, const void* v, int batch, int heads,
                               int head_dim, int nside, int block, double* qbar, double* kbar,
-                              float* vbar, void* stream) {
+                              float* vbar, float* knorm, void* stream) {
   REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v);
   REQUIRE_PTR(qbar); REQUIRE_PTR(kbar); REQUIRE_PTR(vbar);
   REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16);
-  REQUIRE_ALIGN(qbar, 16); REQUIRE_ALIGN(kbar, 16); REQUIRE_ALIGN(vbar, 16);
+  REQUIRE_ALIGN(qbar, 16); REQUIRE_ALIGN(kbar, 16); REQUIRE_ALIGN(vbar, 16); REQUIRE_ALIGN(knorm, 4);
   Shape s;
   mosaic_status st = check_shape(batch, heads, head_dim, nside, block, 0, 0, 0, &s);
   if (st != MOSAIC_OK) return st;
   return hip_status(mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                         static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices,
-                                        s.n_tok, s.d, s.block, static_cast<hipStream_t>(stream)),
+                                        s.n_tok, s.d, s.block, static_cast<hipStream_t>(stream), knorm),
                     "bsa_pool launch");
 }
 
@@ -257,20 +258,20 @@ mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar,
 }
 
 mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const float* gates,
-                              const float* o_cg, const int32_t* sel_idx, int batch, int heads,
-                              int head_dim, int nside, int block, int topn, int window, float* out,
-                              void* stream) {
+                              const float* o_cg, const int32_t* sel_idx, const float* knorm, int batch,
+                              int heads, int head_dim, int nside, int block, int topn, int window,
+                              float* out, void* stream) {
   REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(o_cg);
   REQUIRE_PTR(sel_idx); REQUIRE_PTR(out);
   REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
-  REQUIRE_ALIGN(o_cg, 16); REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(out, 16);
+  REQUIRE_ALIGN(o_cg, 16); REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(knorm, 4);
   Shape s;
   mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
   if (st != MOSAIC_OK) return st;
   return hip_status(mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                         static_cast<const uint16_t*>(v), gates, o_cg, sel_idx, out,
                                         s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
-                                        static_cast<hipStream_t>(stream)),
+                                        static_cast<hipStream_t>(stream), knorm),
                     "bsa_fine launch");
 }
 
@@ -293,16 +294,17 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
   double* kbar = reinterpret_cast<double*>(ws + w.kbar);
   float* vbar = reinterpret_cast<float*>(ws + w.vbar);
   float* ocg = reinterpret_cast<float*>(ws + w.ocg);
+  float* knorm = reinterpret_cast<float*>(ws + w.knorm);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                      static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
-                                     s.d, s.block, hs);
+                                     s.d, s.block, hs, knorm);
   if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
   e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
-                          s.block, s.topn, s.window, hs);
+                          s.block, s.topn, s.window, hs, knorm);
   return hip_status(e, "bsa_fine launch");
 }
 
@@ -432,16 +434,17 @@ mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const vo
   double* kbar = reinterpret_cast<double*>(bws + w.kbar);
   float* vbar = reinterpret_cast<float*>(bws + w.vbar);
   float* ocg = reinterpret_cast<float*>(bws + w.ocg);
+  float* knorm = reinterpret_cast<float*>(bws + w.knorm);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = mosaic::launch_layer_in(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_in), batch,
                                          s.n_tok, channels, heads, s.d, q, k, v, gates, hs);
   if (e != hipSuccess) return hip_status(e, "layer input projection launch");
-  e = mosaic::launch_pool(q, k, v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs);
+  e = mosaic::launch_pool(q, k, v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs, knorm);
   if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
   e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(q, k, v, gates, ocg, sel_idx, nullptr, s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
-                          hs, nullptr, nullptr, attn, heads);
+                          hs, knorm, nullptr, nullptr, attn, heads);
   if (e != hipSuccess) return hip_status(e, "bsa_fine launch");
   return hip_status(mosaic::launch_layer_out_merged(attn, static_cast<const uint16_t*>(w_out),
                                                     static_cast<const uint16_t*>(x), batch, s.n_tok, channels, heads,
@@ -476,16 +479,17 @@ mosaic_status mosaic_bsa_forward_train(const void* q, const void* k, const void*
   double* kbar = reinterpret_cast<double*>(ws + w.kbar);
   float* vbar = reinterpret_cast<float*>(ws + w.vbar);
   float* ocg = reinterpret_cast<float*>(ws + w.ocg);
+  float* knorm = reinterpret_cast<float*>(ws + w.knorm);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                      static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
-                                     s.d, s.block, hs);
+                                     s.d, s.block, hs, knorm);
   if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
   e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
-                          s.block, s.topn, s.window, hs, reinterpret_cast<float*>(base + sv.o),
+                          s.block, s.topn, s.window, hs, knorm, reinterpret_cast<float*>(base + sv.o),
                           reinterpret_cast<float*>(base + sv.lse));
   return hip_status(e, "bsa_fine launch");
 }

@@ -64,7 +64,8 @@ def main() -> int:
         from .locality_study import permute_tokens
         from .synth import nest_ring_order
         q, k, v, g = permute_tokens([q, k, v, g], nest_ring_order(cfg.nside))
-    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
+    knorm = torch.empty((cfg.batch, cfg.heads, cfg.n_blocks), dtype=torch.float32, device="cuda")
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
     torch.cuda.synchronize()
     if args.stage == "backward":
@@ -81,11 +82,11 @@ def main() -> int:
         elif args.stage == "train":
             _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
         elif args.stage == "pool":
-            _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar)
+            _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar, knorm=knorm)
         elif args.stage == "select":
             _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel)
         elif args.stage == "fine":
-            _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window)
+            _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
         else:
             _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
     torch.cuda.synchronize()

@@ -41,7 +41,7 @@ def test_header_declares_and_library_exports_the_same_symbols():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.mosaic_bsa_abi_version() == 5
+    assert L.mosaic_bsa_abi_version() == 6
     for code, name in _lib.STATUS_NAMES.items():
         assert L.mosaic_status_string(code).decode() == name
     assert L.mosaic_status_string(99).decode() == "MOSAIC_ERR_UNKNOWN"
@@ -49,13 +49,14 @@ def test_version_and_status_strings():
 
 def test_workspace_bytes_layout():
     L = _lib.lib()
-    # ns128: S = 192, m = 3072, d = 64 -> two float64 and two float32 [S][m][d] sections
+    # ns128: S = 192, m = 3072, d = 64 -> two float64 and two float32 [S][m][d] sections, then
+    # the float32 [S][m] largest key norm per block
     e = 192 * 3072 * 64
-    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) == e * (8 + 8 + 4 + 4)
+    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) == e * (8 + 8 + 4 + 4) + 192 * 3072 * 4
     # tiny: S = 2, m = 48, d = 32 -> sections rounded up to 256 bytes
     e = 2 * 48 * 32
     r = lambda x: (x + 255) // 256 * 256
-    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 4) == 2 * r(8 * e) + 2 * r(4 * e)
+    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 4) == 2 * r(8 * e) + 2 * r(4 * e) + r(4 * 2 * 48)
     assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 0) == 0      # invalid -> 0
     assert L.mosaic_bsa_workspace_bytes(1, 2, 48, 8, 16, 4) == 0      # unsupported -> 0
 
@@ -89,14 +90,17 @@ def test_forward_validation(kw, code):
 
 def test_stage_entry_points_validate():
     L = _lib.lib()
-    assert L.mosaic_bsa_pool(FAKE, FAKE, None, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None) == NULL
-    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 12, FAKE, FAKE, FAKE, None) == SHAPE
-    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, FAKE + 8, FAKE, FAKE, None) == MISAL
+    assert L.mosaic_bsa_pool(FAKE, FAKE, None, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None, None) == NULL
+    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 12, FAKE, FAKE, FAKE, None, None) == SHAPE
+    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, FAKE + 8, FAKE, FAKE, None, None) == MISAL
+    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, FAKE + 2, None) == MISAL
     assert L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 0, FAKE, FAKE, None) == SHAPE
     assert L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 4, None, FAKE, None) == NULL
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 4, 0, FAKE, None) == SHAPE
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 32, 8, 16, 4, 32, FAKE, None) == NULL
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 4, 4, 32, FAKE, None) == UNSUP
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 32, 8, 16, 4, 0, FAKE, None) == SHAPE
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 32, 8, 16, 4, 32, FAKE, None) == NULL
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 64, 8, 4, 4, 32, FAKE, None) == UNSUP
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 2, 32, 8, 16, 4, 32, FAKE,
+                             None) == MISAL
 
 
 def test_python_binding_rejects_bad_tensors_without_launch():

@@ -121,17 +121,39 @@ def test_compress_select_topn_above_sixteen(topn):
     _check_compress_select(cfg, q, k, v, topn=topn)
 
 
+def _knorm(cfg):
+    return torch.empty((cfg.batch, cfg.heads, cfg.n_blocks), dtype=torch.float32, device=DEV)
+
+
 @pytest.mark.parametrize("name", ["tiny", "ns32"])
-def test_fine_stage_branches_one_hot(name):
-    """mosaic_bsa_fine with one-hot gates isolates o_CG, o_FG and o_L."""
+def test_pool_block_max_key_norm(name):
+    """The pool's largest key norm per block is max_t |k_t| over the block's tokens, up to float32
+    rounding of the sums of squares (the datum the fine kernel's score bounds come from)."""
     cfg = CONFIGS[name]
     q, k, v, _ = _gpu_inputs(cfg)
-    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
+    knorm = _knorm(cfg)
+    _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
+    torch.cuda.synchronize()
+    want = k.double().cpu().norm(dim=-1).reshape(cfg.batch, cfg.heads, cfg.n_blocks, -1).amax(-1)
+    got = knorm.double().cpu()
+    assert torch.all((got - want).abs() <= 1e-5 * want), (got - want).abs().max().item()
+
+
+@pytest.mark.parametrize("bounds", [False, True])
+@pytest.mark.parametrize("name", ["tiny", "ns32"])
+def test_fine_stage_branches_one_hot(name, bounds):
+    """mosaic_bsa_fine with one-hot gates isolates o_CG, o_FG and o_L, with the running-maximum
+    softmax (no knorm) and with the pool's score bounds."""
+    cfg = CONFIGS[name]
+    q, k, v, _ = _gpu_inputs(cfg)
+    knorm = _knorm(cfg) if bounds else None
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
     for col, key in [(0, "o_cg"), (1, "o_fg"), (2, "o_l")]:
         g = torch.zeros((cfg.batch, cfg.heads, cfg.n_tokens, 3), dtype=torch.float32, device=DEV)
         g[..., col] = 1.0
-        out = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window)
+        out = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                   knorm=knorm)
         torch.cuda.synchronize()
         for b in range(cfg.batch):
             for h in range(min(cfg.heads, 2)):
@@ -140,6 +162,32 @@ def test_fine_stage_branches_one_hot(name):
                                            np.ones((cfg.n_tokens, 3)), cfg.block, cfg.topn, cfg.window, idx=gi)
                 want = ref[key][np.arange(cfg.n_tokens) // cfg.block] if key == "o_cg" else ref[key]
                 assert_close(out[b, h].cpu().numpy(), want, f"{key}[{b},{h}]")
+
+
+@pytest.mark.parametrize("name,scale", [("tiny", 1.0), ("tiny", 3.5), ("tiny", 8.0),
+                                        ("ns32", 1.0), ("ns32", 3.0), ("ns32", 4.0)])
+def test_fine_score_bound_paths(name, scale):
+    """q scaled (and rounded back to bf16) so that the score bounds c*|q|*max|k| from the pool's
+    largest key norms are small for every wave (all take the bound as their fixed reference:
+    tiny and ns32 unscaled), small for some waves only (tiny at 3.5, ns32 at 3), or too large
+    everywhere (the running maximum: tiny at 8, ns32 at 4).  The output matches the oracle in
+    each case, with and without knorm."""
+    cfg = CONFIGS[name]
+    q, k, v, g = _gpu_inputs(cfg)
+    q = (q.float() * scale).to(torch.bfloat16)
+    log(f"[case] q scaled by {scale}")
+    knorm = _knorm(cfg)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
+    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
+    out_b = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
+    out_l = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (cfg.batch - 1, cfg.heads - 1)]:
+        gi = sel[b, h].cpu().numpy()
+        ref = oracle.bsa_slice_ref(_slice(q, b, h), _slice(k, b, h), _slice(v, b, h), _slice(g, b, h),
+                                   cfg.block, cfg.topn, cfg.window, idx=gi)
+        assert_close(out_b[b, h].cpu().numpy(), ref["out"], f"bounded out[{b},{h}]")
+        assert_close(out_l[b, h].cpu().numpy(), ref["out"], f"running-max out[{b},{h}]")
 
 
 # ---------------------------------------------------------- end to end ------
@@ -233,7 +281,10 @@ def test_edge_topn_one():
 def test_edge_window_one_is_v():
     g1 = lambda g: torch.zeros_like(g).index_fill_(-1, torch.tensor([2], device=DEV), 1.0)
     cfg, q, k, v, g, out, idx = _edge(CONFIGS["tiny"], window=1, gates=g1)
-    assert torch.equal(out, v.float())
+    # o_L is v itself; the one weight w need not be exactly 1 (a score bound can be the softmax
+    # reference), so out = (1/w)(w v) is v up to float32 rounding of that product and quotient
+    want = v.float()
+    assert torch.all((out - want).abs() <= 2 * 2.0 ** -23 * want.abs())
 
 
 def test_edge_window_wider_than_sphere():
@@ -307,8 +358,9 @@ def test_forward_equals_stages():
     cfg = CONFIGS["ns32"]
     q, k, v, g = _gpu_inputs(cfg)
     out, idx = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
-    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
+    knorm = _knorm(cfg)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
-    out2 = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    out2 = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
     torch.cuda.synchronize()
     assert torch.equal(idx, sel) and torch.equal(out, out2)
