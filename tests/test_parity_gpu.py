@@ -164,15 +164,29 @@ def test_fine_stage_branches_one_hot(name, bounds):
                 assert_close(out[b, h].cpu().numpy(), want, f"{key}[{b},{h}]")
 
 
+# blocks of 256 tokens: the fine kernel runs 128-query tiles on 4 waves
+WIDE = CONFIGS["ns32"].with_(name="ns16-b256", nside=16, block=256, topn=4, window=100, batch=2, heads=2, seed=16)
+
+
+def test_forward_wide_tiles_all_slices():
+    """Blocks of 256 tokens (4-wave, 128-query fine tiles) at a size the oracle runs in full."""
+    cfg = WIDE
+    q, k, v, g = _gpu_inputs(cfg)
+    out, idx = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    torch.cuda.synchronize()
+    _full_compare(cfg, q, k, v, g, out, idx)
+
+
 @pytest.mark.parametrize("name,scale", [("tiny", 1.0), ("tiny", 3.5), ("tiny", 8.0),
-                                        ("ns32", 1.0), ("ns32", 3.0), ("ns32", 4.0)])
+                                        ("ns32", 1.0), ("ns32", 3.0), ("ns32", 4.0),
+                                        ("wide", 1.0), ("wide", 4.0)])
 def test_fine_score_bound_paths(name, scale):
     """q scaled (and rounded back to bf16) so that the score bounds c*|q|*max|k| from the pool's
     largest key norms are small for every wave (all take the bound as their fixed reference:
     tiny and ns32 unscaled), small for some waves only (tiny at 3.5, ns32 at 3), or too large
     everywhere (the running maximum: tiny at 8, ns32 at 4).  The output matches the oracle in
     each case, with and without knorm."""
-    cfg = CONFIGS[name]
+    cfg = WIDE if name == "wide" else CONFIGS[name]
     q, k, v, g = _gpu_inputs(cfg)
     q = (q.float() * scale).to(torch.bfloat16)
     log(f"[case] q scaled by {scale}")
