@@ -38,7 +38,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 // (it cannot tell which buffer those reads touch), which serialises the
 // prefetch of the next chunk with the current one.  The loads have no
 // register results; their completion is awaited explicitly (s_waitcnt
-// vmcnt, then a barrier) before a buffer is read.  M0 is restored.
+// vmcnt, then a barrier) before a buffer is read.  M0 is restored.  A
+// scalar write of M0 needs one wait state before an LDS-DMA load reads it
+// (the compiler cannot insert it inside the assembly), hence the s_nop 0.
 typedef int int32x4 __attribute__((ext_vector_type(4)));
 
 // LDS byte address of p as a scalar (the asm operands below must be SGPRs;
@@ -52,6 +54,7 @@ __device__ __forceinline__ void dma_buffer(const void* lds, int voff, int32x4 rs
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -64,6 +67,7 @@ __device__ __forceinline__ void dma_global(const void* lds, const void* src) {
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -81,6 +85,7 @@ __device__ __forceinline__ void dma_buffer_at(int lds_base, int voff, int32x4 rs
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_add_u32 m0, %1, %5\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -94,10 +99,48 @@ __device__ __forceinline__ void dma_global_at(int lds_base, const void* src) {
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_add_u32 m0, %1, %3\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds_base), "v"(src), "n"(OFF)
+      : "memory", "scc");
+}
+
+// The same for two loads sharing one M0 save and restore: K and V rows at
+// the same per-lane offset into two buffers (OFF0, OFF1 bytes past lds_base).
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void dma_buffer_pair_at(int lds_base, int voff, int32x4 r0, int32x4 r1, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %6\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %5 offen lds\n\t"
+      "s_add_u32 m0, %1, %7\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(r0), "s"(r1), "s"(__builtin_amdgcn_readfirstlane(soff)), "n"(OFF0),
+        "n"(OFF1)
+      : "memory", "scc");
+}
+
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void dma_global_pair_at(int lds_base, const void* src0, const void* src1) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_add_u32 m0, %1, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(src0), "v"(src1), "n"(OFF0), "n"(OFF1)
       : "memory", "scc");
 }
 

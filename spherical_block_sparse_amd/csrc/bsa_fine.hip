@@ -461,9 +461,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     if (valid >= 64 && use_rsrc) {   // whole chunk of consecutive tokens: no per-lane checks
       const int soff = __builtin_amdgcn_readfirstlane(tok0 * (D * 2));   // uniform by construction
       static_for<0, LPW>([&](auto gg) __attribute__((always_inline)) {
-        const int off = 2 * lane_off[gg];
-        dma_buffer_at<at(P, 0, gg)>(lds_base, off, rk, soff);
-        dma_buffer_at<at(P, 1, gg)>(lds_base, off, rv, soff);
+        dma_buffer_pair_at<at(P, 0, gg), at(P, 1, gg)>(lds_base, 2 * lane_off[gg], rk, rv, soff);
       });
       return;
     }
@@ -472,8 +470,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     static_for<0, LPW>([&](auto gg) __attribute__((always_inline)) {
       const bool ok = lane_row[gg] < valid;
       const unsigned off = 2u * (unsigned)lane_off[gg];
-      dma_global_at<at(P, 0, gg)>(lds_base, ok ? (const void*)(kbase + off) : (const void*)&kZero16);
-      dma_global_at<at(P, 1, gg)>(lds_base, ok ? (const void*)(vbase + off) : (const void*)&kZero16);
+      dma_global_pair_at<at(P, 0, gg), at(P, 1, gg)>(lds_base, ok ? (const void*)(kbase + off) : (const void*)&kZero16,
+                                                    ok ? (const void*)(vbase + off) : (const void*)&kZero16);
     });
   };
   auto issue_gather = [&](int ci, auto P) __attribute__((always_inline)) {
@@ -481,10 +479,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       const int row = lane_row[gg];
       const int lc = (lane % CPR) ^ swz<D>(row);
       const int tok = token_of(ci, row);
-      dma_global_at<at(P, 0, gg)>(lds_base, tok >= 0 ? (const void*)(ks + (size_t)tok * D + 8 * lc)
-                                                     : (const void*)&kZero16);
-      dma_global_at<at(P, 1, gg)>(lds_base, tok >= 0 ? (const void*)(vs + (size_t)tok * D + 8 * lc)
-                                                     : (const void*)&kZero16);
+      dma_global_pair_at<at(P, 0, gg), at(P, 1, gg)>(
+          lds_base, tok >= 0 ? (const void*)(ks + (size_t)tok * D + 8 * lc) : (const void*)&kZero16,
+          tok >= 0 ? (const void*)(vs + (size_t)tok * D + 8 * lc) : (const void*)&kZero16);
     });
   };
   // loads of chunk ci into buffer pair P (std::integral_constant 0 or 1)
