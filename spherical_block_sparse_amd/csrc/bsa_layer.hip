@@ -470,12 +470,129 @@ __global__ __launch_bounds__(64 * kBWaves) void layer_gemm_big_kernel(GemmArgs p
   epilogue_staged<OUT>(p, acc, m0, f0, bi0, t0, wm, wf, reinterpret_cast<float*>(smem) + w * 64 * (64 + 4));
 }
 
+// 256 x 256 tiles: twice the FLOPs per staged byte of the 256 x 128 kernel.
+// 8 waves in 4 x 2, each 64 tokens x 128 features (32 MFMA tiles); two LDS
+// stages of 64 KB, the next chunk loading while one is computed (the same
+// 2048 clocks of MFMA work in flight ahead of the loads as three stages of
+// the narrower tile); the epilogue stages each 64-feature half of a wave's
+// tile through LDS.
+constexpr int kWT = 256;
+constexpr int kWRS = 64 + 4;   // floats per staged epilogue row
+constexpr int kWSmem = (2 * 2 * kWT * kGK) > (kBWaves * 64 * kWRS * 2) ? (2 * 2 * kWT * kGK) : (kBWaves * 64 * kWRS * 2);
+
+template <bool OUT>
+__global__ __launch_bounds__(64 * kBWaves) void layer_gemm_wide_kernel(GemmArgs p) {
+  // stage s: A (256 x 64) at s * 2*kWT*kGK, then B (256 x 64); the epilogue
+  // reuses the whole array (uint16 units)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kWSmem];
+  auto As = [&](int st) __attribute__((always_inline)) { return smem + st * 2 * kWT * kGK; };
+  auto Bs = [&](int st) __attribute__((always_inline)) { return smem + st * 2 * kWT * kGK + kWT * kGK; };
+  const long long tiles = (long long)p.m_tiles * p.f_tiles;
+  long long logical;
+  {
+    const long long b = blockIdx.x, q8 = tiles / 8, r8 = tiles % 8, xcd = b % 8, kq = b / 8;
+    logical = xcd < r8 ? xcd * (q8 + 1) + kq : r8 * (q8 + 1) + (xcd - r8) * q8 + kq;
+  }
+  const long long m0 = (logical / p.f_tiles) * kWT;
+  const int f0 = (int)(logical % p.f_tiles) * kWT;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = w & 3, wf = w >> 2;   // the wave's 64-token and 128-feature part
+  const int nk = p.K / kGK;
+  const long long bi0 = m0 / p.n_tok;
+  const int t0 = (int)(m0 - bi0 * p.n_tok);
+  constexpr int kLoadsA = kWT / 8 / kBWaves, kLoadsB = kWT / 8 / kBWaves;   // 4 + 4 per wave and chunk
+  constexpr int kLoads = kLoadsA + kLoadsB;
+  // per-lane source pointers, formed once (rows past the matrix clamped to
+  // its last row: they only feed results the epilogue never stores)
+  const int lane = threadIdx.x % kWave;
+  const uint16_t* srcA[kLoadsA];
+  const uint16_t* srcB[kLoadsB];
+#pragma unroll
+  for (int i = 0; i < kLoadsA; ++i) {
+    const int row = 8 * (w + kBWaves * i) + lane / 8;
+    const long long r = m0 + row < p.M ? m0 + row : p.M - 1;
+    srcA[i] = p.a + r * p.K + 8 * ((lane % 8) ^ gswz(row));
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsB; ++i) {
+    const int row = 8 * (w + kBWaves * i) + lane / 8;
+    const long long r = f0 + row < p.F ? f0 + row : p.F - 1;
+    srcB[i] = p.b + r * p.K + 8 * ((lane % 8) ^ gswz(row));
+  }
+  const int lds_wave = lds_addr(smem) + w * 1024;   // the wave's first 1 KB slot
+  auto stage = [&](int c, int s) __attribute__((always_inline)) {
+    const int k0 = c * kGK;
+    const int a_base = __builtin_amdgcn_readfirstlane(lds_wave + s * (2 * kWT * kGK * 2));
+    const int b_base = __builtin_amdgcn_readfirstlane(lds_wave + s * (2 * kWT * kGK * 2) + kWT * kGK * 2);
+    static_for<0, kLoadsA>([&](auto i) __attribute__((always_inline)) {
+      dma_global_at<decltype(i)::value * kBWaves * 1024>(a_base, srcA[decltype(i)::value] + k0);
+    });
+    static_for<0, kLoadsB>([&](auto i) __attribute__((always_inline)) {
+      dma_global_at<decltype(i)::value * kBWaves * 1024>(b_base, srcB[decltype(i)::value] + k0);
+    });
+  };
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int ft = 0; ft < 8; ++ft)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[ft][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  for (int c = 0; c < nk; ++c) {
+    const int s = c & 1;
+    // stage s^1 was last read in chunk c-1, before the barrier that ended it
+    if (c + 1 < nk) stage(c + 1, s ^ 1);
+    const uint16_t* a_t = As(s) + wm * 64 * kGK;
+    const uint16_t* b_t = Bs(s) + wf * 128 * kGK;
+#pragma unroll
+    for (int kk = 0; kk < kGK / 32; ++kk) {
+      bf16x8 bo[8], ao[4];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) bo[t] = tile_operand(b_t, t, kk);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ao[t] = tile_operand(a_t, t, kk);
+#pragma unroll
+      for (int ft = 0; ft < 8; ++ft)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[ft][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo[ft], ao[mt], acc[ft][mt], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // chunk c+1 has landed
+    __syncthreads();
+  }
+  // the stages are free (every wave passed the last barrier): each wave takes
+  // a 64 x 68 float region and writes its two 64-feature halves in turn (a
+  // wave's own LDS reads and writes are processed in order)
+  float* lds = reinterpret_cast<float*>(smem) + w * 64 * kWRS;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    floatx4 half[4][4];
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) half[ft][mt] = acc[4 * h + ft][mt];
+    epilogue_staged<OUT>(p, half, m0, f0 + 128 * wf + 64 * h, bi0, t0, wm, 0, lds);
+  }
+}
+
 hipError_t launch_gemm(GemmArgs p, bool out, bool a32, hipStream_t stream) {
   p.f_tiles = (p.F + kGT - 1) / kGT;
   if (a32) {
     p.m_tiles = (int)((p.M + kGT - 1) / kGT);
     const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
     hipLaunchKernelGGL((layer_gemm_kernel<true, true>), grid, dim3(64 * kGWaves), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (p.F >= kWT) {   // 256 x 256 tiles
+    p.f_tiles = (p.F + kWT - 1) / kWT;
+    p.m_tiles = (int)((p.M + kWT - 1) / kWT);
+    const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
+    if (out)
+      hipLaunchKernelGGL(layer_gemm_wide_kernel<true>, grid, dim3(64 * kBWaves), 0, stream, p);
+    else
+      hipLaunchKernelGGL(layer_gemm_wide_kernel<false>, grid, dim3(64 * kBWaves), 0, stream, p);
     return hipGetLastError();
   }
   p.m_tiles = (int)((p.M + kBT - 1) / kBT);
