@@ -26,38 +26,61 @@
 namespace mosaic {
 namespace {
 
+// rows handled by each 8-lane group: their loads are all issued before any
+// is used, so a wave keeps kRowsPerGroup KB in flight (one 16-byte load per
+// lane and row leaves the kernel latency-bound at about half of HBM peak)
+constexpr int kRowsPerGroup = 4;
+
 __global__ __launch_bounds__(256) void kappa_kernel(const uint16_t* k, const float* w_q, float4* kappa, long long rows,
                                                     int d, float inv_sqrt_d) {
   __shared__ float W[256 * 3];
   for (int e = threadIdx.x; e < 3 * d; e += 256) W[e] = w_q[e];
   __syncthreads();
   // 8 lanes per row, each taking 16-byte pieces 8*e, 8*e + 64, ... of it, so
-  // a wave reads 8 consecutive rows as one contiguous span
-  const long long row = (long long)blockIdx.x * 32 + threadIdx.x / 8;
+  // a wave reads 8 consecutive rows as one contiguous span; the group's rows
+  // are 32 apart, so each of its loads is one such span of its wave
+  const long long row0 = (long long)blockIdx.x * 32 * kRowsPerGroup + threadIdx.x / 8;
   const int e = threadIdx.x % 8;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f;
-  if (row < rows) {
-    const uint16_t* src = k + row * d;
-    for (int c = 8 * e; c < d; c += 64) {
-      const uint4 u = *reinterpret_cast<const uint4*>(src + c);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int c0 = 0; c0 < d; c0 += 64) {   // d <= 64 in one pass; larger d in passes of 64
+    const int c = c0 + 8 * e;
+    uint4 u[kRowsPerGroup];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = __builtin_bit_cast(float, i & 1 ? (w[i / 2] & 0xffff0000u) : (w[i / 2] << 16));
-        const float* wr = W + 3 * (c + i);   // w_q[d][3], row c + i
-        a0 = fmaf(wr[0], x, a0);
-        a1 = fmaf(wr[1], x, a1);
-        a2 = fmaf(wr[2], x, a2);
+    for (int r = 0; r < kRowsPerGroup; ++r) {
+      const long long row = row0 + 32 * r;
+      u[r] = row < rows && c < d ? *reinterpret_cast<const uint4*>(k + row * d + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerGroup; ++r) {
+      const long long row = row0 + 32 * r;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+      const uint32_t w[4] = {u[r].x, u[r].y, u[r].z, u[r].w};
+      if (c < d) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = __builtin_bit_cast(float, i & 1 ? (w[i / 2] & 0xffff0000u) : (w[i / 2] << 16));
+          const float* wr = W + 3 * (c + i);   // w_q[d][3], row c + i
+          a0 = fmaf(wr[0], x, a0);
+          a1 = fmaf(wr[1], x, a1);
+          a2 = fmaf(wr[2], x, a2);
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        a0 += __shfl_xor(a0, o, 8);
+        a1 += __shfl_xor(a1, o, 8);
+        a2 += __shfl_xor(a2, o, 8);
+      }
+      if (row < rows && e == 0) {
+        if (c0 == 0) {
+          kappa[row] = make_float4(a0 * inv_sqrt_d, a1 * inv_sqrt_d, a2 * inv_sqrt_d, 0.f);
+        } else {
+          float4 t = kappa[row];
+          t.x += a0 * inv_sqrt_d; t.y += a1 * inv_sqrt_d; t.z += a2 * inv_sqrt_d;
+          kappa[row] = t;
+        }
       }
     }
   }
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) {
-    a0 += __shfl_xor(a0, o, 8);
-    a1 += __shfl_xor(a1, o, 8);
-    a2 += __shfl_xor(a2, o, 8);
-  }
-  if (row < rows && e == 0) kappa[row] = make_float4(a0 * inv_sqrt_d, a1 * inv_sqrt_d, a2 * inv_sqrt_d, 0.f);
 }
 
 __global__ __launch_bounds__(256) void interp_kernel(const float4* kappa, const uint16_t* v, const int32_t* nbr,
@@ -122,8 +145,8 @@ hipError_t launch_interp(const uint16_t* k, const uint16_t* v, const float* w_q,
                          const float* rel, long long slices, int n_src, int n_dst, int n_nbr, int d, float* out,
                          float4* kappa, hipStream_t stream) {
   const long long rows = slices * n_src;
-  hipLaunchKernelGGL(kappa_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, k, w_q, kappa, rows, d,
-                     (float)(1.0 / sqrt((double)d)));
+  hipLaunchKernelGGL(kappa_kernel, dim3((unsigned)((rows + 32 * kRowsPerGroup - 1) / (32 * kRowsPerGroup))), dim3(256),
+                     0, stream, k, w_q, kappa, rows, d, (float)(1.0 / sqrt((double)d)));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long groups = slices * n_dst;
