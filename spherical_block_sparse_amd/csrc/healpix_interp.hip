@@ -13,10 +13,11 @@
 //     the eight lanes; HBM-bound (d*2 bytes read, 16 written);
 //   * interp_kernel: one 16-lane group per target.  Lane l holds neighbour l
 //     (index, relative position, kappa -> score); max and sum over the group
-//     by shuffles; then lane l accumulates output dims 4l .. 4l+3 over the
-//     neighbours, each neighbour's v row read by the 16 lanes as one
-//     contiguous 128-byte line, all 16 rows in flight at once and issued
-//     as soon as the indices are known.  Targets in NESTED order share most of
+//     by shuffles; then lane l accumulates 8 output dims over half of the
+//     neighbours from 16-byte pieces (one load instruction brings two whole
+//     128-byte v rows per group), and lanes l, l ^ 8 add their halves.  All
+//     16 rows are in flight at once, issued as soon as the indices are
+//     known.  Targets in NESTED order share most of
 //     their stencils, so the gathered rows hit in L2; the workgroup order is
 //     XCD-contiguous.  HBM-bound.
 #include "bsa_common.h"
@@ -105,11 +106,14 @@ __global__ __launch_bounds__(256) void interp_kernel(const float4* kappa, const 
   }
   // the 16 value rows depend only on the indices: they are all issued before
   // the scores are formed, so their latency overlaps the kappa gather (a
-  // lane past n_nbr has index 0 and, below, weight 0)
-  const uint16_t* vs = v + s * (long long)n_src * DV + 4 * l;
-  ushort4 rows[16];
+  // lane past n_nbr has index 0 and, below, weight 0).  Lane l reads 16-byte
+  // pieces 8*(l%8) .. +7 of rows 2*i + l/8: one load instruction brings two
+  // whole 128-byte rows per group.
+  const int h = l >> 3, c8 = 8 * (l & 7);
+  const uint16_t* vs = v + s * (long long)n_src * DV + c8;
+  uint4 rows[8];
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) rows[jj] = *reinterpret_cast<const ushort4*>(vs + (long long)__shfl(j, jj, 16) * DV);
+  for (int ii = 0; ii < 8; ++ii) rows[ii] = *reinterpret_cast<const uint4*>(vs + (long long)__shfl(j, 2 * ii + h, 16) * DV);
 
   float score = -INFINITY;
   if (l < n_nbr) {
@@ -126,17 +130,26 @@ __global__ __launch_bounds__(256) void interp_kernel(const float4* kappa, const 
   for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 16);
   const float pw = e / sum;
 
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8];
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const float pj = __shfl(pw, jj, 16);
-    const ushort4 b = rows[jj];
-    acc.x = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.x << 16), acc.x);
-    acc.y = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.y << 16), acc.y);
-    acc.z = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.z << 16), acc.z);
-    acc.w = fmaf(pj, __builtin_bit_cast(float, (uint32_t)b.w << 16), acc.w);
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const float pj = __shfl(pw, 2 * ii + h, 16);
+    const uint32_t wv[4] = {rows[ii].x, rows[ii].y, rows[ii].z, rows[ii].w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      acc[q] = fmaf(pj, __builtin_bit_cast(float, q & 1 ? (wv[q / 2] & 0xffff0000u) : (wv[q / 2] << 16)), acc[q]);
   }
-  *reinterpret_cast<float4*>(out + item * DV + 4 * l) = acc;
+  // lanes l and l ^ 8 hold the two halves of the rows for the same 8 dims:
+  // lane l keeps dims c8 + 4h .. +3 of the sum
+  float4 o4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float mine = acc[4 * h + q], other = __shfl_xor(acc[4 * (1 - h) + q], 8, 16);
+    (&o4.x)[q] = mine + other;
+  }
+  *reinterpret_cast<float4*>(out + item * DV + c8 + 4 * h) = o4;
 }
 
 }  // namespace
