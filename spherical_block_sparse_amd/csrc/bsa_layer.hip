@@ -12,21 +12,24 @@
 // with bf16 activations between the steps (q, k, v, the merged attention
 // output and y are rounded to bf16 once, round-to-nearest-even).
 //
-// Both projections are one GEMM kernel, D[m][n] = sum_k A[m][k] B[n][k]
-// (A: tokens x K, B: features x K, both with K contiguous), with
-// v_mfma_f32_16x16x32_bf16:
-//   * a workgroup owns a 128-token x 128-feature tile, four waves in 2 x 2,
-//     each 64 x 64 = 4 x 4 MFMA tiles (64 accumulator registers);
-//   * K streams through LDS in 64-wide chunks, double-buffered: bf16 rows
-//     arrive by direct global->LDS loads into XOR-swizzled [64][64] tiles;
-//     within the layer the attention output arrives already in bf16 with the
-//     heads side by side (the fine kernel's merged mode); the stage entry
-//     point's float32 [b][H][N][d] input is instead loaded into registers
-//     one chunk ahead, rounded to bf16 and written to LDS;
+// Both projections are GEMMs D[m][n] = sum_k A[m][k] B[n][k] (A: tokens x K,
+// B: features x K, both with K contiguous) with v_mfma_f32_16x16x32_bf16:
+//   * bf16 operands, 256 or more output features (the input projection, and
+//     the output projection from the attention output that the fine
+//     kernel's merged mode writes in bf16 with the heads side by side): a
+//     workgroup owns a 256-token x 256-feature tile, eight waves in 4 x 2,
+//     each 64 tokens x 128 features (128 accumulator registers); K streams
+//     through two 64 KB LDS stages by direct global->LDS loads into
+//     XOR-swizzled rows; fewer than 256 features use 256 x 128 tiles with
+//     three stages;
+//   * the stage entry point's float32 [b][H][N][d] attention output is
+//     instead loaded into registers one chunk ahead, rounded to bf16 and
+//     written to LDS, in 128 x 128 tiles of four waves;
 //   * the MFMA computes the transposed tile (features x tokens), so each
-//     lane ends with four consecutive features of one token: the epilogue
-//     stores 8 contiguous bytes per lane (the head split of q, k, v, the
-//     sigmoid of the gate logits, or x + the projection);
+//     lane ends with four consecutive features of one token; the epilogue
+//     stages a wave's 64 x 64 results through LDS and stores whole 128-byte
+//     rows (the head split of q, k, v, or x + the projection); the sigmoid
+//     gate logits are stored from registers;
 //   * workgroups are renumbered so each XCD runs a contiguous run of tiles:
 //     the feature tiles of one token tile then share its rows in one L2.
 #include "bsa_common.h"
