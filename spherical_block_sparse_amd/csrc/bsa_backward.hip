@@ -739,15 +739,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 // inverted selection, one workgroup per slice: off[j] .. off[j+1] indexes
 // the ascending list of query blocks whose selection holds key block j.
 // Counts and cursors live in LDS (m <= kIndexMaxBlocks); the entries are
-// scattered into `tmp` in arrival order and then each list is rank-sorted by
-// one wave into `list`, ordered by (query block, position in `tmp`) so that
-// the result is deterministic and a permutation even if a selection row
-// repeats an index.
+// scattered into `tmp` in arrival order.  bwd_list_sort_kernel then
+// rank-sorts each list by one wave into `list`, ordered by (query block,
+// position in `tmp`), so that the result is deterministic and a permutation
+// even if a selection row repeats an index.
 
 constexpr int kIndexThreads = 1024;
 
 __global__ __launch_bounds__(kIndexThreads) void bwd_index_kernel(const int32_t* sel, int32_t* off, int32_t* tmp,
-                                                                   int32_t* list, int m, int n) {
+                                                                   int m, int n) {
   __shared__ int32_t cnt[kIndexMaxBlocks + 1];
   __shared__ int32_t wsum[kIndexThreads / 64];
   const long long slice = blockIdx.x;
@@ -756,7 +756,6 @@ __global__ __launch_bounds__(kIndexThreads) void bwd_index_kernel(const int32_t*
   const int32_t* s = sel + slice * total;
   int32_t* o = off + slice * (m + 1);
   int32_t* t = tmp + slice * total;
-  int32_t* l = list + slice * total;
   for (int j = tid; j < m; j += kIndexThreads) cnt[j] = 0;
   __syncthreads();
   for (int e = tid; e < total; e += kIndexThreads) atomicAdd(&cnt[min(max(s[e], 0), m - 1)], 1);
@@ -786,26 +785,39 @@ __global__ __launch_bounds__(kIndexThreads) void bwd_index_kernel(const int32_t*
   __syncthreads();
 
   for (int e = tid; e < total; e += kIndexThreads) t[atomicAdd(&cnt[min(max(s[e], 0), m - 1)], 1)] = e / n;
-  __syncthreads();
+}
 
-  // rank sort, one wave per list: the element at position p of the list
-  // goes to the number of elements before it in (value, position) order
-  for (int j = w; j < m; j += kIndexThreads / 64) {
-    const int b = j ? cnt[j - 1] : 0, len = cnt[j] - b;   // cnt[j] is now the end of list j
-    for (int pc = 0; pc < len; pc += 64) {
-      const int p = pc + lane;
-      const int x = p < len ? t[b + p] : INT_MAX;
-      int rank = 0;
-      for (int qc = 0; qc < len; qc += 64) {
-        const int y = qc + lane < len ? t[b + qc + lane] : INT_MAX;
-        const int qn = min(64, len - qc);
-        for (int r = 0; r < qn; ++r) {
-          const int yr = __shfl(y, r);
-          rank += (yr < x) || (yr == x && qc + r < p);
-        }
+// Each inverted list sorted by query block (the scatter above leaves the
+// order of its atomics), so that dk/dv accumulate in a fixed order: one wave
+// per list over all slices, a rank sort (the element at position p goes to
+// the number of elements before it in (value, position) order).
+constexpr int kSortWaves = 4;
+
+__global__ __launch_bounds__(64 * kSortWaves) void bwd_list_sort_kernel(const int32_t* off, const int32_t* tmp,
+                                                                        int32_t* list, long long lists, int m,
+                                                                        int total) {
+  const long long id = (long long)blockIdx.x * kSortWaves + threadIdx.x / 64;
+  if (id >= lists) return;   // whole waves leave together
+  const int lane = threadIdx.x & 63;
+  const long long slice = id / m;
+  const int j = (int)(id - slice * m);
+  const int32_t* o = off + slice * (m + 1);
+  const int32_t* t = tmp + slice * total;
+  int32_t* l = list + slice * total;
+  const int b = o[j], len = o[j + 1] - b;
+  for (int pc = 0; pc < len; pc += 64) {
+    const int p = pc + lane;
+    const int x = p < len ? t[b + p] : INT_MAX;
+    int rank = 0;
+    for (int qc = 0; qc < len; qc += 64) {
+      const int y = qc + lane < len ? t[b + qc + lane] : INT_MAX;
+      const int qn = min(64, len - qc);
+      for (int r = 0; r < qn; ++r) {
+        const int yr = __shfl(y, r);
+        rank += (yr < x) || (yr == x && qc + r < p);
       }
-      if (p < len) l[b + rank] = x;
     }
+    if (p < len) l[b + rank] = x;
   }
 }
 
@@ -840,7 +852,10 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
   // fine branches
   if (m > kIndexMaxBlocks) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_index_kernel, dim3((unsigned)S), dim3(kIndexThreads), 0, stream, L.sel, L.inv_off,
-                     L.inv_tmp, L.inv_list, m, L.topn);
+                     L.inv_tmp, m, L.topn);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_list_sort_kernel, dim3((unsigned)((S * m + kSortWaves - 1) / kSortWaves)),
+                     dim3(64 * kSortWaves), 0, stream, L.inv_off, L.inv_tmp, L.inv_list, S * m, m, m * L.topn);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   BwdArgs f = {};
   f.q = L.q; f.k = L.k; f.v = L.v; f.dob = L.dob; f.dof = L.dout; f.gates = L.gates; f.sel = L.sel;
