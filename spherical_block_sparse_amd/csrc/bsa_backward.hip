@@ -812,8 +812,8 @@ __global__ __launch_bounds__(64 * kSortWaves) void bwd_list_sort_kernel(const in
     for (int qc = 0; qc < len; qc += 64) {
       const int y = qc + lane < len ? t[b + qc + lane] : INT_MAX;
       const int qn = min(64, len - qc);
-      for (int r = 0; r < qn; ++r) {
-        const int yr = __shfl(y, r);
+      for (int r = 0; r < qn; ++r) {   // r is uniform: a scalar broadcast, no LDS permute
+        const int yr = __builtin_amdgcn_readlane(y, r);
         rank += (yr < x) || (yr == x && qc + r < p);
       }
     }
