@@ -256,11 +256,11 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs p, const floatx4 
   }
 }
 
-// OUT false: input projection (A = x via direct loads, head-split epilogue);
-// OUT true: output projection (residual epilogue), A either bf16 [M][K] via
-// direct loads or (A32) the float32 [b][H][N][d] attention output
-template <bool OUT, bool A32>
-__global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
+// The output projection (residual epilogue) from the float32 [b][H][N][d]
+// attention output of the stage entry point: 128 x 128 tiles on four waves,
+// A loaded into registers one chunk ahead and rounded to bf16 into LDS.
+template <bool OUT>
+__global__ __launch_bounds__(64 * kGWaves) void layer_gemm_a32_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kGT * kGK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGT * kGK];
   const long long tiles = (long long)p.m_tiles * p.f_tiles;
@@ -312,7 +312,6 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
     }
   };
   auto stage = [&](int c, int s) __attribute__((always_inline)) {
-    if constexpr (!A32) stage_bf16(As[s], p.a, m0, p.M, p.K, c * kGK, w);
     stage_bf16(Bs[s], p.b, f0, p.F, p.K, c * kGK, w);
   };
 
@@ -322,10 +321,8 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[ft][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (A32) {
-    load_a32(0);
-    store_a32(As[0]);
-  }
+  load_a32(0);
+  store_a32(As[0]);
   stage(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads have landed
   __syncthreads();
@@ -333,7 +330,7 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
     const int s = c & 1;
     if (c + 1 < nk) {
       stage(c + 1, s ^ 1);
-      if constexpr (A32) load_a32(c + 1);
+      load_a32(c + 1);
     }
     const uint16_t* a_t = As[s] + wm * 64 * kGK;
     const uint16_t* b_t = Bs[s] + wf * 64 * kGK;
@@ -352,9 +349,7 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
           acc[ft][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo[ft], ao[mt], acc[ft][mt], 0, 0, 0);
     }
     // buffer s^1 was last read in chunk c-1, before the barrier that ended it
-    if constexpr (A32) {
-      if (c + 1 < nk) store_a32(As[s ^ 1]);
-    }
+    if (c + 1 < nk) store_a32(As[s ^ 1]);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
@@ -362,13 +357,10 @@ __global__ __launch_bounds__(64 * kGWaves) void layer_gemm_kernel(GemmArgs p) {
   epilogue<OUT>(p, acc, m0, f0, bi0, t0, wm, wf);
 }
 
-// Both operands bf16 (input projection, and the output projection inside the
-// layer): 256-token x 128-feature tiles, 8 waves in 4 x 2 (each 64 x 64, two
-// per SIMD, one workgroup per CU), three LDS stages (144 KB): chunk c+2 loads
-// while c is computed, so two chunks of loads are in flight per CU.  With
-// K = 512 a tile is only 8 chunks long, and the doubled tile and deeper
-// pipeline keep the matrix cores fed where the 128 x 128, two-stage tile
-// waits on its loads.
+// Both operands bf16, fewer than 256 output features: 256-token x
+// 128-feature tiles, 8 waves in 4 x 2 (each 64 x 64, two per SIMD, one
+// workgroup per CU), three LDS stages (144 KB): chunk c+2 loads while c is
+// computed, so two chunks of loads are in flight per CU.
 constexpr int kBT = 256;
 constexpr int kBWaves = 8;
 
@@ -585,7 +577,7 @@ hipError_t launch_gemm(GemmArgs p, bool out, bool a32, hipStream_t stream) {
   if (a32) {
     p.m_tiles = (int)((p.M + kGT - 1) / kGT);
     const dim3 grid((unsigned)((long long)p.m_tiles * p.f_tiles));
-    hipLaunchKernelGGL((layer_gemm_kernel<true, true>), grid, dim3(64 * kGWaves), 0, stream, p);
+    hipLaunchKernelGGL(layer_gemm_a32_kernel<true>, grid, dim3(64 * kGWaves), 0, stream, p);
     return hipGetLastError();
   }
   if (p.F >= kWT) {   // 256 x 256 tiles
