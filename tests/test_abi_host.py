@@ -41,7 +41,10 @@ def test_header_declares_and_library_exports_the_same_symbols():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.mosaic_bsa_abi_version() == 6
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mosaic_bsa.h")
+    with open(hdr) as f:
+        want = int(re.search(r"#define MOSAIC_BSA_ABI_VERSION (\d+)", f.read()).group(1))
+    assert L.mosaic_bsa_abi_version() == want
     for code, name in _lib.STATUS_NAMES.items():
         assert L.mosaic_status_string(code).decode() == name
     assert L.mosaic_status_string(99).decode() == "MOSAIC_ERR_UNKNOWN"
