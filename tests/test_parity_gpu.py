@@ -1,10 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle.
 
 Every case prints its name, shape and seed before it touches the GPU.
-Small workloads are compared element by element on every slice; the
-Nside = 128 and 256 workloads run in the bench's launch configuration
-(whole batch, one forward call) and are compared on all index rows of a
-sample of slices and on sampled output tokens.
+Small workloads are compared element by element on every slice.  The
+Nside = 64, 128 and 256 workloads run in the bench's launch configuration
+(whole batch, one forward call); every index row of every slice is checked,
+and every output element of all ns64 slices and of 8 seeded slices at
+ns128 and ns256 (the oracle runs in a pool of host processes).
 """
 
 from __future__ import annotations
@@ -18,7 +19,8 @@ from spherical_block_sparse_amd import CONFIGS, BSAConfig, make_inputs
 from spherical_block_sparse_amd import _lib
 from spherical_block_sparse_amd.synth import to_f64
 
-from parity import assert_close, check_indices, log, ocg_tolerance, selection_ref
+import oracle_jobs
+from parity import MAX_ABS, NEAR_TIE, REL_L2, assert_close, check_indices, log, ocg_tolerance, selection_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -215,56 +217,82 @@ def test_forward_all_slices(name):
     _full_compare(cfg, q, k, v, g, out, idx)
 
 
-def test_forward_ns64_indices_all_outputs_two_slices():
-    cfg = CONFIGS["ns64"]
-    q, k, v, g = _gpu_inputs(cfg)
-    out, idx = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
-    torch.cuda.synchronize()
-    near = 0
-    for b in range(cfg.batch):
-        for h in range(cfg.heads):
-            ref = selection_ref(_slice(q, b, h), _slice(k, b, h), _slice(v, b, h), cfg.block, cfg.topn)
-            near += check_indices(idx[b, h].cpu().numpy(), ref, cfg.topn)["near_ties"]
-    log(f"    indices: {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
-    _full_compare(cfg, q, k, v, g, out, idx, slices=[(0, 0), (cfg.batch - 1, cfg.heads - 1)])
+def _bits(x):
+    """Host copy of a bf16 device tensor as its uint16 bit patterns."""
+    return x.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _sampled_full_size(cfg: BSAConfig, n_slices=4, n_tokens=192):
+def _full_size(cfg: BSAConfig, n_out_slices=None):
+    """The workload in the bench's launch configuration (whole batch, one
+    forward call): every index row of every slice against the oracle's
+    selection, and every output element of ``n_out_slices`` seeded slices
+    (first and last included; all slices when None) against the oracle run
+    with the GPU's indices.  The oracle runs in a pool of host processes."""
     q, k, v, g = _gpu_inputs(cfg)
     need = _lib.mosaic_bsa_workspace_bytes(cfg.batch, cfg.heads, cfg.head_dim, cfg.nside, cfg.block, cfg.topn)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     out, idx = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window, workspace=ws)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
-    rng = np.random.default_rng(cfg.seed)
     S = cfg.slices
-    picks = sorted(set([0, S - 1] + list(rng.choice(S, n_slices - 2, replace=False))))
-    N, B = cfg.n_tokens, cfg.block
-    errs, refs = [], []
-    for sidx in picks:
-        b, h = divmod(int(sidx), cfg.heads)
-        qs, ks, vs, gs = _slice(q, b, h), _slice(k, b, h), _slice(v, b, h), _slice(g, b, h)
-        ref_sel = selection_ref(qs, ks, vs, B, cfg.topn)
-        gi = idx[b, h].cpu().numpy()
-        st = check_indices(gi, ref_sel, cfg.topn)
-        toks = np.unique(np.concatenate([np.arange(64), N - 64 + np.arange(64),
-                                         rng.choice(N, n_tokens, replace=False),
-                                         B * rng.choice(N // B, 8, replace=False)]))
-        r = oracle.bsa_rows_ref(qs, ks, vs, gs, B, cfg.topn, cfg.window, toks, idx=gi)
-        got = out[b, h].cpu().numpy()[toks]
-        assert_close(got, r["out"], f"slice ({b},{h}) {toks.size} tokens, {st['rows']} idx rows, "
-                                    f"{st['near_ties']} near-ties")
-        errs.append(got - r["out"])
-        refs.append(r["out"])
-    assert_close(np.concatenate(errs) + np.concatenate(refs), np.concatenate(refs), "all sampled tokens")
+    if n_out_slices is None or n_out_slices >= S:
+        out_slices = set(range(S))
+    else:
+        rng = np.random.default_rng(cfg.seed)
+        out_slices = {0, S - 1} | set(int(x) for x in rng.choice(np.arange(1, S - 1), n_out_slices - 2, replace=False))
+    log(f"    oracle on {oracle_jobs.workers()} host processes: {S} slices of index rows, "
+        f"{len(out_slices)} whole output slices {sorted(out_slices)}")
+    pending = []
+    with oracle_jobs.pool() as pool:
+        for sidx in range(S):
+            b, h = divmod(sidx, cfg.heads)
+            qb, kb, vb, gi = _bits(q[b, h]), _bits(k[b, h]), _bits(v[b, h]), idx[b, h].cpu().numpy()
+            pending.append(pool.apply_async(oracle_jobs.index_job,
+                                            ((b, h), qb, kb, vb, cfg.block, cfg.topn, gi)))
+            if sidx in out_slices:
+                pending.append(pool.apply_async(oracle_jobs.output_job,
+                                                ((b, h), qb, kb, vb, g[b, h].cpu().numpy(), cfg.block, cfg.topn,
+                                                 cfg.window, gi, out[b, h].cpu().numpy())))
+        del q, k, v, g, out
+        rows = near = n_out = 0
+        diff2 = ref2 = worst = 0.0
+        for i, res in enumerate(pending):
+            r = res.get()
+            if "ok" in r:
+                assert r["ok"], f"slice {r['tag']}: {r['msg']}"
+                rows += r["rows"]
+                near += r["near_ties"]
+            else:
+                assert r["finite"], f"slice {r['tag']}: non-finite output"
+                assert r["max_abs"] <= MAX_ABS and r["rel"] <= REL_L2, \
+                    f"slice {r['tag']}: max-abs {r['max_abs']:.3e} rel-L2 {r['rel']:.3e}"
+                n_out += 1
+                diff2 += r["diff2"]
+                ref2 += r["ref2"]
+                worst = max(worst, r["max_abs"])
+            if (i + 1) % 32 == 0 or i + 1 == len(pending):
+                log(f"    {i + 1}/{len(pending)} oracle jobs checked")
+    rel = (diff2 / ref2) ** 0.5
+    log(f"    indices: {rows} rows ({S} slices x {cfg.n_blocks}), all bit-exact except {near} near-tie rows "
+        f"(checked top-{cfg.topn} within {NEAR_TIE:g})")
+    log(f"    outputs: {n_out} whole slices, max-abs {worst:.3e}, rel-L2 over them {rel:.3e}")
+    assert rows == S * cfg.n_blocks and n_out == len(out_slices)
+    assert rel <= REL_L2
 
 
-def test_forward_ns128_full_size_sampled():
-    _sampled_full_size(CONFIGS["ns128"])
+def test_forward_ns64_every_slice():
+    """ns64: every index row and every output element of all 32 slices."""
+    _full_size(CONFIGS["ns64"])
 
 
-def test_forward_ns256_full_size_sampled():
-    _sampled_full_size(CONFIGS["ns256"])
+def test_forward_ns128_full_size():
+    """ns128 (the bench workload): every index row of the 192 slices, whole outputs of 8 slices."""
+    _full_size(CONFIGS["ns128"], n_out_slices=8)
+
+
+def test_forward_ns256_full_size():
+    """ns256: every index row of the 32 slices, whole outputs of 8 slices."""
+    _full_size(CONFIGS["ns256"], n_out_slices=8)
 
 
 # ------------------------------------------------------------- edge cases ---
