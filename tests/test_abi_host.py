@@ -2,7 +2,15 @@
 
 Only argument sets that the library rejects during validation are passed, so
 no call here reaches the HIP runtime (validation completes before any HIP
-call; the fake pointers below are never dereferenced).
+call; the fake pointers below are never dereferenced).  Every case that
+expects a shape or support error also carries a workspace (or saved state)
+that is too small, which validation checks later: should the shape become
+valid, the call still stops at MOSAIC_ERR_WORKSPACE (and the test fails)
+instead of launching kernels on the fake pointers.  Host-only by design: the
+module is skipped when a GPU is visible.
+
+MOSAIC_ABI_TEST_LIB, when set, names the library to load instead of the
+package's own (the host-only sanitizer build of tests/test_abi_sanitized.py).
 """
 
 import ctypes
@@ -17,7 +25,19 @@ from spherical_block_sparse_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mosaic_bsa.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmosaic_bsa.so not built")
+if os.environ.get("MOSAIC_ABI_TEST_LIB"):
+    _lib.LIB_PATH = os.environ["MOSAIC_ABI_TEST_LIB"]
+
+
+def _gpu_visible() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0   # counts devices without initialising one
+
+
+pytestmark = [
+    pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmosaic_bsa.so not built"),
+    pytest.mark.skipif(_gpu_visible(), reason="host-only checks with fake device pointers: not run where a GPU is visible"),
+]
 
 FAKE = 0x10000          # 256-byte aligned, never dereferenced
 OK, NULL, SHAPE, UNSUP, MISAL, WS, HIP = range(7)
@@ -65,10 +85,8 @@ def test_workspace_bytes_layout():
 
 
 def fwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=32, nside=8, block=16, topn=4,
-        window=32, out=FAKE, sel=FAKE, ws=FAKE, ws_bytes=None):
+        window=32, out=FAKE, sel=FAKE, ws=FAKE, ws_bytes=16):
     L = _lib.lib()
-    if ws_bytes is None:
-        ws_bytes = 1 << 40
     return L.mosaic_bsa_forward(q, k, v, gates, batch, heads, d, nside, block, topn, window, out, sel,
                                 ws, ws_bytes, None)
 
@@ -87,6 +105,8 @@ def fwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=32, nside=8, blo
     (dict(ws_bytes=100), WS),
 ])
 def test_forward_validation(kw, code):
+    # the default workspace (16 bytes) is too small for every shape: a case
+    # that validation let through would stop there, not launch
     assert fwd(**kw) == code
     assert _lib.lib().mosaic_last_error().decode() != ""
 
@@ -101,7 +121,7 @@ def test_stage_entry_points_validate():
     assert L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 4, None, FAKE, None) == NULL
     assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 32, 8, 16, 4, 0, FAKE, None) == SHAPE
     assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 32, 8, 16, 4, 32, FAKE, None) == NULL
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 64, 8, 4, 4, 32, FAKE, None) == UNSUP
+    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 48, 8, 16, 4, 32, FAKE, None) == UNSUP
     assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 2, 32, 8, 16, 4, 32, FAKE,
                              None) == MISAL
 
@@ -118,19 +138,15 @@ def test_python_binding_rejects_bad_tensors_without_launch():
 
 def bwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, sel=FAKE, dout=FAKE, batch=1, heads=2, d=64, nside=32, block=64,
         topn=16, window=256, saved=None, saved_bytes=0, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, ws=FAKE,
-        ws_bytes=None):
+        ws_bytes=16):
     L = _lib.lib()
-    if ws_bytes is None:
-        ws_bytes = 1 << 40
     return L.mosaic_bsa_backward(q, k, v, gates, sel, dout, batch, heads, d, nside, block, topn, window,
                                  saved, saved_bytes, dq, dk, dv, dg, ws, ws_bytes, None)
 
 
 def fwd_train(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=64, nside=32, block=64, topn=16,
-              window=256, out=FAKE, sel=FAKE, saved=FAKE, saved_bytes=None):
+              window=256, out=FAKE, sel=FAKE, saved=FAKE, saved_bytes=16):
     L = _lib.lib()
-    if saved_bytes is None:
-        saved_bytes = 1 << 40
     return L.mosaic_bsa_forward_train(q, k, v, gates, batch, heads, d, nside, block, topn, window, out, sel,
                                       saved, saved_bytes, None)
 
@@ -146,7 +162,7 @@ def fwd_train(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=64, nside=
     (dict(d=48), UNSUP),
     (dict(ws_bytes=1000), WS),
     (dict(saved=FAKE + 16, saved_bytes=1 << 40), MISAL),
-    (dict(saved=FAKE, saved_bytes=1000), WS),    # a saved state smaller than mosaic_bsa_saved_bytes
+    (dict(saved=FAKE, saved_bytes=1000, ws_bytes=1 << 40), WS),   # a saved state smaller than needed
 ])
 def test_backward_validation(kw, code):
     assert bwd(**kw) == code
@@ -188,10 +204,8 @@ def test_backward_workspace_bytes():
 
 
 def layer(x=FAKE, w_in=FAKE, w_out=FAKE, batch=1, heads=2, d=64, channels=128, nside=32, block=64, topn=16,
-          window=256, y=FAKE + 4096, sel=FAKE, ws=FAKE, ws_bytes=None):
+          window=256, y=FAKE + 4096, sel=FAKE, ws=FAKE, ws_bytes=16):
     L = _lib.lib()
-    if ws_bytes is None:
-        ws_bytes = 1 << 40
     return L.mosaic_bsa_layer_forward(x, w_in, w_out, batch, heads, d, channels, nside, block, topn, window,
                                       y, sel, ws, ws_bytes, None)
 
@@ -254,7 +268,7 @@ def test_interp_validation():
     f = L.mosaic_interp_attention
 
     def call(k=FAKE, v=FAKE, w=FAKE, nbr=FAKE, rel=FAKE, s=2, n_src=1000, n_dst=500, K=16, d=64, dv=64,
-             out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+             out=FAKE, ws=FAKE, ws_bytes=16):
         return f(k, v, w, nbr, rel, s, n_src, n_dst, K, d, dv, out, ws, ws_bytes, None)
     assert call(k=None) == NULL
     assert call(rel=None) == NULL
