@@ -5,12 +5,12 @@
 // returned as mosaic_status with a thread-local message.
 #include "mosaic_bsa.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
 #include <cstdio>
 
-#include "bsa_common.h"
+#include "bsa_launch.h"
 
 namespace {
 
@@ -418,10 +418,10 @@ mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const vo
   mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
   if (st != MOSAIC_OK) return st;
   if ((st = check_layer(s, heads, channels)) != MOSAIC_OK) return st;
+  if (x == y) return fail(MOSAIC_ERR_BAD_SHAPE, "y must not alias x");
   const LayerWorkspace lw = layer_layout(s);
   if (workspace_bytes < lw.total)
     return fail(MOSAIC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, lw.total);
-  if (x == y) return fail(MOSAIC_ERR_BAD_SHAPE, "y must not alias x");
   char* ws = static_cast<char*>(workspace);
   uint16_t* q = reinterpret_cast<uint16_t*>(ws + lw.q);
   uint16_t* k = reinterpret_cast<uint16_t*>(ws + lw.k);
