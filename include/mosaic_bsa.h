@@ -34,10 +34,14 @@
  *     launched, outputs are untouched, and the status is returned; the text
  *     of the last error of the calling thread is mosaic_last_error().
  *   - Supported: nside a power of two with N < 2^31; block = 4^k with
- *     16 <= block <= nside^2 (so a block never straddles two base pixels);
- *     1 <= topn <= min(m, 64); window >= 1; head_dim in {32, 64};
- *     batch, heads >= 1.  Blocks of 1 or 4 tokens and topn > 64 return
- *     MOSAIC_ERR_UNSUPPORTED.
+ *     1 <= block <= nside^2 (so a block never straddles two base pixels);
+ *     1 <= topn <= m; window >= 1; head_dim in {32, 64}; batch, heads >= 1;
+ *     batch*heads*N < 2^31 (and below 2^26 when block < 16 or topn > 64,
+ *     whose kernels run one wave per query).  Other head_dim values and
+ *     larger sizes return MOSAIC_ERR_UNSUPPORTED.  Blocks of at least 16
+ *     tokens with topn <= 64 take the tiled kernels; blocks of 1 or 4
+ *     tokens and larger topn take one-wave-per-row kernels (same results,
+ *     slower).
  *   - Alignment: q, k, v, out, o_cg, pooled buffers and sel_idx rows of 16
  *     bytes; gates 4 bytes; workspace 256 bytes.
  */
@@ -51,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 6
+#define MOSAIC_BSA_ABI_VERSION 7
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -248,8 +252,9 @@ size_t mosaic_bsa_backward_workspace_bytes(int batch, int heads, int head_dim, i
  * compressed branch and fine-branch statistics are recomputed.  bf16
  * products with float32 accumulation (dout is rounded to bf16 for the
  * products; D = dout·o uses it in float32).
- * Besides the forward's limits, block >= 64 and m = N/block a multiple of 64
- * and at most 16384 are needed (MOSAIC_ERR_UNSUPPORTED otherwise).
+ * Besides the forward's limits, block >= 64, topn <= 64 and m = N/block a
+ * multiple of 64 and at most 16384 are needed (MOSAIC_ERR_UNSUPPORTED
+ * otherwise).
  * Alignment: q, k, v, dout, dq, dk, dv 16 bytes; gates, sel_idx, dgates 4;
  * workspace and saved 256.  Errors as for the forward: nothing is launched
  * and the outputs are untouched. */

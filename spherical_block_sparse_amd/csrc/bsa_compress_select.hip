@@ -32,6 +32,8 @@
 //     same keys, so most positions are skipped.  The four lists are merged
 //     in registers (two bitonic merges across lanes 16 and 32 apart) and the
 //     n winners are sorted by block index.
+//   * any n > 64: compress_select_generic_kernel, one wave per row with an
+//     exact radix selection (below).
 //   * buffered kernel (16 < n <= 64): each row keeps
 //     its current n-th best key; logits that beat it are appended to an LDS
 //     candidate buffer at prefix-count slots, and a buffer that could
@@ -653,6 +655,141 @@ __global__ __launch_bounds__(256) void compress_select_buffered_kernel(CSArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Any top-n (used for n > 64): one wave per row, exact radix selection.
+//
+// The lane-list and buffered kernels above keep at most 64 candidates per
+// row.  This kernel selects any n <= m.  A wave owns one query-block row and
+// streams the slice's key blocks, lane l taking keys l, l+64, ...; every
+// pass recomputes the row's float64 logits (the same fused multiply-adds in
+// the same order each time, so every pass sees identical values):
+//   1. the row maximum;
+//   2. ā_ij = 2^((s_ij - max)·log2(e)/sqrt(d)) in float32 and
+//      o_CG_i = sum_j ā_ij v̄_j / sum_j ā_ij, lane l accumulating dimension l
+//      while each key's weight is broadcast from the lane that formed it;
+//   3. eight 8-bit radix passes over an order-preserving 64-bit image of the
+//      logits find the n-th largest value V exactly (a 256-bin LDS histogram
+//      per wave and pass) and how many of the keys equal to V belong to the
+//      top n;
+//   4. an ascending sweep writes every j with s_ij > V, and the lowest-index
+//      keys with s_ij = V, in ascending order (ballot prefix counts).
+// The logits are float64 dot products of the exact block means, ranked raw
+// (dividing by sqrt(d) is monotone), so the selection equals a float64
+// evaluation up to the summation order of the products; -0 is folded to +0
+// so that equal logits compare equal.  Cost: about 11 recomputations of the
+// row's m logits; this path serves shapes the fast kernels do not cover.
+__device__ __forceinline__ unsigned long long order_key(double s) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(s + 0.0);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double wave_max_f64(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void compress_select_generic_kernel(CSArgs a, long long rows) {
+  __shared__ __attribute__((aligned(16))) double Qs[4][D];
+  __shared__ unsigned Hist[4][256];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const long long grow = (long long)blockIdx.x * 4 + w;   // slice * m + row
+  if (grow >= rows) return;   // whole waves only; no workgroup barrier below
+  const int m = a.m, n = a.topn;
+  const long long slice = grow / m;
+  const double2* kb = reinterpret_cast<const double2*>(a.kbar + (size_t)slice * m * D);
+  const float* vb = a.vbar + (size_t)slice * m * D;
+  for (int d = lane; d < D; d += kWave) Qs[w][d] = a.qbar[(size_t)grow * D + d];
+  wave_sync_lds();
+  const double2* qs = reinterpret_cast<const double2*>(Qs[w]);
+  auto dot = [&](int j) __attribute__((always_inline)) -> double {
+    const double2* kr = kb + (size_t)j * (D / 2);
+    double s = 0.0;
+#pragma unroll 8
+    for (int e = 0; e < D / 2; ++e) {
+      const double2 kv = kr[e], qv = qs[e];
+      s = fma(qv.x, kv.x, s);
+      s = fma(qv.y, kv.y, s);
+    }
+    return s;
+  };
+
+  // 1. row maximum
+  double mx = -INFINITY;
+  for (int j = lane; j < m; j += kWave) mx = fmax(mx, dot(j));
+  mx = wave_max_f64(mx);
+
+  // 2. softmax weights and o_CG
+  float o = 0.f, lsum = 0.f;
+  for (int base = 0; base < m; base += kWave) {
+    const int j = base + lane;
+    const float p = j < m ? __builtin_amdgcn_exp2f((float)((dot(j) - mx) * a.c_exp2)) : 0.f;
+    lsum += p;
+    const int cnt = min(kWave, m - base);
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float pj = __shfl(p, jj);
+      if (lane < D) o = fmaf(pj, vb[(size_t)(base + jj) * D + lane], o);
+    }
+  }
+  lsum = wave_sum_f32(lsum);
+  if (lane < D) a.o_cg[(size_t)grow * D + lane] = o / lsum;
+
+  // 3. radix selection of the n-th largest key
+  unsigned long long prefix = 0, mask = 0;
+  int k = n;   // rank of the wanted key among the keys matching `prefix`
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int e = lane; e < 256; e += kWave) Hist[w][e] = 0u;
+    wave_sync_lds();
+    for (int j = lane; j < m; j += kWave) {
+      const unsigned long long kk = order_key(dot(j));
+      if ((kk & mask) == prefix) atomicAdd(&Hist[w][(kk >> shift) & 255], 1u);
+    }
+    wave_sync_lds();
+    int dd = 0, above = 0;
+    if (lane == 0) {
+      int acc = 0;
+      for (dd = 255; dd > 0; --dd) {
+        const int h = (int)Hist[w][dd];
+        if (acc + h >= k) break;
+        acc += h;
+      }
+      above = acc;
+    }
+    dd = __shfl(dd, 0);
+    above = __shfl(above, 0);
+    prefix |= (unsigned long long)dd << shift;
+    mask |= 0xFFull << shift;
+    k -= above;
+    wave_sync_lds();
+  }
+
+  // 4. ascending sweep: keys above the n-th value, then the k lowest-index
+  // keys equal to it
+  int32_t* out = a.sel + (size_t)grow * n;
+  int taken = 0, eq_seen = 0;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < m; base += kWave) {
+    const int j = base + lane;
+    const unsigned long long kk = j < m ? order_key(dot(j)) : 0ull;
+    const bool gt = j < m && kk > prefix;
+    const bool eq = j < m && kk == prefix;
+    const unsigned long long eqm = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + __popcll(eqm & below) < k);
+    const unsigned long long tm = __ballot(take);
+    const int pos = taken + __popcll(tm & below);
+    if (take && pos < n) out[pos] = j;   // exactly n are taken; the bound only guards the buffer
+    taken += __popcll(tm);
+    eq_seen += __popcll(eqm);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_compress_select(const double* qbar, const double* kbar, const float* vbar,
@@ -669,6 +806,15 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
   a.row_tiles = (m + 63) / 64;
   a.c_exp2 = 1.4426950408889634 / sqrt((double)head_dim);
   const dim3 grid((unsigned)(slices * a.row_tiles));
+  if (topn > 64) {   // beyond the candidate capacity of the fast kernels
+    const long long rows = slices * (long long)m;
+    const dim3 ggrid((unsigned)((rows + 3) / 4));
+    if (head_dim == 64)
+      hipLaunchKernelGGL(compress_select_generic_kernel<64>, ggrid, dim3(256), 0, stream, a, rows);
+    else
+      hipLaunchKernelGGL(compress_select_generic_kernel<32>, ggrid, dim3(256), 0, stream, a, rows);
+    return hipGetLastError();
+  }
   if (head_dim == 64) {
     if (topn <= 8) hipLaunchKernelGGL((compress_select_list_kernel<64, 8>), grid, dim3(256), 0, stream, a);
     else if (topn <= 16) hipLaunchKernelGGL((compress_select_list_kernel<64, 16>), grid, dim3(256), 0, stream, a);

@@ -91,6 +91,9 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 
 constexpr float kLazy = 8.0f;
+// entries of the tiled kernel's LDS table of selection rows (T/block rows of
+// topn, one row when block >= T); larger selections take the generic kernel
+constexpr int kSelTable = 256;
 // Largest score bound M (log2 units) for which the running maximum is
 // skipped.  The best key's weight is then at least 2^-2M = 2^-96: it, the
 // denominator and its products with v elements above 2^-30 stay normal
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   uint16_t* const Vb0 = KVb + 64 * D;
   uint16_t* const Kb1 = KVb + 2 * 64 * D;
   uint16_t* const Vb1 = KVb + 3 * 64 * D;
-  __shared__ int SelT[4 * 64];   // selection rows of the tile's query blocks (<= T/16 rows of <= 64)
+  __shared__ int SelT[kSelTable];   // selection rows of the tile's query blocks
 
   // contiguous run of tiles per XCD (workgroups are dispatched round-robin)
   long long logical;
@@ -661,6 +664,145 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   }
 }
 
+// ---------------------------------------------------------------------------
+// Any block size and top-n: one wave per query.
+//
+// The tiled kernel above needs blocks of at least 16 tokens (a 16-query
+// sub-tile then lies inside one query block) and a tile's selection rows
+// within its 256-entry LDS table.  This kernel covers every other shape
+// (blocks of 1 or 4 tokens, or more selected blocks than the table holds).
+// A wave owns one query t.  Each branch streams its key list 64 keys at a
+// time: lane l forms the float32 score of key l of the group (the query in
+// LDS, the key row read whole), the wave takes the group maximum and
+// rescales its running sums, and lane d accumulates output dimension d
+// while each key's weight and token are broadcast from the lane that formed
+// them.  Weights stay float32 (no bf16 rounding).  The selected branch's
+// keys are the tokens of the blocks sel[t / block] in listed order, the
+// local branch's the clipped centred window; the epilogue is the gated sum
+// (and, as in the tiled kernel, the SAVE and MERGED outputs).
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void fine_generic_kernel(FineArgs a) {
+  __shared__ float Qs[4][D];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const long long gq = (long long)blockIdx.x * 4 + w;   // slice * N + t
+  if (gq >= a.groups) return;   // whole waves only; no workgroup barrier below
+  const int N = a.n_tok, B = a.block, n = a.topn, m = a.m;
+  const long long slice = gq / N;
+  const int t = (int)(gq % N);
+  const int lb = 31 - __builtin_clz(B);
+  const uint16_t* ks = a.k + (size_t)slice * N * D;
+  const uint16_t* vs = a.v + (size_t)slice * N * D;
+  if (lane < D) Qs[w][lane] = bf16_to_f32(a.q[(size_t)gq * D + lane]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float c = a.scale_log2;
+
+  struct Acc {
+    float o, l, m;   // lane's output dimension, lane's share of the denominator, running max (log2 units)
+  };
+  // one branch over `count` keys, key v of the list being token tok(v)
+  auto attend = [&](int count, auto tok) __attribute__((always_inline)) -> Acc {
+    Acc r{0.f, 0.f, -INFINITY};
+    for (int base = 0; base < count; base += kWave) {
+      const int v = base + lane;
+      const int u = v < count ? tok(v) : -1;
+      float sc = -INFINITY;
+      if (u >= 0) {
+        const uint4* kr = reinterpret_cast<const uint4*>(ks + (size_t)u * D);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < D / 8; ++e) {
+          const uint4 x = kr[e];
+          const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            acc = fmaf(Qs[w][8 * e + 2 * h], __uint_as_float(xs[h] << 16), acc);
+            acc = fmaf(Qs[w][8 * e + 2 * h + 1], __uint_as_float(xs[h] & 0xffff0000u), acc);
+          }
+        }
+        sc = acc * c;
+      }
+      const float mn = fmaxf(r.m, wave_max_f32(sc));   // finite: the group's first key is valid
+      const float alpha = __builtin_amdgcn_exp2f(r.m - mn);   // 0 while r.m = -inf
+      r.o *= alpha;
+      r.l *= alpha;
+      r.m = mn;
+      const float p = u >= 0 ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
+      r.l += p;
+      const int cnt = min(kWave, count - base);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const float pj = __shfl(p, jj);
+        const int uj = __shfl(u, jj);
+        if (lane < D) r.o = fmaf(pj, bf16_to_f32(vs[(size_t)uj * D + lane]), r.o);
+      }
+    }
+    r.l = wave_sum_f32(r.l);
+    return r;
+  };
+
+  const int blk = t >> lb;
+  const int32_t* selrow = a.sel + ((size_t)slice * m + blk) * n;
+  const Acc fg = attend(n << lb, [&](int v) __attribute__((always_inline)) {
+    int j = selrow[v >> lb];
+    j = j < 0 ? 0 : (j >= m ? m - 1 : j);   // a bad index never addresses outside the slice
+    return (j << lb) + (v & (B - 1));
+  });
+  const int lo = max(0, t - a.window / 2);
+  const int hi = (int)min((long long)N, (long long)t + (a.window - a.window / 2));
+  const Acc lc = attend(hi - lo, [&](int v) __attribute__((always_inline)) { return lo + v; });
+
+  const size_t row = (size_t)gq;
+  if constexpr (MODE == kSave) {
+    if (lane < D) {
+      a.save_o[(row * 2 + 0) * D + lane] = fg.o / fg.l;
+      a.save_o[(row * 2 + 1) * D + lane] = lc.o / lc.l;
+    }
+    if (lane == 0) {
+      a.save_lse[row * 2 + 0] = fg.m + log2f(fg.l);
+      a.save_lse[row * 2 + 1] = lc.m + log2f(lc.l);
+    }
+  }
+  if (lane < D) {
+    const float* g = a.gates + row * 3;
+    const float r = g[0] * a.o_cg[((size_t)slice * m + blk) * D + lane] + g[1] * (fg.o / fg.l) +
+                    g[2] * (lc.o / lc.l);
+    if constexpr (MODE == kMerged) {
+      const long long bi = slice / a.heads, h = slice % a.heads;
+      a.out_merged[(((size_t)bi * N + t) * a.heads + h) * D + lane] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));
+    } else {
+      a.out[row * D + lane] = r;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_generic(FineArgs a, long long slices, hipStream_t stream) {
+  a.groups = slices * a.n_tok;   // queries, four per workgroup
+  const dim3 grid((unsigned)((a.groups + 3) / 4));
+  if (a.save_o)
+    hipLaunchKernelGGL((fine_generic_kernel<D, kSave>), grid, dim3(256), 0, stream, a);
+  else if (a.out_merged)
+    hipLaunchKernelGGL((fine_generic_kernel<D, kMerged>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fine_generic_kernel<D, kPlain>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 // One workgroup per tile of 32*WAVES queries of every slice: the tile size
 // fixes the tile count and the grid together.
 template <int D, int WAVES>
@@ -706,6 +848,12 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   // 128-query tiles when a block holds >= 128 tokens (N is then a multiple of
   // 128), else 64 (N = 12*nside^2 with nside^2 >= block >= 16 is a multiple of 64)
   const bool wide = block >= 128 && n_tok % 128 == 0;
+  // the tiled kernel's selection table holds kSelTable entries: the rows of
+  // the tile's T/block query blocks (one row when block >= T)
+  const int tile = wide ? 128 : 64;
+  const long long table = (long long)(block >= tile ? 1 : tile / block) * topn;
+  if (block < 16 || table > kSelTable)
+    return head_dim == 64 ? launch_generic<64>(a, slices, stream) : launch_generic<32>(a, slices, stream);
   if (head_dim == 64) return wide ? launch<64, 4>(a, slices, stream) : launch<64, 2>(a, slices, stream);
   return wide ? launch<32, 4>(a, slices, stream) : launch<32, 2>(a, slices, stream);
 }

@@ -12,7 +12,8 @@
 // 256-thread workgroup streams 256/(D/8) blocks side by side, every lane
 // walking its 16-byte column slice down all rows of its block.  Each wave
 // instruction touches 64/(D/8) full 128-byte (D=64) row segments; no
-// cross-lane reduction is needed.  Sums are float64: exact for bf16 inputs
+// cross-lane reduction is needed.  A sweep step loads 8 rows; blocks of 1 or
+// 4 tokens take one row per step.  Sums are float64: exact for bf16 inputs
 // (8-bit significands, at most a few thousand terms), and block = 4^k makes
 // the final scaling exact.  HBM-bound: 6*D bytes read per token.
 //
@@ -104,10 +105,41 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
       if (c == 0) a.knorm[gb] = sqrtf(nmax);
     }
   };
-  if (tensor == 1 && a.knorm)
+  // blocks of 1 or 4 tokens (fewer than the 8 rows a sweep step loads): one
+  // row per step, each row's |k|^2 summed over its TPR lanes
+  auto sweep_small = [&](auto NORM) __attribute__((always_inline)) {
+    float nmax = 0.f;
+    for (int r = 0; r < a.block; ++r) {
+      const u32x4 w = __builtin_nontemporal_load(p + (size_t)r * TPR);
+      const uint32_t x[4] = {w[0], w[1], w[2], w[3]};
+      float ss = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float lo = __uint_as_float(x[h] << 16), hi = __uint_as_float(x[h] & 0xffff0000u);
+        acc[2 * h] += (double)lo;
+        acc[2 * h + 1] += (double)hi;
+        if constexpr (decltype(NORM)::value) ss = fmaf(hi, hi, fmaf(lo, lo, ss));
+      }
+      if constexpr (decltype(NORM)::value) {
+#pragma unroll
+        for (int off = 1; off < TPR; off *= 2) ss += __shfl_xor(ss, off);
+        nmax = fmaxf(nmax, ss);
+      }
+    }
+    if constexpr (decltype(NORM)::value) {
+      if (c == 0) a.knorm[gb] = sqrtf(nmax);
+    }
+  };
+  if (a.block < 8) {
+    if (tensor == 1 && a.knorm)
+      sweep_small(std::true_type{});
+    else
+      sweep_small(std::false_type{});
+  } else if (tensor == 1 && a.knorm) {
     sweep(std::true_type{});
-  else
+  } else {
     sweep(std::false_type{});
+  }
 
   const size_t o = (size_t)gb * D + c * 8;
   if (tensor < 2) {

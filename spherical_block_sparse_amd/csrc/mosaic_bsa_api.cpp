@@ -57,18 +57,22 @@ mosaic_status check_shape(int batch, int heads, int head_dim, int nside, int blo
   if ((long long)block > (long long)nside * nside)
     return fail(MOSAIC_ERR_BAD_SHAPE, "block (%d) must be <= nside^2 (%lld) so it is one coarse pixel", block,
                 (long long)nside * nside);
-  if (block < 16) return fail(MOSAIC_ERR_UNSUPPORTED, "block %d: the kernels need block >= 16", block);
   const long long m = n_tok / block;
-  if (uses & kUsesTopn) {
-    if (topn < 1 || topn > m) return fail(MOSAIC_ERR_BAD_SHAPE, "topn (%d) must lie in [1, m=%lld]", topn, m);
-    if (topn > 64) return fail(MOSAIC_ERR_UNSUPPORTED, "topn %d: the selection keeps at most 64 blocks", topn);
-  }
+  if ((uses & kUsesTopn) && (topn < 1 || topn > m))
+    return fail(MOSAIC_ERR_BAD_SHAPE, "topn (%d) must lie in [1, m=%lld]", topn, m);
   if ((uses & kUsesWindow) && window < 1) return fail(MOSAIC_ERR_BAD_SHAPE, "window (%d) must be >= 1", window);
   if (head_dim != 32 && head_dim != 64)
     return fail(MOSAIC_ERR_UNSUPPORTED, "head_dim %d: supported head_dim is 32 or 64", head_dim);
   const long long slices = (long long)batch * heads;
-  // one-dimensional grids: the largest is the pooling grid, 3 * slices*m/(256/(d/8)) groups of 256 lanes
-  if (slices * (n_tok / 64) > 0x7fffffffLL || slices * m * 3 * 8 > 0x7fffffffLL)
+  // One-dimensional grids whose work-item count must fit in 32 bits: the
+  // tiled fine kernel launches 2 work-items per token, the selection 4 per
+  // block and the pooling 24 per block; the one-wave kernels for blocks of
+  // 1 or 4 tokens or top-n above 64 launch 64 per query (fine) or per
+  // query block (selection).
+  const bool big_topn = (uses & kUsesTopn) && topn > 64;
+  long long items = 24 * slices * m;
+  if (block < 16 || big_topn) items = 64 * slices * n_tok;
+  if (slices * n_tok > 0x7fffffffLL || items > 0xffffffffLL)
     return fail(MOSAIC_ERR_UNSUPPORTED, "batch*heads*N too large for one launch");
   s->slices = slices;
   s->n_tok = (int)n_tok;
@@ -153,6 +157,7 @@ BwdWorkspace bwd_layout(const Shape& s) {
 // what the backward kernels implement beyond the forward's own limits
 mosaic_status check_backward_shape(const Shape& s) {
   if (s.block < 64) return fail(MOSAIC_ERR_UNSUPPORTED, "backward: block %d, the kernels need block >= 64", s.block);
+  if (s.topn > 64) return fail(MOSAIC_ERR_UNSUPPORTED, "backward: topn %d, the kernels take at most 64", s.topn);
   if (s.m % 64) return fail(MOSAIC_ERR_UNSUPPORTED, "backward: m = N/block = %d must be a multiple of 64", s.m);
   if (s.m > mosaic::kIndexMaxBlocks)
     return fail(MOSAIC_ERR_UNSUPPORTED, "backward: m = N/block = %d, at most %d blocks", s.m, mosaic::kIndexMaxBlocks);

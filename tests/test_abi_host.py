@@ -100,8 +100,11 @@ def fwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=32, nside=8, blo
     (dict(nside=3), SHAPE), (dict(nside=0), SHAPE),
     (dict(block=8), SHAPE), (dict(block=32), SHAPE), (dict(block=256), SHAPE),   # 256 > nside^2 = 64
     (dict(topn=0), SHAPE), (dict(topn=49), SHAPE), (dict(window=0), SHAPE),
-    (dict(block=4), UNSUP), (dict(block=1), UNSUP), (dict(d=48), UNSUP), (dict(d=128), UNSUP),
-    (dict(nside=16, block=16, topn=65), UNSUP), (dict(nside=16384), UNSUP),
+    (dict(d=48), UNSUP), (dict(d=128), UNSUP), (dict(nside=16384), UNSUP),
+    (dict(nside=4096, block=1, heads=1), UNSUP),    # 2^26 queries: too many for the one-wave-per-query kernel
+    (dict(nside=4096, block=16, heads=85), UNSUP),  # batch*heads*N >= 2^31
+    # valid shapes that only the too-small workspace stops (blocks of 1 and 4, top-n above 64)
+    (dict(block=4), WS), (dict(block=1), WS), (dict(nside=16, block=16, topn=65), WS), (dict(topn=48), WS),
     (dict(ws_bytes=100), WS),
 ])
 def test_forward_validation(kw, code):
@@ -158,6 +161,7 @@ def fwd_train(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, batch=1, heads=2, d=64, nside=
     (dict(ws=FAKE + 16), MISAL),
     (dict(batch=0), SHAPE), (dict(topn=0), SHAPE), (dict(window=0), SHAPE), (dict(block=32), SHAPE),
     (dict(block=16), UNSUP),                     # backward needs block >= 64
+    (dict(topn=65), UNSUP),                      # and topn <= 64
     (dict(nside=16, block=64), UNSUP),           # m = 48, not a multiple of 64
     (dict(d=48), UNSUP),
     (dict(ws_bytes=1000), WS),

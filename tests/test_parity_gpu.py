@@ -406,3 +406,117 @@ def test_forward_equals_stages():
     out2 = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
     torch.cuda.synchronize()
     assert torch.equal(idx, sel) and torch.equal(out, out2)
+
+
+# ------------------------------- blocks of 1 and 4 tokens, top-n above 64 ---
+# These shapes run the one-wave-per-row kernels (generic selection when
+# topn > 64, generic fine attention when block < 16 or the tiled kernel's
+# selection table would overflow) and the pool's one-row sweep.
+
+B1 = CONFIGS["tiny"].with_(name="tiny-b1", block=1, seed=81)
+B4 = CONFIGS["tiny"].with_(name="tiny-b4", block=4, seed=84)
+
+
+@pytest.mark.parametrize("cfg", [B1, B4], ids=lambda c: c.name)
+def test_pool_small_blocks_bit_exact_and_key_norms(cfg):
+    q, k, v, _ = _gpu_inputs(cfg)
+    knorm = _knorm(cfg)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
+    torch.cuda.synchronize()
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            np.testing.assert_array_equal(qbar[b, h].cpu().numpy(), oracle.pool_mean(_slice(q, b, h), cfg.block))
+            np.testing.assert_array_equal(kbar[b, h].cpu().numpy(), oracle.pool_mean(_slice(k, b, h), cfg.block))
+            np.testing.assert_array_equal(vbar[b, h].cpu().numpy(),
+                                          oracle.pool_mean(_slice(v, b, h), cfg.block).astype(np.float32))
+    want = k.double().cpu().norm(dim=-1).reshape(cfg.batch, cfg.heads, cfg.n_blocks, -1).amax(-1)
+    assert torch.all((knorm.double().cpu() - want).abs() <= 1e-5 * want)
+
+
+def test_block_one_compressed_branch_is_dense_attention():
+    """Blocks of one token: q̄, k̄, v̄ are q, k, v, so o_CG is dense softmax
+    attention over the whole sphere (torch float64 here, independent of the
+    oracle); then the whole forward against the oracle."""
+    cfg = B1
+    q, k, v, g = _gpu_inputs(cfg)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
+    o_cg, _ = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
+    torch.cuda.synchronize()
+    qd, kd, vd = (x.double().cpu() for x in (q, k, v))
+    dense = torch.softmax(qd @ kd.transpose(-1, -2) / cfg.head_dim ** 0.5, dim=-1) @ vd
+    tol = ocg_tolerance(vd.numpy())
+    err = float((o_cg.double().cpu() - dense).abs().max())
+    log(f"    o_CG vs dense attention: max-abs {err:.3e} (bound {tol:.3e})")
+    assert err <= tol
+    _edge(cfg)
+
+
+def test_block_four_forward():
+    _edge(B4)
+
+
+def test_block_four_forward_save_state():
+    """mosaic_bsa_forward_train on blocks of 4 (generic fine kernel, SAVE
+    outputs): the same out and selection as the forward, and the saved
+    normalised branch outputs against the oracle's branches."""
+    cfg = B4
+    q, k, v, g = _gpu_inputs(cfg)
+    out0, sel0 = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    out, sel, saved = _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel0)
+    assert float((out - out0).abs().max()) <= 1e-6 * float(out0.abs().max())
+    S, N, d = cfg.slices, cfg.n_tokens, cfg.head_dim
+    o = saved[:S * N * 2 * d * 4].view(torch.float32).view(cfg.batch, cfg.heads, N, 2, d)
+    for h in range(cfg.heads):
+        qs, ks, vs = _slice(q, 0, h), _slice(k, 0, h), _slice(v, 0, h)
+        gi = sel[0, h].cpu().numpy()
+        assert_close(o[0, h, :, 0].cpu().numpy(), oracle.fine_selected_branch(qs, ks, vs, gi, cfg.block), f"o_FG[{h}]")
+        assert_close(o[0, h, :, 1].cpu().numpy(), oracle.local_branch(qs, ks, vs, cfg.window), f"o_L[{h}]")
+
+
+def test_topn_all_blocks_ns32():
+    """top-n = m = 192 (the exact radix selection): every row selects every
+    block, and the selected branch is dense attention."""
+    cfg, *_, idx = _edge(CONFIGS["ns32"].with_(name="ns32-all", heads=2), topn=192)
+    assert torch.equal(idx.cpu(), torch.arange(192, dtype=torch.int32).expand(1, 2, 192, 192))
+
+
+@pytest.mark.parametrize("topn", [65, 100, 191])
+def test_compress_select_stage_any_topn(topn):
+    cfg = CONFIGS["ns32"]
+    q, k, v, _ = _gpu_inputs(cfg)
+    near = _check_compress_select(cfg, q, k, v, topn=topn)
+    log(f"    topn {topn}: {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
+
+
+# nside 16, blocks of 16 (m = 192): top-100 overflows the tiled kernel's selection table
+N16 = BSAConfig("n16-b16-top100", 16, 1, 3, 64, 16, 100, 64, "iid", 161)
+
+
+def test_topn_above_the_tile_table():
+    _edge(N16)
+
+
+def test_topn_above_64_exact_ties():
+    """Block-constant inputs with repeated key blocks: exact ties in the
+    radix selection go to the lower block index."""
+    def mutate(q, k, v):
+        rep = lambda x: x[:, :, ::16].repeat_interleave(16, dim=2).contiguous()
+        kk = rep(k)
+        kk[:, :, 16 * 20:16 * 60] = kk[:, :, 0:16].repeat(1, 1, 40, 1)   # forty copies of block 0
+        return rep(q), kk, rep(v)
+    _edge(N16.with_(name="n16-top100-ties"), mutate=mutate)
+
+
+def test_block_four_top80_ns32():
+    """Blocks of 4 on the Nside-32 mesh (m = 3072), top-80: the radix
+    selection over 3072 keys per row and the generic fine kernel."""
+    _edge(CONFIGS["ns32"].with_(name="ns32-b4-top80", block=4, topn=80, heads=2, seed=324))
+
+
+def test_block_one_ns32_one_head():
+    """Blocks of one token on the Nside-32 mesh: m = N = 12288 rows in the
+    lane-list selection, the generic fine kernel on 16 single-token blocks
+    plus the window."""
+    _edge(CONFIGS["ns32"].with_(name="ns32-b1", block=1, heads=1, seed=321))
