@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 7
+#define MOSAIC_BSA_ABI_VERSION 8
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -94,6 +94,24 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
                                  int batch, int heads, int head_dim, int nside, int block, int topn,
                                  int window, float* out, int32_t* sel_idx, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* mosaic_bsa_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a static
+ * device array of 256 MiB inside the library: each GPU the library runs
+ * this on holds its own copy until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its
+ * first call on a device looks up that device's copy.  Sizes whose
+ * workspace (mosaic_bsa_workspace_bytes) exceeds 256 MiB return
+ * MOSAIC_ERR_UNSUPPORTED before any HIP call: e.g. batch 2 x 16 heads at
+ * nside 256 (152 MB) fit, batch 24 x 8 heads at nside 128 (1.06 GB) do
+ * not.  Every call on one GPU shares that GPU's scratch, which keeps the
+ * last call's contents: calls that overlap on one GPU (other streams or
+ * threads without ordering between them) race.  Arguments, outputs and
+ * errors otherwise as for mosaic_bsa_forward. */
+mosaic_status mosaic_bsa_forward_noalloc(const void* q, const void* k, const void* v, const float* gates,
+                                         int batch, int heads, int head_dim, int nside, int block, int topn,
+                                         int window, float* out, int32_t* sel_idx, void* stream);
 
 /* Pooling only: q̄, k̄ (float64) and v̄ (float32), [batch][heads][m][head_dim],
  * the mean of each block's `block` consecutive NESTED tokens (the block

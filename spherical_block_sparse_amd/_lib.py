@@ -26,7 +26,7 @@ STATUS_NAMES = {
 
 EXPORTED = (
     "mosaic_bsa_abi_version", "mosaic_status_string", "mosaic_last_error",
-    "mosaic_bsa_workspace_bytes", "mosaic_bsa_forward", "mosaic_bsa_pool",
+    "mosaic_bsa_workspace_bytes", "mosaic_bsa_forward", "mosaic_bsa_forward_noalloc", "mosaic_bsa_pool",
     "mosaic_bsa_compress_select", "mosaic_bsa_fine",
     "mosaic_bsa_saved_bytes", "mosaic_bsa_forward_train",
     "mosaic_bsa_layer_workspace_bytes", "mosaic_bsa_layer_forward", "mosaic_bsa_layer_in", "mosaic_bsa_layer_out",
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.mosaic_bsa_forward.restype = I
         L.mosaic_bsa_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, P, S, P]
+        L.mosaic_bsa_forward_noalloc.restype = I
+        L.mosaic_bsa_forward_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, P]
         L.mosaic_bsa_pool.restype = I
         L.mosaic_bsa_pool.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P]
         L.mosaic_bsa_compress_select.restype = I
@@ -166,6 +168,24 @@ def mosaic_bsa_forward(q, k, v, gates, nside, block, topn, window, out=None, sel
         _ptr(out, torch.float32, (b, h, n, d), "out"),
         _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, sel_idx
+
+
+def mosaic_bsa_forward_noalloc(q, k, v, gates, nside, block, topn, window, out=None, sel_idx=None, stream=None):
+    """mosaic_bsa_forward with the library's static device scratch as the workspace (the C entry point
+    allocates nothing; out and sel_idx are allocated here only when not given)."""
+    b, h, n, d = _dims(q, nside)
+    m = n // block
+    if out is None:
+        out = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((b, h, m, topn), dtype=torch.int32, device=q.device)
+    _check(lib().mosaic_bsa_forward_noalloc(
+        _ptr(q, torch.bfloat16, (b, h, n, d), "q"), _ptr(k, torch.bfloat16, (b, h, n, d), "k"),
+        _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
+        b, h, d, nside, block, topn, window,
+        _ptr(out, torch.float32, (b, h, n, d), "out"),
+        _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"), _stream(stream)))
     return out, sel_idx
 
 

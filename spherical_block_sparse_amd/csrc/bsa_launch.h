@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime_api.h>
 #include <hip/hip_vector_types.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace mosaic {
@@ -98,6 +99,12 @@ hipError_t launch_coarsen(const uint16_t* x, float* y, long long batch, int n_to
 hipError_t launch_interp(const uint16_t* k, const uint16_t* v, const float* w_q, const int32_t* nbr,
                          const float* rel, long long slices, int n_src, int n_dst, int n_nbr, int d, float* out,
                          float4* kappa, hipStream_t stream);
+
+// Bytes of the static device scratch that mosaic_bsa_forward_noalloc uses as
+// its workspace (bsa_scratch.hip), and the current device's address of it
+// (looked up once per device).
+constexpr size_t kScratchBytes = size_t(256) << 20;
+hipError_t scratch_buffer(void** ptr);
 
 // largest m = N/block the backward's inverted-selection kernel holds in LDS
 constexpr int kIndexMaxBlocks = 16384;

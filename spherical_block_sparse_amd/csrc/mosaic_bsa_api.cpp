@@ -200,6 +200,28 @@ LayerWorkspace layer_layout(const Shape& s) {
 }
 
 
+// The forward's three launches on a validated shape, with the workspace at ws
+// (layout(s).total bytes, 256-byte aligned).
+mosaic_status run_forward(const Shape& s, const void* q, const void* k, const void* v, const float* gates,
+                          float* out, int32_t* sel_idx, char* ws, hipStream_t hs) {
+  const Workspace w = layout(s);
+  double* qbar = reinterpret_cast<double*>(ws + w.qbar);
+  double* kbar = reinterpret_cast<double*>(ws + w.kbar);
+  float* vbar = reinterpret_cast<float*>(ws + w.vbar);
+  float* ocg = reinterpret_cast<float*>(ws + w.ocg);
+  float* knorm = reinterpret_cast<float*>(ws + w.knorm);
+  hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
+                                     s.d, s.block, hs, knorm);
+  if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
+  if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
+                          s.block, s.topn, s.window, hs, knorm);
+  return hip_status(e, "bsa_fine launch");
+}
+
 #define REQUIRE_PTR(p) \
   if (!(p)) return fail(MOSAIC_ERR_NULL_POINTER, "%s is NULL", #p)
 #define REQUIRE_ALIGN(p, a) \
@@ -294,23 +316,27 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
   const Workspace w = layout(s);
   if (workspace_bytes < w.total)
     return fail(MOSAIC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, w.total);
-  char* ws = static_cast<char*>(workspace);
-  double* qbar = reinterpret_cast<double*>(ws + w.qbar);
-  double* kbar = reinterpret_cast<double*>(ws + w.kbar);
-  float* vbar = reinterpret_cast<float*>(ws + w.vbar);
-  float* ocg = reinterpret_cast<float*>(ws + w.ocg);
-  float* knorm = reinterpret_cast<float*>(ws + w.knorm);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                     static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
-                                     s.d, s.block, hs, knorm);
-  if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
-  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
-  if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
-  e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                          static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
-                          s.block, s.topn, s.window, hs, knorm);
-  return hip_status(e, "bsa_fine launch");
+  return run_forward(s, q, k, v, gates, out, sel_idx, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+mosaic_status mosaic_bsa_forward_noalloc(const void* q, const void* k, const void* v, const float* gates,
+                                         int batch, int heads, int head_dim, int nside, int block, int topn,
+                                         int window, float* out, int32_t* sel_idx, void* stream) {
+  REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(out); REQUIRE_PTR(sel_idx);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
+  REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(sel_idx, 4);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
+  if (st != MOSAIC_OK) return st;
+  const Workspace w = layout(s);
+  if (w.total > mosaic::kScratchBytes)
+    return fail(MOSAIC_ERR_UNSUPPORTED,
+                "these sizes need %zu bytes of workspace; the static scratch holds %zu (use mosaic_bsa_forward)",
+                w.total, mosaic::kScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = mosaic::scratch_buffer(&ws);
+  if (e != hipSuccess) return hip_status(e, "static scratch lookup");
+  return run_forward(s, q, k, v, gates, out, sel_idx, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -50,5 +50,6 @@ hipError_t launch_interp(const uint16_t*, const uint16_t*, const float*, const i
   return reached();
 }
 hipError_t launch_backward(const BwdLaunch&, hipStream_t) { return reached(); }
+hipError_t scratch_buffer(void**) { return reached(); }
 
 }  // namespace mosaic

@@ -289,3 +289,24 @@ def test_interp_validation():
     assert call(ws_bytes=100) == WS
     assert L.mosaic_interp_workspace_bytes(2, 1000) >= 2 * 1000 * 16
     assert L.mosaic_interp_workspace_bytes(0, 1000) == 0
+
+
+def test_forward_noalloc_validation():
+    L = _lib.lib()
+
+    def call(q=FAKE, gates=FAKE, batch=1, heads=2, d=32, nside=8, block=16, topn=4, window=32, out=FAKE, sel=FAKE):
+        return L.mosaic_bsa_forward_noalloc(q, FAKE, FAKE, gates, batch, heads, d, nside, block, topn, window,
+                                            out, sel, None)
+    assert call(q=None) == NULL
+    assert call(sel=None) == NULL
+    assert call(out=FAKE + 4) == MISAL
+    assert call(gates=FAKE + 2) == MISAL
+    assert call(topn=0) == SHAPE
+    assert call(block=8) == SHAPE
+    assert call(d=48) == UNSUP
+    # a valid shape whose workspace exceeds the 256 MiB static scratch: rejected before any HIP call
+    # (batch 24 x 8 heads at nside 128 needs 1.06 GB)
+    assert call(batch=24, heads=8, d=64, nside=128, block=64, topn=16, window=512) == UNSUP
+    assert "static scratch" in L.mosaic_last_error().decode()
+    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) > 256 << 20
+    assert L.mosaic_bsa_workspace_bytes(2, 16, 64, 256, 256, 8) <= 256 << 20
