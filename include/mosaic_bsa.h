@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 8
+#define MOSAIC_BSA_ABI_VERSION 9
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -78,8 +78,10 @@ const char* mosaic_last_error(void);
 
 /* Bytes of device workspace mosaic_bsa_forward needs: pooled q̄, k̄ (float64),
  * pooled v̄ and o_CG (float32), each [batch][heads][m][head_dim], then the
- * largest key norm of each block (float32 [batch][heads][m]), 256-byte aligned
- * sections.  Returns 0 if the shape is invalid or unsupported. */
+ * largest key norm of each block (float32 [batch][heads][m]), the bf16
+ * pieces of k̄ ([batch][heads][m][2][head_dim]) and |k̄_j|^2 (float32
+ * [batch][heads][m]), 256-byte aligned sections.  Returns 0 if the shape is
+ * invalid or unsupported. */
 size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn);
 
 /* The whole BSA forward pass (pool -> compressed + selection -> selected and
@@ -118,20 +120,36 @@ mosaic_status mosaic_bsa_forward_noalloc(const void* q, const void* k, const voi
  * summaries of the BSA item; the mean is this library's reading of the
  * unspecified pooling).  knorm (may be NULL): float32 [batch][heads][m], the
  * largest key norm max_t |k_t| of each block (float32 sums of squares); not
- * part of the method, it lets mosaic_bsa_fine bound scores in advance. */
+ * part of the method, it lets mosaic_bsa_fine bound scores in advance.
+ * kpieces, kbn2 (both NULL, or both given; not part of the method): k̄ as
+ * two bf16 pieces, k1 = bf16(k̄) and k2 = bf16(k̄ - k1) (formed in float32),
+ * uint16 bits [batch][heads][m][2][head_dim] with k1 first (16-byte
+ * aligned), and |k̄_j|^2 of each block, float32 [batch][heads][m], rounded
+ * up; mosaic_bsa_compress_select ranks on them.  One of the two without the
+ * other: MOSAIC_ERR_NULL_POINTER. */
 mosaic_status mosaic_bsa_pool(const void* q, const void* k, const void* v, int batch, int heads,
                               int head_dim, int nside, int block, double* qbar, double* kbar,
-                              float* vbar, float* knorm, void* stream);
+                              float* vbar, float* knorm, uint16_t* kpieces, float* kbn2, void* stream);
 
 /* Compressed branch and top-n selection from pooled tensors: o_cg
  * [batch][heads][m][head_dim] float32 = sum_j softmax_j(q̄_i·k̄_j/sqrt(d)) v̄_j,
  * and sel_idx [batch][heads][m][topn] = the topn largest logits of each row,
- * ties to the lower block index, listed in ascending order.  Logits are
- * formed in float64, so the selection matches a float64 evaluation except on
- * rows whose n-th and (n+1)-th logits differ by a few float64 ulps. */
+ * ties to the lower block index, listed in ascending order.  The selection
+ * matches a float64 evaluation of the logits except on rows whose n-th and
+ * (n+1)-th logits differ by a few float64 ulps.
+ * kpieces, kbn2: NULL, or mosaic_bsa_pool's outputs for the same k̄ (both or
+ * neither, else MOSAIC_ERR_NULL_POINTER).  Without them the logits are
+ * float64 dot products.  With them and topn <= 16, each row is ranked on
+ * bf16-piece logits (error below 2^-12.5 |q̄_i| max_j |k̄_j|) and certified:
+ * keys within twice that bound of the n-th value are rescored in float64,
+ * and a row that cannot be certified is redone in float64, so the selection
+ * is the same; o_cg is formed from the approximate logits (its weights are
+ * rounded to bf16 either way).  Pieces that do not belong to k̄ void the
+ * selection. */
 mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar, const float* vbar,
                                          int batch, int heads, int head_dim, int nside, int block,
-                                         int topn, float* o_cg, int32_t* sel_idx, void* stream);
+                                         int topn, const uint16_t* kpieces, const float* kbn2, float* o_cg,
+                                         int32_t* sel_idx, void* stream);
 
 /* Selected-block and sliding-window fine attention plus the gated sum, from
  * q, k, v (bf16), gates, o_cg (per block, float32) and sel_idx (any topn

@@ -65,9 +65,9 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_forward_noalloc.restype = I
         L.mosaic_bsa_forward_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, P]
         L.mosaic_bsa_pool.restype = I
-        L.mosaic_bsa_pool.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P]
+        L.mosaic_bsa_pool.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]
         L.mosaic_bsa_compress_select.restype = I
-        L.mosaic_bsa_compress_select.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
+        L.mosaic_bsa_compress_select.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P]
         L.mosaic_bsa_fine.restype = I
         L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
         L.mosaic_bsa_backward_workspace_bytes.restype = S
@@ -189,9 +189,11 @@ def mosaic_bsa_forward_noalloc(q, k, v, gates, nside, block, topn, window, out=N
     return out, sel_idx
 
 
-def mosaic_bsa_pool(q, k, v, nside, block, qbar=None, kbar=None, vbar=None, knorm=None, stream=None):
+def mosaic_bsa_pool(q, k, v, nside, block, qbar=None, kbar=None, vbar=None, knorm=None, kpieces=None,
+                    kbn2=None, stream=None):
     """q̄, k̄ (float64) and v̄ (float32), [b,H,m,d]: block means.  knorm, if given (float32
-    [b,H,m]), receives each block's largest key norm."""
+    [b,H,m]), receives each block's largest key norm; kpieces (bf16 [b,H,m,2,d]) and kbn2
+    (float32 [b,H,m]), given together, receive k̄'s two bf16 pieces and |k̄_j|^2."""
     b, h, n, d = _dims(q, nside)
     m = n // block
     qbar = torch.empty((b, h, m, d), dtype=torch.float64, device=q.device) if qbar is None else qbar
@@ -202,12 +204,16 @@ def mosaic_bsa_pool(q, k, v, nside, block, qbar=None, kbar=None, vbar=None, knor
         _ptr(v, torch.bfloat16, (b, h, n, d), "v"), b, h, d, nside, block,
         _ptr(qbar, torch.float64, (b, h, m, d), "qbar"), _ptr(kbar, torch.float64, (b, h, m, d), "kbar"),
         _ptr(vbar, torch.float32, (b, h, m, d), "vbar"),
-        None if knorm is None else _ptr(knorm, torch.float32, (b, h, m), "knorm"), _stream(stream)))
+        None if knorm is None else _ptr(knorm, torch.float32, (b, h, m), "knorm"),
+        None if kpieces is None else _ptr(kpieces, torch.bfloat16, (b, h, m, 2, d), "kpieces"),
+        None if kbn2 is None else _ptr(kbn2, torch.float32, (b, h, m), "kbn2"), _stream(stream)))
     return qbar, kbar, vbar
 
 
-def mosaic_bsa_compress_select(qbar, kbar, vbar, nside, block, topn, o_cg=None, sel_idx=None, stream=None):
-    """o_cg [b,H,m,d] fp32 and sel_idx [b,H,m,topn] int32 from the pooled tensors."""
+def mosaic_bsa_compress_select(qbar, kbar, vbar, nside, block, topn, o_cg=None, sel_idx=None, kpieces=None,
+                               kbn2=None, stream=None):
+    """o_cg [b,H,m,d] fp32 and sel_idx [b,H,m,topn] int32 from the pooled tensors.  kpieces and
+    kbn2: the pool's bf16 pieces of k̄ and |k̄_j|^2 (together), which topn <= 16 ranks on."""
     b, h, m, d = qbar.shape
     if m * block != 12 * nside * nside:
         raise ValueError("m * block must equal 12*nside^2")
@@ -216,6 +222,8 @@ def mosaic_bsa_compress_select(qbar, kbar, vbar, nside, block, topn, o_cg=None, 
     _check(lib().mosaic_bsa_compress_select(
         _ptr(qbar, torch.float64, (b, h, m, d), "qbar"), _ptr(kbar, torch.float64, (b, h, m, d), "kbar"),
         _ptr(vbar, torch.float32, (b, h, m, d), "vbar"), b, h, d, nside, block, topn,
+        None if kpieces is None else _ptr(kpieces, torch.bfloat16, (b, h, m, 2, d), "kpieces"),
+        None if kbn2 is None else _ptr(kbn2, torch.float32, (b, h, m), "kbn2"),
         _ptr(o_cg, torch.float32, (b, h, m, d), "o_cg"),
         _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"), _stream(stream)))
     return o_cg, sel_idx

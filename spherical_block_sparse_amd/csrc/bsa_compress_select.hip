@@ -59,6 +59,9 @@ struct CSArgs {
   int topn;
   int row_tiles;
   double c_exp2;   // log2(e) / sqrt(d): exp(s) = 2^(dot * c_exp2)
+  int redo;        // list kernel only: recompute just the row tiles holding a row marked -1
+  const uint16_t* kpieces;   // approximate kernel: bf16 pieces of k̄ [slices][m][2][D]
+  const float* kbn2;         // approximate kernel: |k̄_j|^2 [slices][m]
 };
 
 constexpr int kCap = 128;   // candidate buffer per row
@@ -367,6 +370,11 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
   const int lg = lane / 16;   // lane group 0..3: keys congruent to lg mod 4
   const int rw = tile * 64 + w * 16;
   const int row = rw + lr;
+  if (a.redo) {   // only tiles in which the approximate pass left a row uncertified
+    const int r = tile * 64 + (int)threadIdx.x;
+    const bool marked = threadIdx.x < 64 && r < m && a.sel[((size_t)slice * m + r) * n] < 0;
+    if (!__syncthreads_or(marked)) return;
+  }
 
   const double* qb = a.qbar + (size_t)slice * m * D;
   const char* kbytes = reinterpret_cast<const char*>(a.kbar + (size_t)slice * m * D);
@@ -463,6 +471,440 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
 #pragma unroll
     for (int j = 0; j < K; ++j)
       if (j / (K / 4) == lg && j < n) dst[j] = ix[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Approximate kernel, n <= 16: bf16-piece logits, then a certified selection.
+//
+// The float64 logits above cost 2·m²·d float64 matrix work, about half of
+// this stage.  Only the order of each row's keys at its n-th/(n+1)-th
+// boundary needs float64.  This kernel ranks with approximate logits and
+// certifies the result:
+//   * pieces: x = x1 + x2 + r with x1 = bf16(x), x2 = bf16(x - x1) and
+//     |r| <= (2^-16 + 2^-24) |x|.  The pooling writes the pieces of k̄
+//     ([m][2][d] bf16, natural channel order) and |k̄_j|^2 of every block;
+//     q̄ is split here, in registers.  The logit s~ = q1·k1 + q1·k2 + q2·k1
+//     takes 3 products per 32 of d on v_mfma_f32_16x16x32_bf16, whose
+//     bf16 x bf16 products are exact in float32.  The dropped terms are below
+//     3.1·2^-16 |q̄_c k̄_c| per channel and the float32 sum of the 3d products
+//     errs by at most γ_{3d-1} = 191·2^-24 (d = 64) of the sum of their
+//     magnitudes, twice that if the accumulator truncated; together under
+//     2^-13.8 Σ_c |q̄_c k̄_c| <= 2^-13.8 |q̄| |k̄|.  The bound used is
+//     ε_i = 2^-12.5 |q̄_i| max_j |k̄_j|, the maximum over the slice's key
+//     blocks, read from the block norms before streaming.
+//   * a chunk of 32 key blocks is 32 rows of pieces (4d bytes each) and 32
+//     rows of v̄, staged by direct loads, double-buffered, one barrier per
+//     chunk.  The MFMA's A rows are the chunk's keys in the order
+//     4(m%4) + m/4, which leaves each logit in the lane and register where
+//     the float64 kernel has it: the online softmax, ā·v̄ and the lane lists
+//     are unchanged in structure (o_CG uses the approximate logits; its
+//     weights are rounded to bf16 anyway).
+//   * every key a lane's list lets go -- not inserted, evicted, or dropped by
+//     the final merges -- updates the row's largest dropped value R.  The
+//     merges keep the best 32 of the row.  A row is certified when
+//     R < s~_(n) - 2ε: every dropped key is then below the exact n-th logit.
+//     Keys above s~_(n) + 2ε are in the top n, keys below s~_(n) - 2ε are
+//     out, and the few in between are rescored in float64 (the same fused
+//     multiply-adds for every key, so equal k̄ rows give equal values) and
+//     ranked by (value, index).
+//   * a row that fails (more than kBandMax keys in the band, or R inside
+//     it: massive ties) gets -1 as its first index; a second launch of the
+//     float64 list kernel redoes only the row tiles holding such a row.
+// A key more than 4ε below a lower bound of its row's n-th best is not
+// inserted: it is below the final s~_(n) - 2ε, so it cannot fail the row.
+constexpr double kApxEps = 1.7263349e-4;   // 2^-12.5
+constexpr int kBandMax = 8;
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+
+template <int K>
+__device__ __forceinline__ void list_insert_f(float (&tv)[K], int (&ti)[K], float x, int xi) {
+  bool c[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) c[j] = x > tv[j];
+#pragma unroll
+  for (int j = K - 1; j >= 1; --j) {
+    tv[j] = fmaxf(tv[j], fminf(tv[j - 1], x));
+    ti[j] = c[j - 1] ? ti[j - 1] : (c[j] ? xi : ti[j]);
+  }
+  tv[0] = fmaxf(tv[0], x);
+  ti[0] = c[0] ? xi : ti[0];
+}
+
+__device__ __forceinline__ bool beats_f(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+__device__ __forceinline__ void order_pair_f(float& av, int& ai, float& bv, int& bi) {
+  if (beats_f(bv, bi, av, ai)) {
+    const float tv = av; const int t = ai;
+    av = bv; ai = bi; bv = tv; bi = t;
+  }
+}
+
+// bitonic merge of a length-L bitonic sequence into best-first order
+template <int L>
+__device__ __forceinline__ void bitonic_merge_f(float (&v)[L], int (&ix)[L]) {
+#pragma unroll
+  for (int s = L / 2; s >= 1; s >>= 1)
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+      if ((j & s) == 0) order_pair_f(v[j], ix[j], v[j + s], ix[j + s]);
+}
+
+// Float version of chunk_softmax_pv (same layout and rounding).
+template <int D>
+__device__ __forceinline__ void chunk_softmax_pv_f(const floatx4 (&acc)[2], const float* vb, float c, float lazy,
+                                                   float& m_run, float& l_run, floatx4 (&oacc)[D / 16], int lr,
+                                                   int lg) {
+  float lmax = acc[0][0];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, acc[ct][i]);
+  if (__ballot(lmax > m_run + lazy)) {
+    float row = fmaxf(lmax, __shfl_xor(lmax, 16));
+    row = fmaxf(row, __shfl_xor(row, 32));
+    const float m_new = fmaxf(m_run, row);
+    const float alpha = m_run == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+  }
+  const float nmc = -m_run * c;
+  bf16x8 pb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(acc[e / 4][e % 4], c, nmc)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e], pb[e + 1]}, ones, l_run, false);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int col = dt * 16 + lr;
+    bf16x8 va;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 16 * (e / 4) + 4 * (e % 4) + lg;
+      va[e] = static_cast<__bf16>(vb[r * D + 4 * ((col >> 2) ^ vswz<D>(r)) + (col & 3)]);
+    }
+    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
+  }
+}
+
+// LDS rows of k̄ pieces: 4d bytes (k1 then k2, d/8 16-byte chunks each),
+// chunk c of row r at c ^ pswz(r): the 16 rows an MFMA operand read takes
+// at one chunk index land on 16 different 16-byte bank groups
+template <int D>
+__device__ __forceinline__ int pswz(int r) { return D == 64 ? (r & 15) : ((r >> 1) & 7); }
+
+template <int D>
+__device__ __forceinline__ void issue_pieces(int c0, uint16_t* pb, float* vb, const char* pbytes,
+                                             const char* vbytes, int32x4 rp, int32x4 rv, bool use_rsrc,
+                                             int m, int w, int lane) {
+  constexpr int PROW = D * 4, VROW = D * 4;   // bytes per LDS row
+  constexpr int PLOADS = kCols * PROW / 1024 / 4, VLOADS = kCols * VROW / 1024 / 4;   // 1 KB loads per wave
+  static_assert(PLOADS >= 1 && VLOADS >= 1, "chunk split");
+  const bool whole = use_rsrc && c0 + kCols <= m;
+#pragma unroll
+  for (int gg = 0; gg < PLOADS; ++gg) {
+    const int g = w + 4 * gg;
+    const int byte = 1024 * g + 16 * lane;
+    const int r = byte / PROW, pc = (byte % PROW) / 16;
+    const int off = r * PROW + 16 * (pc ^ pswz<D>(r));
+    char* dst = reinterpret_cast<char*>(pb) + 1024 * g;
+    if (whole) dma_buffer(dst, off, rp, c0 * PROW);
+    else dma_global(dst, c0 + r < m ? (const void*)(pbytes + (size_t)c0 * PROW + off) : (const void*)&kZero16);
+  }
+#pragma unroll
+  for (int gg = 0; gg < VLOADS; ++gg) {
+    const int g = w + 4 * gg;
+    const int byte = 1024 * g + 16 * lane;
+    const int r = byte / VROW, pc = (byte % VROW) / 16;
+    const int off = r * VROW + 16 * (pc ^ vswz<D>(r));
+    char* dst = reinterpret_cast<char*>(vb) + 1024 * g;
+    if (whole) dma_buffer(dst, off, rv, c0 * VROW);
+    else dma_global(dst, c0 + r < m ? (const void*)(vbytes + (size_t)c0 * VROW + off) : (const void*)&kZero16);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void compress_select_apx_kernel(CSArgs a) {
+  constexpr int K = 16;                  // list entries per lane while streaming
+  constexpr int H = D / 32;              // 32-wide halves of d
+  constexpr int PE = 2 * D;              // bf16 per row of pieces
+  __shared__ __attribute__((aligned(16))) uint16_t Pb0[kCols * PE];
+  __shared__ __attribute__((aligned(16))) uint16_t Pb1[kCols * PE];
+  __shared__ __attribute__((aligned(16))) float Vb0[kCols * D];
+  __shared__ __attribute__((aligned(16))) float Vb1[kCols * D];
+  __shared__ float Kmax2[4];
+
+  long long logical;   // contiguous run of row tiles per XCD
+  {
+    const long long G = gridDim.x, b = blockIdx.x;
+    const long long q8 = G / 8, r8 = G % 8, xcd = b % 8, k = b / 8;
+    logical = xcd < r8 ? xcd * (q8 + 1) + k : r8 * (q8 + 1) + (xcd - r8) * q8 + k;
+  }
+  const int m = a.m;
+  const int n = a.topn;
+  const int jb = (n + 3) / 4 - 1;   // each lane's entry jb bounds its row's n-th best from below
+  const long long slice = logical / a.row_tiles;
+  const int tile = (int)(logical % a.row_tiles);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int lr = lane % 16;   // this lane's row within the wave
+  const int lg = lane / 16;   // lane group: keys congruent to lg mod 4
+  const int row = tile * 64 + w * 16 + lr;
+
+  const double* qb = a.qbar + (size_t)slice * m * D;
+  const double* kslice = a.kbar + (size_t)slice * m * D;
+  const char* pbytes = reinterpret_cast<const char*>(a.kpieces + (size_t)slice * m * PE);
+  const char* vbytes = reinterpret_cast<const char*>(a.vbar + (size_t)slice * m * D);
+  const bool use_rsrc = (long long)m * D * 4 < 0x7fffffffLL;
+  const int32x4 rp = slice_rsrc(pbytes, use_rsrc ? m * D * 4 : 0);
+  const int32x4 rv = slice_rsrc(vbytes, use_rsrc ? m * D * 4 : 0);
+  const float c = (float)a.c_exp2;
+  const float lazy = 8.0f / c;
+
+  issue_pieces<D>(0, Pb0, Vb0, pbytes, vbytes, rp, rv, use_rsrc, m, w, lane);
+
+  // q̄ of this lane's row, channels 32h + 8lg + e (the B operand slots of
+  // half h), and its pieces
+  double qa[D / 4];
+#pragma unroll
+  for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qa[8 * hh + e] = row < m ? qb[(size_t)row * D + 32 * hh + 8 * lg + e] : 0.0;
+  bf16x8 q1[H], q2[H];
+  double qn2 = 0.0;
+#pragma unroll
+  for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double x = qa[8 * hh + e];
+      const __bf16 b1 = static_cast<__bf16>(static_cast<float>(x));
+      q1[hh][e] = b1;
+      q2[hh][e] = static_cast<__bf16>(static_cast<float>(x - static_cast<double>(static_cast<float>(b1))));
+      qn2 = fma(x, x, qn2);
+    }
+  qn2 += __shfl_xor(qn2, 16);
+  qn2 += __shfl_xor(qn2, 32);
+  const double qn = sqrt(qn2);
+
+  // largest |k̄_j|^2 of the slice
+  {
+    const float* kb2 = a.kbn2 + (size_t)slice * m;
+    float mx = 0.f;
+    for (int j = threadIdx.x; j < m; j += 256) mx = fmaxf(mx, kb2[j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) Kmax2[w] = mx;
+  }
+  // (the first barrier of the stream loop publishes Kmax2)
+
+  floatx4 oacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  float tv[K];
+  int ti[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    tv[j] = -INFINITY;
+    ti[j] = 0x7fffffff;
+  }
+  float rej = -INFINITY;   // largest value this lane's list has let go
+  const int pr = 4 * (lr & 3) + (lr >> 2);   // A row lr of a 16-key tile holds key pr
+  float eps = 0.f;
+
+  auto chunk = [&](int c0, const uint16_t* pb, const float* vb) __attribute__((always_inline)) {
+    floatx4 acc[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * ct + pr;
+      const uint16_t* prow = pb + r * PE;
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh) {
+        const int c1 = 4 * hh + lg, c2 = D / 8 + 4 * hh + lg;   // logical 16-byte chunks of k1, k2
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(prow + 8 * (c1 ^ pswz<D>(r)));
+        const bf16x8 k2 = *reinterpret_cast<const bf16x8*>(prow + 8 * (c2 ^ pswz<D>(r)));
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, q1[hh], acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, q1[hh], acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, q2[hh], acc[ct], 0, 0, 0);
+      }
+    }
+    if (c0 + kCols > m) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c0 + 16 * ct + 4 * i + lg >= m) acc[ct][i] = -INFINITY;
+    }
+    chunk_softmax_pv_f<D>(acc, vb, c, lazy, m_run, l_run, oacc, lr, lg);
+    // keys within 4ε below a lower bound of the row's n-th best are kept
+    float bound = tv[0];
+#pragma unroll
+    for (int j = 1; j < K && j < 4; ++j)
+      if (jb == j) bound = tv[j];
+    bound = fminf(bound, __shfl_xor(bound, 16));
+    bound = fminf(bound, __shfl_xor(bound, 32));
+    const float low = bound - 4.0f * eps;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = acc[ct][i];
+        float dropped = x;
+        if (__ballot(x > tv[K - 1] && x >= low)) {
+          dropped = x > tv[K - 1] ? tv[K - 1] : x;
+          list_insert_f<K>(tv, ti, x, c0 + 16 * ct + 4 * i + lg);
+        }
+        rej = fmaxf(rej, dropped);
+      }
+  };
+
+  // stream: wait for chunk c, then (every wave being past chunk c-1) load
+  // chunk c+1 into the other buffers while chunk c is computed
+  for (int c0 = 0; c0 < m; c0 += kCols) {
+    const int par = (c0 / kCols) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (c0 == 0) {
+      const float k2 = fmaxf(fmaxf(Kmax2[0], Kmax2[1]), fmaxf(Kmax2[2], Kmax2[3]));
+      eps = (float)(kApxEps * qn * sqrt((double)k2)) * 1.0001f;
+    }
+    if (c0 + kCols < m)
+      issue_pieces<D>(c0 + kCols, par ? Pb0 : Pb1, par ? Vb0 : Vb1, pbytes, vbytes, rp, rv, use_rsrc, m, w, lane);
+    chunk(c0, par ? Pb1 : Pb0, par ? Vb1 : Vb0);
+  }
+
+  store_ocg<D>(a.o_cg + ((size_t)slice * m + row) * D, oacc, l_run, lg, row < m);
+
+  // the row's best 2K: merge the lane groups pairwise (first without loss)
+  constexpr int L = 2 * K;
+  float lv[L];
+  int li[L];
+  {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      lv[j] = tv[j];
+      li[j] = ti[j];
+      lv[L - 1 - j] = __shfl_xor(tv[j], 16);   // partner's list reversed: a bitonic sequence
+      li[L - 1 - j] = __shfl_xor(ti[j], 16);
+    }
+    bitonic_merge_f<L>(lv, li);
+  }
+  rej = fmaxf(rej, __shfl_xor(rej, 16));
+  {
+    float pv[L];
+    int pi[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      pv[j] = __shfl_xor(lv[j], 32);
+      pi[j] = __shfl_xor(li[j], 32);
+    }
+    // the better of lv[j] and pv[L-1-j] is the best L as a bitonic sequence;
+    // the worse ones are dropped
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const bool take = beats_f(pv[L - 1 - j], pi[L - 1 - j], lv[j], li[j]);
+      rej = fmaxf(rej, take ? lv[j] : pv[L - 1 - j]);
+      if (take) {
+        lv[j] = pv[L - 1 - j];
+        li[j] = pi[L - 1 - j];
+      }
+    }
+    bitonic_merge_f<L>(lv, li);
+  }
+  rej = fmaxf(rej, __shfl_xor(rej, 32));
+
+  // certification and the band around the n-th value
+  float vn = lv[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j)
+    if (j == n - 1) vn = lv[j];
+  const float band_lo = vn - 2.0f * eps, band_hi = vn + 2.0f * eps;
+  int above = 0, inband = 0;
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    above += lv[j] > band_hi ? 1 : 0;
+    inband += (lv[j] >= band_lo && lv[j] <= band_hi) ? 1 : 0;
+  }
+  bool ok = rej < band_lo && inband <= kBandMax;
+  // band entries (positions above .. above+inband-1 of the sorted list)
+  int bidx[kBandMax];
+#pragma unroll
+  for (int t = 0; t < kBandMax; ++t) {
+    int v = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+      if (j == above + t) v = li[j];
+    bidx[t] = t < inband ? v : 0x7fffffff;
+  }
+  // exact rescoring: each lane forms its channels' share (32h + 8lg + e)
+  // with the same fused multiply-adds in the same order for every key, then
+  // the row's four lanes add their shares in a fixed pairing
+  double ex[kBandMax];
+  const unsigned long long bandset = __ballot(ok && inband > 0);
+  int bmax = inband;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) bmax = max(bmax, __shfl_xor(bmax, o));
+#pragma unroll
+  for (int t = 0; t < kBandMax; ++t) {
+    ex[t] = -INFINITY;
+    if (t < bmax && bandset) {
+      const int kj = (t < inband && bidx[t] < m) ? bidx[t] : 0;
+      const double* kr = kslice + (size_t)kj * D + 8 * lg;
+      double part = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fma(qa[8 * hh + e], kr[32 * hh + e], part);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      ex[t] = part;
+    }
+  }
+  const int need = n - above;
+  int ix[32];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ix[j] = j < above ? li[j] : 0x7fffffff;
+#pragma unroll
+  for (int t = 0; t < kBandMax; ++t) {
+    int rank = 0;
+#pragma unroll
+    for (int u = 0; u < kBandMax; ++u)
+      if (u < inband && u != t && (ex[u] > ex[t] || (ex[u] == ex[t] && bidx[u] < bidx[t]))) ++rank;
+    ix[16 + t] = (t < inband && rank < need) ? bidx[t] : 0x7fffffff;
+  }
+#pragma unroll
+  for (int t = 16 + kBandMax; t < 32; ++t) ix[t] = 0x7fffffff;
+  // ascending block order (bitonic sort of 32)
+#pragma unroll
+  for (int k = 2; k <= 32; k <<= 1)
+#pragma unroll
+    for (int sd = k / 2; sd >= 1; sd >>= 1)
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if ((j & sd) == 0) {
+          const bool up = (j & k) == 0;
+          const int lo = min(ix[j], ix[j + sd]), hi = max(ix[j], ix[j + sd]);
+          ix[j] = up ? lo : hi;
+          ix[j + sd] = up ? hi : lo;
+        }
+  if (row < m) {
+    int32_t* dst = a.sel + ((size_t)slice * m + row) * n;
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j / 4 == lg && j < n) dst[j] = ix[j];
+    } else if (lg == 0) {
+      dst[0] = -1;   // uncertified: the float64 list kernel redoes this row's tile
+    }
   }
 }
 
@@ -794,8 +1236,11 @@ __global__ __launch_bounds__(256) void compress_select_generic_kernel(CSArgs a, 
 
 hipError_t launch_compress_select(const double* qbar, const double* kbar, const float* vbar,
                                   float* o_cg, int32_t* sel, long long slices, int m, int head_dim,
-                                  int topn, hipStream_t stream) {
+                                  int topn, hipStream_t stream, const uint16_t* kpieces,
+                                  const float* kbn2) {
   CSArgs a;
+  a.kpieces = kpieces;
+  a.kbn2 = kbn2;
   a.qbar = qbar;
   a.kbar = kbar;
   a.vbar = vbar;
@@ -805,7 +1250,15 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
   a.topn = topn;
   a.row_tiles = (m + 63) / 64;
   a.c_exp2 = 1.4426950408889634 / sqrt((double)head_dim);
+  a.redo = 0;
   const dim3 grid((unsigned)(slices * a.row_tiles));
+  if (topn <= 16 && kpieces && kbn2) {   // approximate logits, certified; the float64 kernel redoes uncertified tiles
+    if (head_dim == 64) hipLaunchKernelGGL(compress_select_apx_kernel<64>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(compress_select_apx_kernel<32>, grid, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.redo = 1;
+  }
   if (topn > 64) {   // beyond the candidate capacity of the fast kernels
     const long long rows = slices * (long long)m;
     const dim3 ggrid((unsigned)((rows + 3) / 4));

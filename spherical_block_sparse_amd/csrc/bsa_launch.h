@@ -11,14 +11,22 @@
 
 namespace mosaic {
 
-// knorm non-null: also write the largest key norm max_t |k_t| of each block, float32 [slices][m]
+// knorm non-null: also write the largest key norm max_t |k_t| of each block, float32 [slices][m].
+// kpieces, kbn2 non-null (both): also write k̄ as bf16 pieces k1 = bf16(k̄), k2 = bf16(k̄ - k1),
+// [slices][m][2][head_dim] (natural channel order, k1 first), and |k̄_j|^2 per block (float32,
+// rounded up), [slices][m].
 hipError_t launch_pool(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* qbar,
                        double* kbar, float* vbar, long long slices, int n_tok, int head_dim,
-                       int block, hipStream_t stream, float* knorm = nullptr);
+                       int block, hipStream_t stream, float* knorm = nullptr, uint16_t* kpieces = nullptr,
+                       float* kbn2 = nullptr);
 
+// kpieces, kbn2 non-null (the pool's): topn <= 16 ranks on approximate logits from the pieces and
+// certifies every row (float64 rescoring of the band at its n-th value; uncertified row tiles are
+// redone in float64).  Without them, or for larger topn, the logits are float64 throughout.
 hipError_t launch_compress_select(const double* qbar, const double* kbar, const float* vbar,
                                   float* o_cg, int32_t* sel, long long slices, int m, int head_dim,
-                                  int topn, hipStream_t stream);
+                                  int topn, hipStream_t stream, const uint16_t* kpieces = nullptr,
+                                  const float* kbn2 = nullptr);
 
 // knorm non-null (the pool's largest key norm per block): waves whose scores
 // it bounds tightly enough skip the running maximum of the online softmax.

@@ -17,6 +17,9 @@
 // (8-bit significands, at most a few thousand terms), and block = 4^k makes
 // the final scaling exact.  HBM-bound: 6*D bytes read per token.
 //
+// With kpieces, the key workgroups also write k̄ as two bf16 pieces and each
+// block's |k̄|^2, the inputs of the approximate compressed-branch logits.
+//
 // The key workgroups can also write each block's largest key norm
 // max_t |k_t| (float32 [slices][m]).  It is not part of the method: the
 // fine-attention kernel turns it into an upper bound on a query's scores
@@ -32,6 +35,8 @@ struct PoolArgs {
   double* dst64[2];   // q̄, k̄
   float* dst32;       // v̄
   float* knorm;       // largest key norm of each block, or null
+  uint16_t* kpieces;  // bf16 pieces of k̄ [slices][m][2][D], or null
+  float* kbn2;        // |k̄_j|^2 of each block [slices][m] (rounded up), with kpieces
   long long total_blocks;   // slices * m
   long long wgs_per_tensor;
   int block;
@@ -147,6 +152,37 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     double2* d2 = reinterpret_cast<double2*>(dst);
 #pragma unroll
     for (int j = 0; j < 4; ++j) d2[j] = make_double2(acc[2 * j] * a.inv_block, acc[2 * j + 1] * a.inv_block);
+    if (tensor == 1 && a.kpieces) {
+      // k̄ = k1 + k2 + r with k1 = bf16(k̄), k2 = bf16(k̄ - k1) (through float32:
+      // |r| <= (2^-16 + 2^-24)|k̄|), natural channel order, and |k̄|^2 of the
+      // block (the approximate selection's error bound)
+      uint4 p1, p2;
+      uint32_t* w1 = reinterpret_cast<uint32_t*>(&p1);
+      uint32_t* w2 = reinterpret_cast<uint32_t*>(&p2);
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t b1[2], b2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const double x = acc[2 * j + h] * a.inv_block;
+          const float xf = static_cast<float>(x);
+          const __bf16 k1 = static_cast<__bf16>(xf);
+          const __bf16 k2 = static_cast<__bf16>(xf - static_cast<float>(k1));
+          b1[h] = __builtin_bit_cast(uint16_t, k1);
+          b2[h] = __builtin_bit_cast(uint16_t, k2);
+          ss = fma(x, x, ss);
+        }
+        w1[j] = b1[0] | (b1[1] << 16);
+        w2[j] = b2[0] | (b2[1] << 16);
+      }
+      uint16_t* prow = a.kpieces + (size_t)gb * 2 * D + c * 8;
+      *reinterpret_cast<uint4*>(prow) = p1;
+      *reinterpret_cast<uint4*>(prow + D) = p2;
+#pragma unroll
+      for (int off = 1; off < TPR; off *= 2) ss += __shfl_xor(ss, off);
+      if (c == 0) a.kbn2[gb] = static_cast<float>(ss * (1.0 + 1e-6));
+    }
   } else {
     float4* d4 = reinterpret_cast<float4*>(a.dst32 + o);
     d4[0] = make_float4((float)(acc[0] * a.inv_block), (float)(acc[1] * a.inv_block),
@@ -160,8 +196,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 
 hipError_t launch_pool(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* qbar,
                        double* kbar, float* vbar, long long slices, int n_tok, int head_dim,
-                       int block, hipStream_t stream, float* knorm) {
+                       int block, hipStream_t stream, float* knorm, uint16_t* kpieces, float* kbn2) {
   PoolArgs a;
+  a.kpieces = kpieces;
+  a.kbn2 = kbn2;
   a.src[0] = q;
   a.src[1] = k;
   a.src[2] = v;

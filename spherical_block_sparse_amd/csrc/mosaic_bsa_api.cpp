@@ -87,7 +87,7 @@ mosaic_status check_shape(int batch, int heads, int head_dim, int nside, int blo
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Workspace {
-  size_t qbar, kbar, vbar, ocg, knorm, total;
+  size_t qbar, kbar, vbar, ocg, knorm, kpieces, kbn2, total;
 };
 
 Workspace layout(const Shape& s) {
@@ -98,7 +98,9 @@ Workspace layout(const Shape& s) {
   w.vbar = w.kbar + align256(e * sizeof(double));
   w.ocg = w.vbar + align256(e * sizeof(float));
   w.knorm = w.ocg + align256(e * sizeof(float));
-  w.total = w.knorm + align256((size_t)s.slices * s.m * sizeof(float));
+  w.kpieces = w.knorm + align256((size_t)s.slices * s.m * sizeof(float));
+  w.kbn2 = w.kpieces + align256(e * 2 * sizeof(uint16_t));
+  w.total = w.kbn2 + align256((size_t)s.slices * s.m * sizeof(float));
   return w;
 }
 
@@ -210,11 +212,14 @@ mosaic_status run_forward(const Shape& s, const void* q, const void* k, const vo
   float* vbar = reinterpret_cast<float*>(ws + w.vbar);
   float* ocg = reinterpret_cast<float*>(ws + w.ocg);
   float* knorm = reinterpret_cast<float*>(ws + w.knorm);
+  uint16_t* kpieces = reinterpret_cast<uint16_t*>(ws + w.kpieces);
+  float* kbn2 = reinterpret_cast<float*>(ws + w.kbn2);
   hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                      static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
-                                     s.d, s.block, hs, knorm);
+                                     s.d, s.block, hs, knorm, kpieces, kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
-  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs, kpieces,
+                                     kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
@@ -256,31 +261,38 @@ size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside,
 
 mosaic_status mosaic_bsa_pool(const void* q, const void* k, const void* v, int batch, int heads,
                               int head_dim, int nside, int block, double* qbar, double* kbar,
-                              float* vbar, float* knorm, void* stream) {
+                              float* vbar, float* knorm, uint16_t* kpieces, float* kbn2, void* stream) {
   REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v);
   REQUIRE_PTR(qbar); REQUIRE_PTR(kbar); REQUIRE_PTR(vbar);
   REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16);
   REQUIRE_ALIGN(qbar, 16); REQUIRE_ALIGN(kbar, 16); REQUIRE_ALIGN(vbar, 16); REQUIRE_ALIGN(knorm, 4);
+  REQUIRE_ALIGN(kpieces, 16); REQUIRE_ALIGN(kbn2, 4);
+  if ((kpieces == nullptr) != (kbn2 == nullptr))
+    return fail(MOSAIC_ERR_NULL_POINTER, "kpieces and kbn2 are given together or not at all");
   Shape s;
   mosaic_status st = check_shape(batch, heads, head_dim, nside, block, 0, 0, 0, &s);
   if (st != MOSAIC_OK) return st;
   return hip_status(mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                         static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices,
-                                        s.n_tok, s.d, s.block, static_cast<hipStream_t>(stream), knorm),
+                                        s.n_tok, s.d, s.block, static_cast<hipStream_t>(stream), knorm, kpieces,
+                                        kbn2),
                     "bsa_pool launch");
 }
 
 mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar, const float* vbar,
                                          int batch, int heads, int head_dim, int nside, int block,
-                                         int topn, float* o_cg, int32_t* sel_idx, void* stream) {
+                                         int topn, const uint16_t* kpieces, const float* kbn2, float* o_cg,
+                                         int32_t* sel_idx, void* stream) {
   REQUIRE_PTR(qbar); REQUIRE_PTR(kbar); REQUIRE_PTR(vbar); REQUIRE_PTR(o_cg); REQUIRE_PTR(sel_idx);
   REQUIRE_ALIGN(qbar, 16); REQUIRE_ALIGN(kbar, 16); REQUIRE_ALIGN(vbar, 16); REQUIRE_ALIGN(o_cg, 16);
-  REQUIRE_ALIGN(sel_idx, 4);
+  REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(kpieces, 16); REQUIRE_ALIGN(kbn2, 4);
+  if ((kpieces == nullptr) != (kbn2 == nullptr))
+    return fail(MOSAIC_ERR_NULL_POINTER, "kpieces and kbn2 are given together or not at all");
   Shape s;
   mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, 0, kUsesTopn, &s);
   if (st != MOSAIC_OK) return st;
   return hip_status(mosaic::launch_compress_select(qbar, kbar, vbar, o_cg, sel_idx, s.slices, s.m, s.d,
-                                                   s.topn, static_cast<hipStream_t>(stream)),
+                                                   s.topn, static_cast<hipStream_t>(stream), kpieces, kbn2),
                     "bsa_compress_select launch");
 }
 
@@ -466,13 +478,16 @@ mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const vo
   float* vbar = reinterpret_cast<float*>(bws + w.vbar);
   float* ocg = reinterpret_cast<float*>(bws + w.ocg);
   float* knorm = reinterpret_cast<float*>(bws + w.knorm);
+  uint16_t* kpieces = reinterpret_cast<uint16_t*>(bws + w.kpieces);
+  float* kbn2 = reinterpret_cast<float*>(bws + w.kbn2);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = mosaic::launch_layer_in(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_in), batch,
                                          s.n_tok, channels, heads, s.d, q, k, v, gates, hs);
   if (e != hipSuccess) return hip_status(e, "layer input projection launch");
-  e = mosaic::launch_pool(q, k, v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs, knorm);
+  e = mosaic::launch_pool(q, k, v, qbar, kbar, vbar, s.slices, s.n_tok, s.d, s.block, hs, knorm, kpieces, kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
-  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs, kpieces,
+                                     kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(q, k, v, gates, ocg, sel_idx, nullptr, s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
                           hs, knorm, nullptr, nullptr, attn, heads);
@@ -511,12 +526,15 @@ mosaic_status mosaic_bsa_forward_train(const void* q, const void* k, const void*
   float* vbar = reinterpret_cast<float*>(ws + w.vbar);
   float* ocg = reinterpret_cast<float*>(ws + w.ocg);
   float* knorm = reinterpret_cast<float*>(ws + w.knorm);
+  uint16_t* kpieces = reinterpret_cast<uint16_t*>(ws + w.kpieces);
+  float* kbn2 = reinterpret_cast<float*>(ws + w.kbn2);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = mosaic::launch_pool(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                      static_cast<const uint16_t*>(v), qbar, kbar, vbar, s.slices, s.n_tok,
-                                     s.d, s.block, hs, knorm);
+                                     s.d, s.block, hs, knorm, kpieces, kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_pool launch");
-  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs);
+  e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs, kpieces,
+                                     kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,

@@ -20,11 +20,11 @@ hipError_t reached() {
 }  // namespace
 
 hipError_t launch_pool(const uint16_t*, const uint16_t*, const uint16_t*, double*, double*, float*, long long, int,
-                       int, int, hipStream_t, float*) {
+                       int, int, hipStream_t, float*, uint16_t*, float*) {
   return reached();
 }
 hipError_t launch_compress_select(const double*, const double*, const float*, float*, int32_t*, long long, int, int,
-                                  int, hipStream_t) {
+                                  int, hipStream_t, const uint16_t*, const float*) {
   return reached();
 }
 hipError_t launch_fine(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*, const int32_t*,

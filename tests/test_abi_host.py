@@ -72,14 +72,15 @@ def test_version_and_status_strings():
 
 def test_workspace_bytes_layout():
     L = _lib.lib()
-    # ns128: S = 192, m = 3072, d = 64 -> two float64 and two float32 [S][m][d] sections, then
-    # the float32 [S][m] largest key norm per block
+    # ns128: S = 192, m = 3072, d = 64 -> two float64 and two float32 [S][m][d] sections, the
+    # float32 [S][m] largest key norm per block, the bf16 [S][m][2][d] pieces of k̄ and the
+    # float32 [S][m] |k̄_j|^2
     e = 192 * 3072 * 64
-    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) == e * (8 + 8 + 4 + 4) + 192 * 3072 * 4
+    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) == e * (8 + 8 + 4 + 4 + 4) + 192 * 3072 * 4 * 2
     # tiny: S = 2, m = 48, d = 32 -> sections rounded up to 256 bytes
     e = 2 * 48 * 32
     r = lambda x: (x + 255) // 256 * 256
-    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 4) == 2 * r(8 * e) + 2 * r(4 * e) + r(4 * 2 * 48)
+    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 4) == 2 * r(8 * e) + 3 * r(4 * e) + 2 * r(4 * 2 * 48)
     assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 0) == 0      # invalid -> 0
     assert L.mosaic_bsa_workspace_bytes(1, 2, 48, 8, 16, 4) == 0      # unsupported -> 0
 
@@ -116,12 +117,21 @@ def test_forward_validation(kw, code):
 
 def test_stage_entry_points_validate():
     L = _lib.lib()
-    assert L.mosaic_bsa_pool(FAKE, FAKE, None, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None, None) == NULL
-    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 12, FAKE, FAKE, FAKE, None, None) == SHAPE
-    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, FAKE + 8, FAKE, FAKE, None, None) == MISAL
-    assert L.mosaic_bsa_pool(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, FAKE + 2, None) == MISAL
-    assert L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 0, FAKE, FAKE, None) == SHAPE
-    assert L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, 1, 2, 32, 8, 16, 4, None, FAKE, None) == NULL
+    pool = lambda *a: L.mosaic_bsa_pool(FAKE, FAKE, *a, None)
+    assert pool(None, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None, None, None) == NULL
+    assert pool(FAKE, 1, 2, 32, 8, 12, FAKE, FAKE, FAKE, None, None, None) == SHAPE
+    assert pool(FAKE, 1, 2, 32, 8, 16, FAKE + 8, FAKE, FAKE, None, None, None) == MISAL
+    assert pool(FAKE, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, FAKE + 2, None, None) == MISAL
+    assert pool(FAKE, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None, FAKE + 8, FAKE) == MISAL     # kpieces
+    assert pool(FAKE, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None, FAKE, FAKE + 2) == MISAL     # kbn2
+    assert pool(FAKE, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None, FAKE, None) == NULL          # pieces alone
+    assert pool(FAKE, 1, 2, 32, 8, 16, FAKE, FAKE, FAKE, None, None, FAKE) == NULL          # norms alone
+    cs = lambda *a: L.mosaic_bsa_compress_select(FAKE, FAKE, FAKE, *a, None)
+    assert cs(1, 2, 32, 8, 16, 0, None, None, FAKE, FAKE) == SHAPE
+    assert cs(1, 2, 32, 8, 16, 4, None, None, None, FAKE) == NULL
+    assert cs(1, 2, 32, 8, 16, 4, FAKE, None, FAKE, FAKE) == NULL
+    assert cs(1, 2, 32, 8, 16, 4, None, FAKE, FAKE, FAKE) == NULL
+    assert cs(1, 2, 32, 8, 16, 4, FAKE + 8, FAKE, FAKE, FAKE) == MISAL
     assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 32, 8, 16, 4, 0, FAKE, None) == SHAPE
     assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 32, 8, 16, 4, 32, FAKE, None) == NULL
     assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 48, 8, 16, 4, 32, FAKE, None) == UNSUP

@@ -67,26 +67,19 @@ def test_pool_stage_bit_exact(name):
                                           oracle.pool_mean(_slice(v, b, h), cfg.block).astype(np.float32))
 
 
-@pytest.mark.parametrize("name", ["tiny", "ns32", "ns64"])
-def test_compress_select_stage(name):
-    cfg = CONFIGS[name]
-    q, k, v, _ = _gpu_inputs(cfg)
-    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
-    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
-    torch.cuda.synchronize()
-    near = 0
-    for b in range(cfg.batch):
-        for h in range(cfg.heads):
-            ref = selection_ref(_slice(q, b, h), _slice(k, b, h), _slice(v, b, h), cfg.block, cfg.topn)
-            near += check_indices(sel[b, h].cpu().numpy(), ref, cfg.topn)["near_ties"]
-            np.testing.assert_allclose(o_cg[b, h].cpu().numpy(), ref["o_cg"], rtol=0, atol=ocg_tolerance(ref["vbar"]))
-    log(f"    indices: {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
+def _pieces(cfg):
+    """Buffers for the pool's bf16 pieces of k̄ and |k̄_j|^2."""
+    return (torch.empty((cfg.batch, cfg.heads, cfg.n_blocks, 2, cfg.head_dim), dtype=torch.bfloat16, device=DEV),
+            torch.empty((cfg.batch, cfg.heads, cfg.n_blocks), dtype=torch.float32, device=DEV))
 
 
-def _check_compress_select(cfg, q, k, v, topn=None):
+def _check_compress_select(cfg, q, k, v, topn=None, pieces=False):
+    """Selection bit-exact (outside near ties) and o_CG within its bound, with the float64
+    logits (pieces False) or the certified bf16-piece logits (pieces True)."""
     topn = topn or cfg.topn
-    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block)
-    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, topn)
+    kp, kb2 = _pieces(cfg) if pieces else (None, None)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, kpieces=kp, kbn2=kb2)
+    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, topn, kpieces=kp, kbn2=kb2)
     torch.cuda.synchronize()
     near = 0
     for b in range(cfg.batch):
@@ -95,6 +88,55 @@ def _check_compress_select(cfg, q, k, v, topn=None):
             near += check_indices(sel[b, h].cpu().numpy(), ref, topn)["near_ties"]
             np.testing.assert_allclose(o_cg[b, h].cpu().numpy(), ref["o_cg"], rtol=0, atol=ocg_tolerance(ref["vbar"]))
     return near
+
+
+@pytest.mark.parametrize("pieces", [False, True], ids=["f64", "pieces"])
+@pytest.mark.parametrize("name", ["tiny", "ns32", "ns64"])
+def test_compress_select_stage(name, pieces):
+    cfg = CONFIGS[name]
+    q, k, v, _ = _gpu_inputs(cfg)
+    near = _check_compress_select(cfg, q, k, v, pieces=pieces)
+    log(f"    indices: {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ns32"])
+def test_pool_key_pieces(name):
+    """The pool's pieces of k̄ are k1 = bf16(float32(k̄)) and k2 = bf16(float32(k̄) - k1), with
+    k̄ the oracle's block mean (rounding to nearest even, as torch rounds), and its |k̄_j|^2 is
+    the float64 sum of squares rounded up by at most 2e-6 relative."""
+    cfg = CONFIGS[name]
+    q, k, v, _ = _gpu_inputs(cfg)
+    kp, kb2 = _pieces(cfg)
+    _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, kpieces=kp, kbn2=kb2)
+    torch.cuda.synchronize()
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            kbar = torch.from_numpy(oracle.pool_mean(_slice(k, b, h), cfg.block))
+            xf = kbar.float()
+            k1 = xf.bfloat16()
+            k2 = (xf - k1.float()).bfloat16()
+            got = kp[b, h].cpu()
+            assert torch.equal(got[:, 0].view(torch.int16), k1.view(torch.int16))
+            assert torch.equal(got[:, 1].view(torch.int16), k2.view(torch.int16))
+            n2 = (kbar * kbar).sum(-1)
+            g2 = kb2[b, h].double().cpu()
+            assert torch.all(g2 >= n2) and torch.all(g2 <= n2 * (1 + 2e-6))
+
+
+@pytest.mark.parametrize("share", [1.0, 0.25], ids=["all", "quarter"])
+def test_compress_select_pieces_massive_ties(share):
+    """Key blocks with identical k̄ (every key block, or one in four) give rows whose n-th logit
+    is shared by more keys than the certified band holds: the approximate pass marks them and
+    the float64 kernel redoes their tiles, so the lower-index rule still decides."""
+    cfg = CONFIGS["ns32"]
+    q, k, v, _ = _gpu_inputs(cfg)
+    B = cfg.block
+    blk = torch.arange(cfg.n_tokens, device=DEV) // B
+    same = (blk % 4 == 0) if share < 1 else torch.ones_like(blk, dtype=torch.bool)
+    # every chosen block repeats the first block's tokens of its slice
+    k = torch.where(same[None, None, :, None], k[:, :, :B].repeat(1, 1, cfg.n_tokens // B, 1), k)
+    near = _check_compress_select(cfg, q, k, v, pieces=True)
+    log(f"    {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
 
 
 def test_compress_select_rows_crowded_into_one_lane_group():
@@ -112,8 +154,19 @@ def test_compress_select_rows_crowded_into_one_lane_group():
     qb = (torch.arange(cfg.n_tokens, device=DEV) // B) % 3 == 0
     k = (k.double() + kb[:, None] * u).bfloat16()
     q = (q.double() + qb[:, None] * u).bfloat16()
-    near = _check_compress_select(cfg, q, k, v)
-    log(f"    {cfg.slices * m} rows ({cfg.slices * ((m + 2) // 3)} crowded), {near} near-tie rows")
+    for pieces in (False, True):
+        near = _check_compress_select(cfg, q, k, v, pieces=pieces)
+        log(f"    {cfg.slices * m} rows ({cfg.slices * ((m + 2) // 3)} crowded), {near} near-tie rows, "
+            f"pieces {pieces}")
+
+
+@pytest.mark.parametrize("topn", [1, 3, 8, 13, 16])
+def test_compress_select_pieces_topn(topn):
+    """The certified approximate ranking at every list depth it serves (n <= 16)."""
+    cfg = CONFIGS["ns32"]
+    q, k, v, _ = _gpu_inputs(cfg)
+    near = _check_compress_select(cfg, q, k, v, topn=topn, pieces=True)
+    log(f"    topn {topn}: {cfg.slices * cfg.n_blocks} rows, {near} near-tie rows")
 
 
 @pytest.mark.parametrize("topn", [17, 32, 64])
@@ -401,8 +454,10 @@ def test_forward_equals_stages():
     q, k, v, g = _gpu_inputs(cfg)
     out, idx = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
     knorm = _knorm(cfg)
-    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
-    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
+    kp, kb2 = _pieces(cfg)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm, kpieces=kp, kbn2=kb2)
+    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, kpieces=kp,
+                                                kbn2=kb2)
     out2 = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
     torch.cuda.synchronize()
     assert torch.equal(idx, sel) and torch.equal(out, out2)
