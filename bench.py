@@ -142,10 +142,14 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
     vbar = torch.empty((b, h, m, d), dtype=torch.float32, device=dev)
     o_cg = torch.empty_like(vbar)
     knorm = torch.empty((b, h, m), dtype=torch.float32, device=dev)
+    kpieces = torch.empty((b, h, m, 2, d), dtype=torch.bfloat16, device=dev)
+    kbn2 = torch.empty((b, h, m), dtype=torch.float32, device=dev)
     sel2 = torch.empty_like(sel)
     out2 = torch.empty_like(out)
-    pool = lambda: _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar, knorm=knorm)
-    cs = lambda: _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel2)
+    pool = lambda: _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar, knorm=knorm,
+                                        kpieces=kpieces, kbn2=kbn2)
+    cs = lambda: _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel2,
+                                                 kpieces=kpieces, kbn2=kbn2)
     fine = lambda: _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel2, cfg.nside, cfg.block, cfg.topn, cfg.window, out2,
                                         knorm=knorm)
     pool(); cs(); fine()

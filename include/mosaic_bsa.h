@@ -142,8 +142,8 @@ mosaic_status mosaic_bsa_pool(const void* q, const void* k, const void* v, int b
  * float64 dot products.  With them and topn <= 16, each row is ranked on
  * bf16-piece logits (error below 2^-12.5 |q̄_i| max_j |k̄_j|) and certified:
  * keys within twice that bound of the n-th value are rescored in float64,
- * and a row that cannot be certified is redone in float64, so the selection
- * is the same; o_cg is formed from the approximate logits (its weights are
+ * and a row that cannot be certified is selected exactly from its float64
+ * logits, so the selection is the same; o_cg is formed from the approximate logits (its weights are
  * rounded to bf16 either way).  Pieces that do not belong to k̄ void the
  * selection. */
 mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar, const float* vbar,

@@ -59,7 +59,6 @@ struct CSArgs {
   int topn;
   int row_tiles;
   double c_exp2;   // log2(e) / sqrt(d): exp(s) = 2^(dot * c_exp2)
-  int redo;        // list kernel only: recompute just the row tiles holding a row marked -1
   const uint16_t* kpieces;   // approximate kernel: bf16 pieces of k̄ [slices][m][2][D]
   const float* kbn2;         // approximate kernel: |k̄_j|^2 [slices][m]
 };
@@ -370,11 +369,6 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
   const int lg = lane / 16;   // lane group 0..3: keys congruent to lg mod 4
   const int rw = tile * 64 + w * 16;
   const int row = rw + lr;
-  if (a.redo) {   // only tiles in which the approximate pass left a row uncertified
-    const int r = tile * 64 + (int)threadIdx.x;
-    const bool marked = threadIdx.x < 64 && r < m && a.sel[((size_t)slice * m + r) * n] < 0;
-    if (!__syncthreads_or(marked)) return;
-  }
 
   const double* qb = a.qbar + (size_t)slice * m * D;
   const char* kbytes = reinterpret_cast<const char*>(a.kbar + (size_t)slice * m * D);
@@ -509,12 +503,14 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
 //     multiply-adds for every key, so equal k̄ rows give equal values) and
 //     ranked by (value, index).
 //   * a row that fails (more than kBandMax keys in the band, or R inside
-//     it: massive ties) gets -1 as its first index; a second launch of the
-//     float64 list kernel redoes only the row tiles holding such a row.
+//     it: massive ties) is settled exactly by the whole workgroup at the
+//     end: its float64 logits (cached in the freed staging LDS when m <= 4096,
+//     else recomputed per pass), eight 8-bit radix passes for the n-th value
+//     and an ascending sweep (exact_row below).
 // A key more than 4ε below a lower bound of its row's n-th best is not
 // inserted: it is below the final s~_(n) - 2ε, so it cannot fail the row.
 constexpr double kApxEps = 1.7263349e-4;   // 2^-12.5
-constexpr int kBandMax = 8;
+constexpr int kBandMax = 16;   // band entries rescored per row (list positions 16 .. 31 of the result)
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
 
@@ -600,6 +596,120 @@ __device__ __forceinline__ void chunk_softmax_pv_f(const floatx4 (&acc)[2], cons
 template <int D>
 __device__ __forceinline__ int pswz(int r) { return D == 64 ? (r & 15) : ((r >> 1) & 7); }
 
+// order-preserving image of a float64 logit (-0 folded to +0, so equal
+// values give equal keys)
+__device__ __forceinline__ unsigned long long order_key(double s) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(s + 0.0);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Exact top-n of one row by a whole workgroup (256 threads): float64 logits
+// (sequential fused multiply-adds over d, the same for every key), kept as
+// order keys in `cache` when m <= cap and recomputed per pass otherwise;
+// eight 8-bit radix passes find the n-th largest key (a 256-bin LDS
+// histogram per pass, the digit found by one wave's scan) and how many keys
+// equal to it are taken; an ascending sweep writes the keys above it and the
+// lowest-index keys equal to it.  Ends with a barrier, so LDS may be reused.
+template <int D>
+__device__ __forceinline__ void exact_row(const CSArgs& a, long long slice, int r,
+                                                    unsigned long long* cache, int cap, double* Qf,
+                                                    unsigned* Hist, int* Xch) {
+  const int m = a.m, n = a.topn;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const double* kslice = a.kbar + (size_t)slice * m * D;
+  if (tid < D) Qf[tid] = a.qbar[((size_t)slice * m + r) * D + tid];
+  __syncthreads();
+  auto key = [&](int j) __attribute__((always_inline)) {
+    const double2* kr = reinterpret_cast<const double2*>(kslice + (size_t)j * D);
+    const double2* qs = reinterpret_cast<const double2*>(Qf);
+    double s = 0.0;
+#pragma unroll 8
+    for (int e = 0; e < D / 2; ++e) {
+      const double2 kv = kr[e], qv = qs[e];
+      s = fma(qv.x, kv.x, s);
+      s = fma(qv.y, kv.y, s);
+    }
+    return order_key(s);
+  };
+  const bool cached = m <= cap;
+  if (cached)
+    for (int j = tid; j < m; j += 256) cache[j] = key(j);
+  unsigned long long prefix = 0, mask = 0;
+  int k = n;   // rank of the wanted key among the keys matching prefix
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    Hist[tid] = 0u;
+    __syncthreads();
+    for (int j = tid; j < m; j += 256) {
+      const unsigned long long x = cached ? cache[j] : key(j);
+      if ((x & mask) == prefix) atomicAdd(&Hist[(x >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lane l takes bins 255-4l .. 252-4l (descending); exclusive prefix
+      // over lanes gives the count of larger digits
+      unsigned h[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = Hist[255 - 4 * lane - i];
+        tot += h[i];
+      }
+      unsigned incl = tot;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      unsigned acc = incl - tot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (acc < (unsigned)k && (unsigned)k <= acc + h[i]) {
+          Xch[0] = 255 - 4 * lane - i;
+          Xch[1] = (int)acc;
+        }
+        acc += h[i];
+      }
+    }
+    __syncthreads();
+    prefix |= (unsigned long long)Xch[0] << shift;
+    mask |= 0xFFull << shift;
+    k -= Xch[1];
+    __syncthreads();
+  }
+  int32_t* out = a.sel + ((size_t)slice * m + r) * n;
+  const unsigned long long below = (1ull << lane) - 1;
+  int taken = 0, eq_seen = 0;
+  for (int base = 0; base < m; base += 256) {
+    const int j = base + tid;
+    const unsigned long long x = j < m ? (cached ? cache[j] : key(j)) : 0ull;
+    const bool gt = j < m && x > prefix;
+    const bool eq = j < m && x == prefix;
+    const unsigned long long eqm = __ballot(eq);
+    if (lane == 0) Xch[w] = __popcll(eqm);
+    __syncthreads();
+    int eq_before = eq_seen + __popcll(eqm & below), eq_all = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      eq_before += u < w ? Xch[u] : 0;
+      eq_all += Xch[u];
+    }
+    const bool take = gt || (eq && eq_before < k);
+    const unsigned long long tm = __ballot(take);
+    __syncthreads();
+    if (lane == 0) Xch[w] = __popcll(tm);
+    __syncthreads();
+    int pos = taken + __popcll(tm & below), t_all = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pos += u < w ? Xch[u] : 0;
+      t_all += Xch[u];
+    }
+    if (take && pos < n) out[pos] = j;   // exactly n are taken; the bound only guards the buffer
+    taken += t_all;
+    eq_seen += eq_all;
+    __syncthreads();
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void issue_pieces(int c0, uint16_t* pb, float* vb, const char* pbytes,
                                              const char* vbytes, int32x4 rp, int32x4 rv, bool use_rsrc,
@@ -630,16 +740,27 @@ __device__ __forceinline__ void issue_pieces(int c0, uint16_t* pb, float* vb, co
   }
 }
 
+// Three waves per SIMD (at most 168 VGPRs, a few spilled in the epilogue)
+// run the stage about 15% faster than two.
 template <int D>
-__global__ __launch_bounds__(256) void compress_select_apx_kernel(CSArgs a) {
+__global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
   constexpr int K = 16;                  // list entries per lane while streaming
   constexpr int H = D / 32;              // 32-wide halves of d
   constexpr int PE = 2 * D;              // bf16 per row of pieces
-  __shared__ __attribute__((aligned(16))) uint16_t Pb0[kCols * PE];
-  __shared__ __attribute__((aligned(16))) uint16_t Pb1[kCols * PE];
-  __shared__ __attribute__((aligned(16))) float Vb0[kCols * D];
-  __shared__ __attribute__((aligned(16))) float Vb1[kCols * D];
+  constexpr int kStage = kCols * D * 16;   // bytes: two chunks of pieces and of v̄
+  // the staging buffers; after the stream loop the exact fallback keeps a
+  // row's logit keys here
+  __shared__ __attribute__((aligned(16))) char Stage[kStage];
+  uint16_t* const Pb0 = reinterpret_cast<uint16_t*>(Stage);
+  uint16_t* const Pb1 = Pb0 + kCols * PE;
+  float* const Vb0 = reinterpret_cast<float*>(Pb1 + kCols * PE);
+  float* const Vb1 = Vb0 + kCols * D;
   __shared__ float Kmax2[4];
+  __shared__ int FailRows[64];
+  __shared__ int NFail;
+  __shared__ __attribute__((aligned(16))) double Qf[D];
+  __shared__ unsigned Hist[256];
+  __shared__ int Xch[4];
 
   long long logical;   // contiguous run of row tiles per XCD
   {
@@ -693,6 +814,7 @@ __global__ __launch_bounds__(256) void compress_select_apx_kernel(CSArgs a) {
   qn2 += __shfl_xor(qn2, 32);
   const double qn = sqrt(qn2);
 
+  if (threadIdx.x == 0) NFail = 0;
   // largest |k̄_j|^2 of the slice
   {
     const float* kb2 = a.kbn2 + (size_t)slice * m;
@@ -834,29 +956,32 @@ __global__ __launch_bounds__(256) void compress_select_apx_kernel(CSArgs a) {
     above += lv[j] > band_hi ? 1 : 0;
     inband += (lv[j] >= band_lo && lv[j] <= band_hi) ? 1 : 0;
   }
+  static_assert(16 + kBandMax <= 32, "result slots");
   bool ok = rej < band_lo && inband <= kBandMax;
+  // the wave's largest band among certified rows: band work stops there
+  int bmax = ok ? inband : 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) bmax = max(bmax, __shfl_xor(bmax, o));
   // band entries (positions above .. above+inband-1 of the sorted list)
   int bidx[kBandMax];
 #pragma unroll
   for (int t = 0; t < kBandMax; ++t) {
     int v = 0x7fffffff;
+    if (t < bmax) {
 #pragma unroll
-    for (int j = 0; j < L; ++j)
-      if (j == above + t) v = li[j];
+      for (int j = 0; j < L; ++j)
+        if (j == above + t) v = li[j];
+    }
     bidx[t] = t < inband ? v : 0x7fffffff;
   }
   // exact rescoring: each lane forms its channels' share (32h + 8lg + e)
   // with the same fused multiply-adds in the same order for every key, then
   // the row's four lanes add their shares in a fixed pairing
   double ex[kBandMax];
-  const unsigned long long bandset = __ballot(ok && inband > 0);
-  int bmax = inband;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) bmax = max(bmax, __shfl_xor(bmax, o));
 #pragma unroll
   for (int t = 0; t < kBandMax; ++t) {
     ex[t] = -INFINITY;
-    if (t < bmax && bandset) {
+    if (t < bmax) {
       const int kj = (t < inband && bidx[t] < m) ? bidx[t] : 0;
       const double* kr = kslice + (size_t)kj * D + 8 * lg;
       double part = 0.0;
@@ -876,9 +1001,11 @@ __global__ __launch_bounds__(256) void compress_select_apx_kernel(CSArgs a) {
 #pragma unroll
   for (int t = 0; t < kBandMax; ++t) {
     int rank = 0;
+    if (t < bmax) {
 #pragma unroll
-    for (int u = 0; u < kBandMax; ++u)
-      if (u < inband && u != t && (ex[u] > ex[t] || (ex[u] == ex[t] && bidx[u] < bidx[t]))) ++rank;
+      for (int u = 0; u < kBandMax; ++u)
+        if (u < bmax && u < inband && u != t && (ex[u] > ex[t] || (ex[u] == ex[t] && bidx[u] < bidx[t]))) ++rank;
+    }
     ix[16 + t] = (t < inband && rank < need) ? bidx[t] : 0x7fffffff;
   }
 #pragma unroll
@@ -896,16 +1023,26 @@ __global__ __launch_bounds__(256) void compress_select_apx_kernel(CSArgs a) {
           ix[j] = up ? lo : hi;
           ix[j + sd] = up ? hi : lo;
         }
-  if (row < m) {
+  if (row < m && ok) {
     int32_t* dst = a.sel + ((size_t)slice * m + row) * n;
-    if (ok) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j / 4 == lg && j < n) dst[j] = ix[j];
-    } else if (lg == 0) {
-      dst[0] = -1;   // uncertified: the float64 list kernel redoes this row's tile
-    }
+    for (int j = 0; j < 16; ++j)
+      if (j / 4 == lg && j < n) dst[j] = ix[j];
   }
+
+  // rows left uncertified: exact, one at a time, by the whole workgroup
+  const bool fail = !ok && lg == 0 && row < m;
+  const unsigned long long fm = __ballot(fail);
+  if (fm) {
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&NFail, __popcll(fm));
+    base = __shfl(base, 0);
+    if (fail) FailRows[base + __popcll(fm & ((1ull << lane) - 1))] = row;
+  }
+  __syncthreads();   // every wave is past the stream loop: Stage is free
+  const int nfail = NFail;
+  for (int f = 0; f < nfail; ++f)
+    exact_row<D>(a, slice, FailRows[f], reinterpret_cast<unsigned long long*>(Stage), kStage / 8, Qf, Hist, Xch);
 }
 
 // ---------------------------------------------------------------------------
@@ -1120,11 +1257,6 @@ __global__ __launch_bounds__(256) void compress_select_buffered_kernel(CSArgs a)
 // evaluation up to the summation order of the products; -0 is folded to +0
 // so that equal logits compare equal.  Cost: about 11 recomputations of the
 // row's m logits; this path serves shapes the fast kernels do not cover.
-__device__ __forceinline__ unsigned long long order_key(double s) {
-  const unsigned long long b = (unsigned long long)__double_as_longlong(s + 0.0);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-
 __device__ __forceinline__ double wave_max_f64(double x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmax(x, __shfl_xor(x, o));
@@ -1250,14 +1382,11 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
   a.topn = topn;
   a.row_tiles = (m + 63) / 64;
   a.c_exp2 = 1.4426950408889634 / sqrt((double)head_dim);
-  a.redo = 0;
   const dim3 grid((unsigned)(slices * a.row_tiles));
-  if (topn <= 16 && kpieces && kbn2) {   // approximate logits, certified; the float64 kernel redoes uncertified tiles
+  if (topn <= 16 && kpieces && kbn2) {   // approximate logits, certified (exact fallback in-kernel)
     if (head_dim == 64) hipLaunchKernelGGL(compress_select_apx_kernel<64>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(compress_select_apx_kernel<32>, grid, dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    a.redo = 1;
+    return hipGetLastError();
   }
   if (topn > 64) {   // beyond the candidate capacity of the fast kernels
     const long long rows = slices * (long long)m;

@@ -14,12 +14,14 @@
 //     for blocks of 64 tokens, 128 when a block holds >= 128 tokens so that
 //     more queries share one gathered key set); each wave owns 32 queries as
 //     two 16-query sub-tiles whose MFMAs share every K / V operand read.
-//   * keys stream into LDS 64 at a time with gfx950 direct global->LDS loads
-//     (global_load_lds_dwordx4: lane l of a wave's load writes bytes
-//     16*l..16*l+15 of a 1 KB span), K and V row-major [key][d] with the
-//     16-byte chunks of each row XOR-swizzled; double-buffered in two
-//     separate LDS objects so the loads of chunk c+1 are in flight while
-//     chunk c is computed, one barrier per chunk, no staging registers.
+//   * keys stream into LDS 64 at a time with gfx950 direct loads to LDS
+//     (lane l of a wave's 16-byte load writes bytes 16*l..16*l+15 of a 1 KB
+//     span): buffer loads with fixed per-lane offsets and the chunk start as
+//     a scalar offset for runs of 64 consecutive tokens, global loads for
+//     gathered or partial chunks.  K and V are row-major [key][d] with the
+//     16-byte chunks of each row XOR-swizzled; two K/V buffer pairs in one
+//     LDS array, so the loads of chunk c+1 are in flight while chunk c is
+//     computed, one barrier per chunk, no staging registers.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (16 keys x 16 queries per
 //     tile); in that layout each lane owns 16 scores of one query, so the
 //     online softmax needs two cross-lane steps per chunk and the

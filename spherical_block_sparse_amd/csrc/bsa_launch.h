@@ -21,8 +21,9 @@ hipError_t launch_pool(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        float* kbn2 = nullptr);
 
 // kpieces, kbn2 non-null (the pool's): topn <= 16 ranks on approximate logits from the pieces and
-// certifies every row (float64 rescoring of the band at its n-th value; uncertified row tiles are
-// redone in float64).  Without them, or for larger topn, the logits are float64 throughout.
+// certifies every row (float64 rescoring of the band at its n-th value; a row it cannot certify is
+// settled by an exact float64 radix selection).  Without them, or for larger topn, the logits are
+// float64 throughout.
 hipError_t launch_compress_select(const double* qbar, const double* kbar, const float* vbar,
                                   float* o_cg, int32_t* sel, long long slices, int m, int head_dim,
                                   int topn, hipStream_t stream, const uint16_t* kpieces = nullptr,

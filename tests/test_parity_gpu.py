@@ -126,8 +126,8 @@ def test_pool_key_pieces(name):
 @pytest.mark.parametrize("share", [1.0, 0.25], ids=["all", "quarter"])
 def test_compress_select_pieces_massive_ties(share):
     """Key blocks with identical k̄ (every key block, or one in four) give rows whose n-th logit
-    is shared by more keys than the certified band holds: the approximate pass marks them and
-    the float64 kernel redoes their tiles, so the lower-index rule still decides."""
+    is shared by more keys than the certified band holds: the workgroup settles those rows with
+    its exact float64 fallback, so the lower-index rule still decides."""
     cfg = CONFIGS["ns32"]
     q, k, v, _ = _gpu_inputs(cfg)
     B = cfg.block
@@ -158,6 +158,40 @@ def test_compress_select_rows_crowded_into_one_lane_group():
         near = _check_compress_select(cfg, q, k, v, pieces=pieces)
         log(f"    {cfg.slices * m} rows ({cfg.slices * ((m + 2) // 3)} crowded), {near} near-tie rows, "
             f"pieces {pieces}")
+
+
+def test_compress_select_pieces_fallback_without_cache():
+    """Blocks of one token at Nside 32: m = 12288 key blocks, more than the exact fallback keeps
+    in LDS, so it recomputes the logits on every radix pass.  32 keys equal one long vector u:
+    for the queries set to u, and for the many random queries with a large q·u, those 32 tie
+    above every other key, and the band overflows.  Every 8th row and every u row is checked
+    against the oracle's selection."""
+    cfg = CONFIGS["ns32"].with_(name="ns32-b1", block=1, heads=1, topn=16, seed=321)
+    q, k, v, _ = _gpu_inputs(cfg)
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    u = torch.randn(cfg.head_dim, generator=gen, dtype=torch.float64)
+    u = (30.0 * u / u.norm()).bfloat16().to(DEV)
+    n = cfg.n_tokens
+    keys = torch.arange(0, n, n // 32, device=DEV)[:32] + 7
+    queries = torch.arange(0, n, n // 16, device=DEV)[:16] + 3
+    k[0, 0, keys] = u
+    q[0, 0, queries] = u
+    kp, kb2 = _pieces(cfg)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, kpieces=kp, kbn2=kb2)
+    _, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, kpieces=kp,
+                                             kbn2=kb2)
+    torch.cuda.synchronize()
+    qb = oracle.pool_mean(_slice(q, 0, 0), 1)
+    kb = oracle.pool_mean(_slice(k, 0, 0), 1)
+    rows = np.union1d(np.arange(0, n, 8), queries.cpu().numpy())
+    idx, gap = oracle.select_topn(qb[rows] @ kb.T, cfg.topn)
+    got = sel[0, 0].cpu().numpy()[rows]
+    exact = ~((gap > 0) & (gap < 1e-6))
+    assert np.array_equal(got[exact], idx[exact])
+    tied = int(np.sum(np.all(np.isin(idx, keys.cpu().numpy()), axis=1)))
+    log(f"    {rows.size} rows checked, {tied} with the u keys as their whole top-16, "
+        f"{int((~exact).sum())} near ties")
+    assert tied >= 16
 
 
 @pytest.mark.parametrize("topn", [1, 3, 8, 13, 16])
