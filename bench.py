@@ -43,6 +43,7 @@ from spherical_block_sparse_amd import CONFIGS, BSAConfig, make_inputs  # noqa: 
 from spherical_block_sparse_amd import _lib  # noqa: E402
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+DURATION_JSON = os.path.join(ROOT, "profiles", "kernel_durations.json")
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP64_TFLOPS = 78.6
@@ -73,20 +74,26 @@ def backward_flops(cfg: BSAConfig) -> float:
 
 def compress_flops(cfg: BSAConfig) -> float:
     m, d = cfg.n_blocks, cfg.head_dim
-    return 4.0 * m * m * d * cfg.slices          # logits (float64) + ā·v̄ (bf16)
+    return 4.0 * m * m * d * cfg.slices          # logits + ā·v̄
 
 
 def compress_bound_ms(cfg: BSAConfig) -> float:
-    """Matrix-core time of one compress+select launch at the published peaks:
-    2*m^2*d float64 FLOPs of logits plus 2*m^2*d bf16 FLOPs of ā·v̄ per slice."""
+    """Matrix-core time of one compress+select launch at the published peaks, in the
+    precision the forward computes it: for top-n <= 16 the logits as three bf16 piece
+    products (3 * 2*m^2*d bf16 FLOPs) and ā·v̄ (2*m^2*d bf16) per slice; above that,
+    float64 logits plus bf16 ā·v̄."""
     half = 2.0 * cfg.n_blocks ** 2 * cfg.head_dim * cfg.slices
+    if cfg.topn <= 16:
+        return 4.0 * half / (PEAK_BF16_TFLOPS * 1e12) * 1e3
     return (half / (PEAK_FP64_TFLOPS * 1e12) + half / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
 
 
 def pool_bytes(cfg: BSAConfig) -> float:
+    """q, k, v read once; q̄, k̄ (float64), v̄ (float32), k̄'s two bf16 pieces, and the
+    per-block key norm and |k̄|^2 (float32) written."""
     e_in = cfg.slices * cfg.n_tokens * cfg.head_dim
     e_out = cfg.slices * cfg.n_blocks * cfg.head_dim
-    return 3.0 * e_in * 2 + e_out * (8 + 8 + 4)
+    return 3.0 * e_in * 2 + e_out * (8 + 8 + 4 + 4) + cfg.slices * cfg.n_blocks * 8
 
 
 def measured_traffic(key: str):
@@ -100,6 +107,21 @@ def measured_traffic(key: str):
         if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
             return None
         return rec["hbm_bytes"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def profiled_ms(key: str):
+    """Mean duration (ms) of a kernel in the committed rocprofv3 kernel trace of
+    the bench command, or None when it is missing or the kernel source has
+    changed since it was taken."""
+    import hashlib
+    try:
+        rec = json.load(open(DURATION_JSON))[key]
+        src = os.path.join(ROOT, rec["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["avg_ms"]
     except (OSError, KeyError, ValueError):
         return None
 
@@ -354,6 +376,9 @@ def main() -> int:
     if args.secondary and args.secondary != args.config:
         s = measure(CONFIGS[args.secondary], max(5, args.steps // 2), max(2, args.warmup // 2),
                     backward=not args.no_backward)
+        cpu2 = None
+        if not args.no_cpu_baseline:
+            cpu2 = cpu_baseline(s["cfg"], s["inputs"], args.cpu_budget)
         del s["inputs"]
         secondary = {
             "workload": s["cfg"].name, "value": s["tokens_per_s"], "unit": "tokens/s", "ms_per_step": s["ms"],
@@ -362,6 +387,7 @@ def main() -> int:
             "compress_select_frac": compress_bound_ms(s["cfg"]) / s["cs_ms"],
             "pool_hbm_frac": s["pool_gbs"] / PEAK_HBM_GBS,
             "backward": s["backward"],
+            "cpu_baseline": cpu2,
         }
 
     c = r["cfg"]
@@ -391,12 +417,18 @@ def main() -> int:
             "achieved": r["fine_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": r["fine_tflops"] / PEAK_BF16_TFLOPS, "traffic": measured_traffic(f"fine_{c.name}"),
             "flops_per_launch": r["fine_flops"], "ms_per_launch": r["fine_ms"],
+            # the same kernel's mean duration in the committed rocprofv3 trace of this command
+            "profiled_ms_per_launch": profiled_ms(f"fine_{c.name}"),
+            "frac_profiled": (None if profiled_ms(f"fine_{c.name}") is None else
+                              r["fine_flops"] / (profiled_ms(f"fine_{c.name}") * 1e-3) / 1e12 / PEAK_BF16_TFLOPS),
         },
         "kernels": {
             "pool": {"ms": r["pool_ms"], "bound": "hbm", "achieved_GBs": r["pool_gbs"],
                      "frac": r["pool_gbs"] / PEAK_HBM_GBS, "bytes_per_launch": r["pool_bytes"],
                      "traffic": measured_traffic(f"pool_{c.name}")},
-            "compress_select": {"ms": r["cs_ms"], "bound": "fp64 + bf16 matrix",
+            "compress_select": {"ms": r["cs_ms"],
+                                "bound": "bf16 matrix (3 piece products + ā·v̄)" if c.topn <= 16
+                                         else "fp64 + bf16 matrix",
                                 "bound_ms": compress_bound_ms(c), "frac": compress_bound_ms(c) / r["cs_ms"],
                                 "achieved_TFLOPs": r["cs_tflops"],
                                 "traffic": measured_traffic(f"select_{c.name}")},

@@ -59,6 +59,7 @@ struct CSArgs {
   int topn;
   int row_tiles;
   double c_exp2;   // log2(e) / sqrt(d): exp(s) = 2^(dot * c_exp2)
+  int redo;        // list kernel only: recompute just the row tiles holding a row marked -1
   const uint16_t* kpieces;   // approximate kernel: bf16 pieces of k̄ [slices][m][2][D]
   const float* kbn2;         // approximate kernel: |k̄_j|^2 [slices][m]
 };
@@ -369,6 +370,11 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
   const int lg = lane / 16;   // lane group 0..3: keys congruent to lg mod 4
   const int rw = tile * 64 + w * 16;
   const int row = rw + lr;
+  if (a.redo) {   // only tiles in which the approximate pass left rows to this kernel
+    const int r = tile * 64 + (int)threadIdx.x;
+    const bool marked = threadIdx.x < 64 && r < m && a.sel[((size_t)slice * m + r) * n] < 0;
+    if (!__syncthreads_or(marked)) return;
+  }
 
   const double* qb = a.qbar + (size_t)slice * m * D;
   const char* kbytes = reinterpret_cast<const char*>(a.kbar + (size_t)slice * m * D);
@@ -503,14 +509,21 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
 //     multiply-adds for every key, so equal k̄ rows give equal values) and
 //     ranked by (value, index).
 //   * a row that fails (more than kBandMax keys in the band, or R inside
-//     it: massive ties) is settled exactly by the whole workgroup at the
-//     end: its float64 logits (cached in the freed staging LDS when m <= 4096,
-//     else recomputed per pass), eight 8-bit radix passes for the n-th value
-//     and an ascending sweep (exact_row below).
+//     it: massive ties, or logits crowded closer than ε) is settled exactly
+//     by the whole workgroup at the end: its float64 logits (cached in the
+//     freed staging LDS when m <= 4096, else recomputed per pass), eight
+//     8-bit radix passes for the n-th value and an ascending sweep
+//     (exact_row).  A tile with more than kExactRows such rows is marked
+//     instead (-1 as the rows' first index), and a second launch of the
+//     float64 list kernel redoes the marked tiles; its other workgroups read
+//     their tile's 64 marks and exit.
 // A key more than 4ε below a lower bound of its row's n-th best is not
 // inserted: it is below the final s~_(n) - 2ε, so it cannot fail the row.
 constexpr double kApxEps = 1.7263349e-4;   // 2^-12.5
 constexpr int kBandMax = 16;   // band entries rescored per row (list positions 16 .. 31 of the result)
+// uncertified rows a workgroup settles itself; beyond that its tile is
+// marked for the float64 list kernel
+constexpr int kExactRows = 4;
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
 
@@ -603,46 +616,84 @@ __device__ __forceinline__ unsigned long long order_key(double s) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Exact top-n of one row by a whole workgroup (256 threads): float64 logits
-// (sequential fused multiply-adds over d, the same for every key), kept as
-// order keys in `cache` when m <= cap and recomputed per pass otherwise;
-// eight 8-bit radix passes find the n-th largest key (a 256-bin LDS
-// histogram per pass, the digit found by one wave's scan) and how many keys
-// equal to it are taken; an ascending sweep writes the keys above it and the
+// Exact top-n of one row by a whole workgroup (256 threads).  Float64
+// logits: eight lanes per key, each with d/8 channels (sequential fused
+// multiply-adds), then a fixed butterfly over the eight, so every key gets
+// the same operation order and the loads are whole 128-byte lines.  They are
+// kept as order keys in `cache` when m <= cap and recomputed per pass
+// otherwise.  Eight 8-bit radix passes find the n-th largest key (a 256-bin
+// LDS histogram per pass, each thread adding its runs of equal digits with
+// one atomic, the digit found by one wave's scan) and how many keys equal to
+// it are taken; an ascending sweep writes the keys above it and the
 // lowest-index keys equal to it.  Ends with a barrier, so LDS may be reused.
 template <int D>
 __device__ __forceinline__ void exact_row(const CSArgs& a, long long slice, int r,
-                                                    unsigned long long* cache, int cap, double* Qf,
-                                                    unsigned* Hist, int* Xch) {
+                                          unsigned long long* cache, int cap, double* Qf,
+                                          unsigned* Hist, int* Xch) {
+  constexpr int E = D / 8;   // channels per lane
   const int m = a.m, n = a.topn;
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int sub = lane & 7, kl = lane >> 3;   // channel group, key within the wave's 8
   const double* kslice = a.kbar + (size_t)slice * m * D;
   if (tid < D) Qf[tid] = a.qbar[((size_t)slice * m + r) * D + tid];
   __syncthreads();
-  auto key = [&](int j) __attribute__((always_inline)) {
-    const double2* kr = reinterpret_cast<const double2*>(kslice + (size_t)j * D);
-    const double2* qs = reinterpret_cast<const double2*>(Qf);
+  double qreg[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qreg[e] = Qf[E * sub + e];
+  // order key of key j formed by the 8 lanes kl of this wave (valid in all 8)
+  auto coop_key = [&](int j) __attribute__((always_inline)) {
     double s = 0.0;
-#pragma unroll 8
-    for (int e = 0; e < D / 2; ++e) {
-      const double2 kv = kr[e], qv = qs[e];
-      s = fma(qv.x, kv.x, s);
-      s = fma(qv.y, kv.y, s);
+    if (j < m) {
+      const double2* kr = reinterpret_cast<const double2*>(kslice + (size_t)j * D + E * sub);
+#pragma unroll
+      for (int e = 0; e < E / 2; ++e) {
+        const double2 kv = kr[e];
+        s = fma(qreg[2 * e], kv.x, s);
+        s = fma(qreg[2 * e + 1], kv.y, s);
+      }
     }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
     return order_key(s);
   };
   const bool cached = m <= cap;
-  if (cached)
-    for (int j = tid; j < m; j += 256) cache[j] = key(j);
+  if (cached) {
+    for (int j0 = 8 * w; j0 < m; j0 += 32) {
+      const int j = j0 + kl;
+      const unsigned long long x = coop_key(j);
+      if (sub == 0 && j < m) cache[j] = x;
+    }
+  }
+  __syncthreads();
   unsigned long long prefix = 0, mask = 0;
   int k = n;   // rank of the wanted key among the keys matching prefix
   for (int shift = 56; shift >= 0; shift -= 8) {
     Hist[tid] = 0u;
     __syncthreads();
-    for (int j = tid; j < m; j += 256) {
-      const unsigned long long x = cached ? cache[j] : key(j);
-      if ((x & mask) == prefix) atomicAdd(&Hist[(x >> shift) & 255], 1u);
+    int cur = -1;
+    unsigned cnt = 0;
+    auto count = [&](unsigned long long x) __attribute__((always_inline)) {
+      if ((x & mask) == prefix) {
+        const int dg = (int)((x >> shift) & 255);
+        if (dg != cur) {
+          if (cnt) atomicAdd(&Hist[cur], cnt);
+          cur = dg;
+          cnt = 0;
+        }
+        ++cnt;
+      }
+    };
+    if (cached) {
+      for (int j = tid; j < m; j += 256) count(cache[j]);
+    } else {
+      for (int j0 = 8 * w; j0 < m; j0 += 32) {
+        const int j = j0 + kl;
+        const unsigned long long x = coop_key(j);
+        if (sub == 0 && j < m) count(x);
+      }
     }
+    if (cnt) atomicAdd(&Hist[cur], cnt);
     __syncthreads();
     if (w == 0) {
       // lane l takes bins 255-4l .. 252-4l (descending); exclusive prefix
@@ -675,12 +726,30 @@ __device__ __forceinline__ void exact_row(const CSArgs& a, long long slice, int 
     k -= Xch[1];
     __syncthreads();
   }
+  // ascending sweep over keys tid, tid + 256, ...: the block's keys of one
+  // step are ordered by thread, so ballots and per-wave counts give each
+  // taken key its output slot
   int32_t* out = a.sel + ((size_t)slice * m + r) * n;
   const unsigned long long below = (1ull << lane) - 1;
   int taken = 0, eq_seen = 0;
   for (int base = 0; base < m; base += 256) {
+    unsigned long long x = 0;
+    if (cached) {
+      const int j = base + tid;
+      x = j < m ? cache[j] : 0ull;
+    } else {
+      // the wave's 64 keys base + 64w + o, eight per call: call i forms
+      // o = 8i + kl in lanes 8kl .. 8kl+7, and lane 8kl + i keeps it, so lane
+      // L holds o = 8(L%8) + L/8; lane t takes its own key o = t from lane
+      // 8(t%8) + t/8
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned long long y = coop_key(base + 64 * w + 8 * i + kl);
+        if (sub == i) x = y;
+      }
+      x = __shfl(x, 8 * (lane % 8) + lane / 8);
+    }
     const int j = base + tid;
-    const unsigned long long x = j < m ? (cached ? cache[j] : key(j)) : 0ull;
     const bool gt = j < m && x > prefix;
     const bool eq = j < m && x == prefix;
     const unsigned long long eqm = __ballot(eq);
@@ -1041,6 +1110,11 @@ __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
   }
   __syncthreads();   // every wave is past the stream loop: Stage is free
   const int nfail = NFail;
+  if (nfail > kExactRows) {
+    // many rows (crowded logits): the float64 list kernel redoes the tile
+    if ((int)threadIdx.x < nfail) a.sel[((size_t)slice * m + FailRows[threadIdx.x]) * n] = -1;
+    return;
+  }
   for (int f = 0; f < nfail; ++f)
     exact_row<D>(a, slice, FailRows[f], reinterpret_cast<unsigned long long*>(Stage), kStage / 8, Qf, Hist, Xch);
 }
@@ -1382,11 +1456,14 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
   a.topn = topn;
   a.row_tiles = (m + 63) / 64;
   a.c_exp2 = 1.4426950408889634 / sqrt((double)head_dim);
+  a.redo = 0;
   const dim3 grid((unsigned)(slices * a.row_tiles));
-  if (topn <= 16 && kpieces && kbn2) {   // approximate logits, certified (exact fallback in-kernel)
+  if (topn <= 16 && kpieces && kbn2) {   // approximate logits, certified; crowded tiles redone in float64
     if (head_dim == 64) hipLaunchKernelGGL(compress_select_apx_kernel<64>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(compress_select_apx_kernel<32>, grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.redo = 1;
   }
   if (topn > 64) {   // beyond the candidate capacity of the fast kernels
     const long long rows = slices * (long long)m;

@@ -9,9 +9,10 @@ entry point (the layer stages with 512 channels)
 beforehand to produce their inputs); --stage backward runs the training
 forward once and then the backward from its saved state `reps` times, with
 a seeded float32 upstream gradient.  --order ring lays the same field out in
-RING (iso-latitude) token order.  --copy-mib N copies an N MiB buffer with torch's
-elementwise copy kernel `reps` times: N MiB read and N MiB written per call,
-the calibration of the FETCH_SIZE / WRITE_SIZE counters.
+RING (iso-latitude) token order.  --copy-mib N copies an N MiB buffer
+`reps` times (torch's copy_ of a contiguous tensor: the runtime's device copy
+kernel): N MiB read and N MiB written per call, the calibration of the
+FETCH_SIZE / WRITE_SIZE counters.
 """
 
 from __future__ import annotations
@@ -64,9 +65,13 @@ def main() -> int:
         from .locality_study import permute_tokens
         from .synth import nest_ring_order
         q, k, v, g = permute_tokens([q, k, v, g], nest_ring_order(cfg.nside))
-    knorm = torch.empty((cfg.batch, cfg.heads, cfg.n_blocks), dtype=torch.float32, device="cuda")
-    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
-    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
+    b, h, m, d = cfg.batch, cfg.heads, cfg.n_blocks, cfg.head_dim
+    knorm = torch.empty((b, h, m), dtype=torch.float32, device="cuda")
+    kp = torch.empty((b, h, m, 2, d), dtype=torch.bfloat16, device="cuda")   # the forward's extra pool outputs
+    kb2 = torch.empty((b, h, m), dtype=torch.float32, device="cuda")
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm, kpieces=kp, kbn2=kb2)
+    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, kpieces=kp,
+                                                kbn2=kb2)
     torch.cuda.synchronize()
     if args.stage == "backward":
         _, sel_t, saved = _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
@@ -82,9 +87,10 @@ def main() -> int:
         elif args.stage == "train":
             _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
         elif args.stage == "pool":
-            _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar, knorm=knorm)
+            _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, qbar, kbar, vbar, knorm=knorm, kpieces=kp, kbn2=kb2)
         elif args.stage == "select":
-            _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel)
+            _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel, kpieces=kp,
+                                            kbn2=kb2)
         elif args.stage == "fine":
             _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
         else:

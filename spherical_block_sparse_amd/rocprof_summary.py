@@ -4,6 +4,7 @@
     python -m spherical_block_sparse_amd.rocprof_summary counters <counter_collection.csv> [--kernel REGEX]
     python -m spherical_block_sparse_amd.rocprof_summary traffic --fetch F.csv --write W.csv \
         --copy-fetch CF.csv --copy-write CW.csv --copy-mib N --kernel REGEX --source FILE
+    python -m spherical_block_sparse_amd.rocprof_summary duration <kernel_stats.csv> --kernel REGEX --source FILE
 
 `stats` lists name, calls, average / min / max duration of every kernel.
 `counters` sums each counter over the dispatches of the matching kernels and
@@ -13,6 +14,9 @@ HBM bytes per dispatch, each scaled by the ratio of the known bytes of a
 plain N MiB copy to what the same counter reported for it, and records the
 SHA-256 of the kernel source so a later reader can tell whether the kernel
 has changed since.
+`duration` records the mean duration of the one kernel matching REGEX in a
+--kernel-trace --stats run, with the same source hash.  With --update
+FILE --key NAME either record is merged into that JSON file under NAME.
 """
 
 from __future__ import annotations
@@ -88,9 +92,23 @@ def traffic(a) -> dict:
     }
 
 
+def duration(a) -> dict:
+    rows = [r for r in csv.DictReader(open(a.csv)) if re.search(a.kernel, r["Name"])]
+    if len(rows) != 1:
+        raise SystemExit(f"/{a.kernel}/ matches {len(rows)} kernels in {a.csv}")
+    r = rows[0]
+    return {
+        "kernel_regex": a.kernel,
+        "source": a.source,
+        "source_sha256": hashlib.sha256(open(a.source, "rb").read()).hexdigest(),
+        "calls": int(r["Calls"]), "avg_ms": float(r["AverageNs"]) / 1e6,
+        "min_ms": float(r["MinNs"]) / 1e6, "max_ms": float(r["MaxNs"]) / 1e6,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["stats", "counters", "traffic"])
+    ap.add_argument("mode", choices=["stats", "counters", "traffic", "duration"])
     ap.add_argument("csv", nargs="?")
     ap.add_argument("--kernel", default=None)
     ap.add_argument("--fetch")
@@ -99,13 +117,26 @@ def main() -> int:
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-mib", type=int, default=0)
     ap.add_argument("--source")
+    ap.add_argument("--update", help="JSON file to merge the record into")
+    ap.add_argument("--key", help="name of the record in --update")
     a = ap.parse_args()
     if a.mode == "stats":
         print(stats(a.csv))
-    elif a.mode == "counters":
+        return 0
+    if a.mode == "counters":
         print(counters(a.csv, a.kernel))
-    else:
-        print(json.dumps(traffic(a), indent=1))
+        return 0
+    rec = traffic(a) if a.mode == "traffic" else duration(a)
+    print(json.dumps(rec, indent=1))
+    if a.update:
+        try:
+            allrec = json.load(open(a.update))
+        except FileNotFoundError:
+            allrec = {}
+        allrec[a.key] = rec
+        with open(a.update, "w") as f:
+            json.dump(allrec, f, indent=1, sort_keys=True)
+            f.write("\n")
     return 0
 
 

@@ -160,38 +160,36 @@ def test_compress_select_rows_crowded_into_one_lane_group():
             f"pieces {pieces}")
 
 
-def test_compress_select_pieces_fallback_without_cache():
-    """Blocks of one token at Nside 32: m = 12288 key blocks, more than the exact fallback keeps
-    in LDS, so it recomputes the logits on every radix pass.  32 keys equal one long vector u:
-    for the queries set to u, and for the many random queries with a large q·u, those 32 tie
-    above every other key, and the band overflows.  Every 8th row and every u row is checked
-    against the oracle's selection."""
-    cfg = CONFIGS["ns32"].with_(name="ns32-b1", block=1, heads=1, topn=16, seed=321)
+@pytest.mark.parametrize("block", [64, 1], ids=["cached", "uncached"])
+def test_compress_select_pieces_exact_rows(block):
+    """A few rows per row tile that the certification cannot settle, so that the workgroup
+    selects them exactly itself: query blocks of slice 0 set to zero, one per row tile or
+    fewer, have every logit equal to 0, so the lower-index rule gives blocks 0 .. n-1.  Blocks
+    of 64 tokens at Nside 32 (m = 192: the logits fit the LDS cache) and blocks of one token
+    (m = 12288: recomputed on every radix pass).  Those rows and every 8th row of slice 0 are
+    checked against the oracle."""
+    cfg = CONFIGS["ns32"].with_(name=f"ns32-b{block}", block=block, heads=1 if block == 1 else 8, topn=16,
+                                seed=321 + block)
     q, k, v, _ = _gpu_inputs(cfg)
-    gen = torch.Generator(device="cpu").manual_seed(9)
-    u = torch.randn(cfg.head_dim, generator=gen, dtype=torch.float64)
-    u = (30.0 * u / u.norm()).bfloat16().to(DEV)
-    n = cfg.n_tokens
-    keys = torch.arange(0, n, n // 32, device=DEV)[:32] + 7
-    queries = torch.arange(0, n, n // 16, device=DEV)[:16] + 3
-    k[0, 0, keys] = u
-    q[0, 0, queries] = u
+    m, B = cfg.n_blocks, cfg.block
+    qblocks = torch.arange(5, m, 96 if m < 1024 else 768)[:16]
+    tok = (qblocks[:, None] * B + torch.arange(B)[None, :]).reshape(-1).to(DEV)
+    q[0, 0, tok] = 0
     kp, kb2 = _pieces(cfg)
     qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, kpieces=kp, kbn2=kb2)
     _, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, kpieces=kp,
                                              kbn2=kb2)
     torch.cuda.synchronize()
-    qb = oracle.pool_mean(_slice(q, 0, 0), 1)
-    kb = oracle.pool_mean(_slice(k, 0, 0), 1)
-    rows = np.union1d(np.arange(0, n, 8), queries.cpu().numpy())
+    qb = oracle.pool_mean(_slice(q, 0, 0), B)
+    kb = oracle.pool_mean(_slice(k, 0, 0), B)
+    rows = np.union1d(np.arange(0, m, 8), qblocks.numpy())
     idx, gap = oracle.select_topn(qb[rows] @ kb.T, cfg.topn)
     got = sel[0, 0].cpu().numpy()[rows]
     exact = ~((gap > 0) & (gap < 1e-6))
     assert np.array_equal(got[exact], idx[exact])
-    tied = int(np.sum(np.all(np.isin(idx, keys.cpu().numpy()), axis=1)))
-    log(f"    {rows.size} rows checked, {tied} with the u keys as their whole top-16, "
-        f"{int((~exact).sum())} near ties")
-    assert tied >= 16
+    zero = np.isin(rows, qblocks.numpy())
+    assert np.array_equal(got[zero], np.tile(np.arange(cfg.topn), (int(zero.sum()), 1)))
+    log(f"    {rows.size} rows checked ({int(zero.sum())} zero-query rows), {int((~exact).sum())} near ties")
 
 
 @pytest.mark.parametrize("topn", [1, 3, 8, 13, 16])
