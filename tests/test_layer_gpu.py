@@ -23,7 +23,7 @@ import oracle
 from spherical_block_sparse_amd import BSAConfig, _lib, make_inputs, make_layer_inputs
 from spherical_block_sparse_amd.synth import to_f64
 
-from parity import log
+from parity import check_indices, log, selection_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +111,16 @@ def test_layer_forward(cfg, channels):
                            cfg.topn, cfg.window, idx=sel.cpu().numpy())
     own = oracle.layer_ref(to_f64(x), to_f64(w_in[0]), to_f64(w_out[0]), cfg.heads, cfg.head_dim, cfg.block,
                            cfg.topn, cfg.window)
+    # on the GPU's own bf16 q, k, v the selection is the oracle's bit for bit (near ties of
+    # 1e-6 aside), as in the attention's parity tests
+    near = 0
+    for bi in range(cfg.batch):
+        for hh in range(cfg.heads):
+            r = selection_ref(to_f64(q[bi, hh]), to_f64(k[bi, hh]), to_f64(v[bi, hh]), cfg.block, cfg.topn)
+            near += check_indices(sel[bi, hh].cpu().numpy(), r, cfg.topn)["near_ties"]
+    log(f"{cfg.name} selection on the GPU's q, k, v: bit-exact except {near} near-tie rows")
+    # against the oracle's own projections q, k, v may differ by one bf16 ulp, so only rows
+    # whose gap no such change can close are compared
     clear = own["gap"] > 1e-3          # rows whose selection no one-ulp input change can flip
     agree = np.all(own["idx"] == sel.cpu().numpy(), axis=-1)
     log(f"{cfg.name} selection: {int(np.sum(agree & clear))} of {int(np.sum(clear))} clear rows agree")
