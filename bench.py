@@ -279,6 +279,33 @@ def measure_layer(cfg: BSAConfig, channels: int, layers: int, steps: int) -> dic
                                 "frac_hbm_peak": co_bytes / (co_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
 
 
+def measure_ceilings() -> dict:
+    """Measured ceilings of this GPU beside the published peaks: a 4 GiB
+    device copy (the runtime's copy kernel: bytes read + written), a 4 GiB
+    float32 reduction (torch's sum: bytes read), and an 8192^3 bf16 GEMM
+    (torch.matmul, contiguous operands)."""
+    print("[bench] measured ceilings", file=sys.stderr, flush=True)
+    n = 1 << 30   # float32 elements: 4 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = time_stream(lambda: dst.copy_(src), 10)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    read_ms = time_stream(lambda: torch.sum(src, out=acc), 10)
+    del src, dst
+    g = torch.Generator(device="cuda").manual_seed(1)
+    a = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    gemm_ms = time_stream(lambda: torch.matmul(a, b, out=c), 10)
+    del a, b, c
+    torch.cuda.empty_cache()
+    nbytes = 4.0 * n
+    return {"copy_GBs": 2 * nbytes / (copy_ms * 1e-3) / 1e9, "read_GBs": nbytes / (read_ms * 1e-3) / 1e9,
+            "bf16_gemm_TFLOPs": 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
+            "published": {"hbm_GBs": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
+            "how": "4 GiB device copy (read + written bytes), 4 GiB float32 torch.sum, 8192^3 bf16 torch.matmul"}
+
+
 def measure_interp(steps: int) -> dict:
     """The lat-lon -> HEALPix interpolation: the 0.25-degree grid (721 x 1440)
     onto Nside 256 for 2 members x 16 heads (d = dv = 64, a 4 x 4 stencil)."""
@@ -367,6 +394,7 @@ def main() -> int:
     if args.layer_channels:
         layer = measure_layer(cfg, args.layer_channels, args.layers, args.steps)
         torch.cuda.empty_cache()
+    ceilings = measure_ceilings()
     interp = None
     if not args.no_interp:
         interp = measure_interp(args.steps)
@@ -438,6 +466,11 @@ def main() -> int:
         "backward": r["backward"],
         "encoder_layer": layer,
         "interpolation": interp,
+        # the fine kernel and the pool against measured ceilings (context; the roofline
+        # above uses the published peaks)
+        "measured_ceilings": dict(ceilings,
+                                  fine_frac_of_gemm=r["fine_tflops"] / ceilings["bf16_gemm_TFLOPs"],
+                                  pool_frac_of_copy=r["pool_gbs"] / ceilings["copy_GBs"]),
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

@@ -7,7 +7,13 @@
 // full resolution.  Ties go to the lower block index; the chosen indices are
 // written in ascending order.
 //
-// Design (gfx950):
+// Kernels: with the pool's bf16 pieces of k̄ and n <= 16 (the forward's
+// path), compress_select_apx_kernel ranks on approximate logits and
+// certifies every row (its own section below), handing tiles it cannot
+// settle to the float64 list kernel; otherwise the float64 kernels below
+// run alone (list n <= 16, buffered n <= 64, generic any n).
+//
+// Design of the float64 kernels (gfx950):
 //   * one workgroup = 64 query-block rows of one slice, 4 waves x 16 rows;
 //     key blocks stream through LDS 32 at a time (k̄ float64, v̄ float32)
 //     with direct global->LDS loads, double-buffered.
@@ -40,7 +46,8 @@
 //     overflow is compacted to its best n by a 128-entry bitonic network over
 //     four rows at once (register and DPP / swizzle exchanges).
 // Roofline: float64 matrix work 2*m^2*d per slice for the logits plus bf16
-// matrix work 2*m^2*d for ā·v̄; HBM traffic is only the pooled tensors, o_CG
+// matrix work 2*m^2*d for ā·v̄ (the approximate kernel: three bf16 products
+// of 2*m^2*d for the logits); HBM traffic is only the pooled tensors, o_CG
 // and the indices.
 #include "bsa_common.h"
 
