@@ -280,30 +280,34 @@ def measure_layer(cfg: BSAConfig, channels: int, layers: int, steps: int) -> dic
 
 
 def measure_ceilings() -> dict:
-    """Measured ceilings of this GPU beside the published peaks: a 4 GiB
-    device copy (the runtime's copy kernel: bytes read + written), a 4 GiB
-    float32 reduction (torch's sum: bytes read), and an 8192^3 bf16 GEMM
-    (torch.matmul, contiguous operands)."""
+    """Measured ceilings of this GPU beside the published peaks, from the
+    probes of libmosaic_probe.so: a streaming read of a 4 GiB buffer (the
+    pooling kernel's access pattern without its arithmetic) and back-to-back
+    bf16 MFMAs on register operands; plus the runtime's device copy of the
+    same buffer (bytes read + written)."""
+    from spherical_block_sparse_amd import probe
     print("[bench] measured ceilings", file=sys.stderr, flush=True)
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
     n = 1 << 30   # float32 elements: 4 GiB
     src = torch.ones(n, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(8 * cus * 64, dtype=torch.float32, device="cuda")
+    rblocks = 8 * cus * 8
+    read_ms = time_stream(lambda: probe.probe_read(src, sink, rblocks), 10)
     dst = torch.empty_like(src)
     copy_ms = time_stream(lambda: dst.copy_(src), 10)
-    acc = torch.empty((), dtype=torch.float32, device="cuda")
-    read_ms = time_stream(lambda: torch.sum(src, out=acc), 10)
     del src, dst
-    g = torch.Generator(device="cuda").manual_seed(1)
-    a = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
-    b = torch.randn((8192, 8192), generator=g, device="cuda").to(torch.bfloat16)
-    c = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
-    gemm_ms = time_stream(lambda: torch.matmul(a, b, out=c), 10)
-    del a, b, c
+    mblocks, iters = 2 * cus * 4, 4096
+    flops = probe.probe_mfma(sink, mblocks, iters)
+    mfma_ms = time_stream(lambda: probe.probe_mfma(sink, mblocks, iters), 10)
     torch.cuda.empty_cache()
     nbytes = 4.0 * n
-    return {"copy_GBs": 2 * nbytes / (copy_ms * 1e-3) / 1e9, "read_GBs": nbytes / (read_ms * 1e-3) / 1e9,
-            "bf16_gemm_TFLOPs": 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
+    return {"read_GBs": nbytes / (read_ms * 1e-3) / 1e9, "copy_GBs": 2 * nbytes / (copy_ms * 1e-3) / 1e9,
+            "bf16_mfma_TFLOPs": flops / (mfma_ms * 1e-3) / 1e12,
             "published": {"hbm_GBs": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
-            "how": "4 GiB device copy (read + written bytes), 4 GiB float32 torch.sum, 8192^3 bf16 torch.matmul"}
+            "how": (f"mosaic_probe_read over 4 GiB ({rblocks} workgroups), the runtime's 4 GiB device copy "
+                    f"(read + written bytes), mosaic_probe_mfma ({mblocks} workgroups x 4 waves x {iters} x 8 "
+                    f"v_mfma_f32_16x16x32_bf16)")}
 
 
 def measure_interp(steps: int) -> dict:
@@ -469,8 +473,8 @@ def main() -> int:
         # the fine kernel and the pool against measured ceilings (context; the roofline
         # above uses the published peaks)
         "measured_ceilings": dict(ceilings,
-                                  fine_frac_of_gemm=r["fine_tflops"] / ceilings["bf16_gemm_TFLOPs"],
-                                  pool_frac_of_copy=r["pool_gbs"] / ceilings["copy_GBs"]),
+                                  fine_frac_of_mfma=r["fine_tflops"] / ceilings["bf16_mfma_TFLOPs"],
+                                  pool_frac_of_read=r["pool_gbs"] / ceilings["read_GBs"]),
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

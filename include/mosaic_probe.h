@@ -1,0 +1,38 @@
+/* Measurement probes of libmosaic_probe.so: ceilings of the GPU that the
+ * BSA kernels' roofline fractions are read against, beside the published
+ * peaks.  Not part of the attention method (see mosaic_bsa.h for that).
+ *
+ * Conventions: device pointers owned by the caller; every call only enqueues
+ * work on `stream` (a hipStream_t, NULL = the legacy default stream) and
+ * returns a hipError_t value (0 = hipSuccess; hipErrorInvalidValue for a
+ * NULL pointer, a misaligned buffer or a non-positive count, checked before
+ * any launch).  The result of a probe is its duration, which the caller
+ * times with events on the same stream. */
+#ifndef MOSAIC_PROBE_H
+#define MOSAIC_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Streaming read of `bytes` (a multiple of 16) at `buf` (16-byte aligned) by
+ * `blocks` workgroups of 256 threads: 16-byte nontemporal loads, eight in
+ * flight per lane, consecutive workgroups on consecutive 4 KB spans.  `sink`
+ * (float32 [blocks]) is written only in a case that does not occur; it
+ * keeps the loads from being dropped. */
+int mosaic_probe_read(const void* buf, size_t bytes, float* sink, int blocks, void* stream);
+
+/* `blocks` workgroups of four waves, each wave issuing `iters` x 8
+ * independent v_mfma_f32_16x16x32_bf16 on register operands: 16384 FLOPs
+ * per instruction, blocks * 4 * iters * 8 instructions in all.  `sink`
+ * (float32 [blocks]) as above. */
+int mosaic_probe_mfma(float* sink, int blocks, int iters, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOSAIC_PROBE_H */

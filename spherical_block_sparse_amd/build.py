@@ -3,7 +3,9 @@
     python -m spherical_block_sparse_amd.build          # always rebuilds
 
 Each HIP source is compiled to an object in parallel, then linked into
-spherical_block_sparse_amd/libmosaic_bsa.so.  Packed fp32 VALU instructions
+spherical_block_sparse_amd/libmosaic_bsa.so (the BSA library, include/
+mosaic_bsa.h) and spherical_block_sparse_amd/libmosaic_probe.so (the
+measurement probes, include/mosaic_probe.h).  Packed fp32 VALU instructions
 are disabled (-packed-fp32-ops).
 """
 
@@ -20,6 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmosaic_bsa.so")
+PROBE_LIB = os.path.join(PKG, "libmosaic_probe.so")
+PROBE_SOURCES = ["peak_probe.hip"]
 
 SOURCES = ["bsa_pool.hip", "bsa_compress_select.hip", "bsa_fine.hip", "bsa_backward.hip", "bsa_layer.hip",
            "healpix_coarsen.hip", "healpix_interp.hip", "bsa_scratch.hip", "mosaic_bsa_api.cpp"]
@@ -60,18 +64,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs: list) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(LIB, objs[:len(SOURCES)])
+    _link(PROBE_LIB, objs[len(SOURCES):])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -59,6 +59,24 @@ def test_header_declares_and_library_exports_the_same_symbols():
         assert hasattr(L, name)
 
 
+def test_probe_header_declares_and_library_exports_the_same_symbols():
+    """libmosaic_probe.so (the measurement probes) exports what include/mosaic_probe.h
+    declares, and rejects bad arguments before any launch."""
+    from spherical_block_sparse_amd import probe
+    L = probe.lib()
+    with open(os.path.join(ROOT, "include", "mosaic_probe.h")) as f:
+        declared = set(re.findall(r"^int (mosaic_probe_\w+)\(", f.read(), flags=re.M))
+    assert declared == set(probe.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name)
+    INVALID = 1   # hipErrorInvalidValue
+    assert L.mosaic_probe_read(None, 1024, FAKE, 4, None) == INVALID
+    assert L.mosaic_probe_read(FAKE + 8, 1024, FAKE, 4, None) == INVALID
+    assert L.mosaic_probe_read(FAKE, 1024, FAKE, 0, None) == INVALID
+    assert L.mosaic_probe_mfma(None, 4, 4, None) == INVALID
+    assert L.mosaic_probe_mfma(FAKE, 4, 0, None) == INVALID
+
+
 def test_version_and_status_strings():
     L = _lib.lib()
     hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mosaic_bsa.h")
