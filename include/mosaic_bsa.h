@@ -106,7 +106,7 @@ mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, co
  * first call on a device looks up that device's copy.  Sizes whose
  * workspace (mosaic_bsa_workspace_bytes) exceeds 256 MiB return
  * MOSAIC_ERR_UNSUPPORTED before any HIP call: e.g. batch 2 x 16 heads at
- * nside 256 (152 MB) fit, batch 24 x 8 heads at nside 128 (1.06 GB) do
+ * nside 256 (177 MB) fit, batch 24 x 8 heads at nside 128 (1.06 GB) do
  * not.  Every call on one GPU shares that GPU's scratch, which keeps the
  * last call's contents: calls that overlap on one GPU (other streams or
  * threads without ordering between them) race.  Arguments, outputs and

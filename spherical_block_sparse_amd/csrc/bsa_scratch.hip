@@ -2,9 +2,9 @@
 //
 // mosaic_bsa_forward_noalloc serves callers that cannot allocate device
 // memory (code under HIP graph capture, tight serving loops, harnesses that
-// forbid hipMalloc).  Its workspace (pooled q̄, k̄, v̄, o_CG and the per-block
-// largest key norms) lives in the file-scope array below instead of a
-// caller buffer.  Each GPU gets its own copy when this code object is loaded
+// forbid hipMalloc).  Its workspace (pooled q̄, k̄, v̄, o_CG, the per-block
+// largest key norms, k̄'s bf16 pieces and |k̄_j|^2) lives in the file-scope
+// array below instead of a caller buffer.  Each GPU gets its own copy when this code object is loaded
 // on it and keeps it until the process ends.  Host code never uses the
 // array's name as a device address: the address comes from
 // hipGetSymbolAddress, looked up once per device with that device current
