@@ -300,10 +300,15 @@ def measure_ceilings() -> dict:
     mblocks, iters = 2 * cus * 4, 4096
     flops = probe.probe_mfma(sink, mblocks, iters)
     mfma_ms = time_stream(lambda: probe.probe_mfma(sink, mblocks, iters), 10)
+    clk = torch.zeros((mblocks, 2), dtype=torch.int64, device="cuda")
+    probe.probe_mfma(sink, mblocks, iters, clk)
+    c = clk.double().sum(0).cpu()
+    mfma_ghz = float(c[0] / c[1]) * 0.1   # shader clocks per 100 MHz tick
     torch.cuda.empty_cache()
     nbytes = 4.0 * n
     return {"read_GBs": nbytes / (read_ms * 1e-3) / 1e9, "copy_GBs": 2 * nbytes / (copy_ms * 1e-3) / 1e9,
-            "bf16_mfma_TFLOPs": flops / (mfma_ms * 1e-3) / 1e12,
+            "bf16_mfma_TFLOPs": flops / (mfma_ms * 1e-3) / 1e12, "mfma_probe_clock_GHz": mfma_ghz,
+            "bf16_mfma_TFLOPs_per_GHz": flops / (mfma_ms * 1e-3) / 1e12 / mfma_ghz,
             "published": {"hbm_GBs": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
             "how": (f"mosaic_probe_read over 4 GiB ({rblocks} workgroups), the runtime's 4 GiB device copy "
                     f"(read + written bytes), mosaic_probe_mfma ({mblocks} workgroups x 4 waves x {iters} x 8 "

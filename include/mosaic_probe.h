@@ -28,8 +28,11 @@ int mosaic_probe_read(const void* buf, size_t bytes, float* sink, int blocks, vo
 /* `blocks` workgroups of four waves, each wave issuing `iters` x 8
  * independent v_mfma_f32_16x16x32_bf16 on register operands: 16384 FLOPs
  * per instruction, blocks * 4 * iters * 8 instructions in all.  `sink`
- * (float32 [blocks]) as above. */
-int mosaic_probe_mfma(float* sink, int blocks, int iters, void* stream);
+ * (float32 [blocks]) as above.  `clocks` (may be NULL): uint64
+ * [blocks][2], each workgroup's elapsed shader clocks (s_memtime) and
+ * 100 MHz ticks (s_memrealtime) over its run; their ratio x 100 MHz is the
+ * shader clock it ran at. */
+int mosaic_probe_mfma(float* sink, int blocks, int iters, unsigned long long* clocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -52,6 +52,9 @@ EXTRA = {
     "bsa_fine.hip": ["-fno-honor-nans"],
     "bsa_backward.hip": ["-fno-honor-nans"],
     "bsa_compress_select.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the MFMA probe's loop is then its eight MFMAs alone (with AGPR
+    # accumulators the compiler rotates them through VGPRs every iteration)
+    "peak_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

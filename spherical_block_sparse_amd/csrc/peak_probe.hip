@@ -9,7 +9,9 @@
 //     consecutive 4 KB spans (the access pattern of the pooling kernel,
 //     without its arithmetic).
 //   * mosaic_probe_mfma: back-to-back v_mfma_f32_16x16x32_bf16 on register
-//     operands, eight independent accumulators per wave (no loads at all).
+//     operands, eight independent accumulators per wave (no loads at all);
+//     optionally each workgroup's shader clocks (s_memtime) and 100 MHz
+//     ticks (s_memrealtime) over its run, which give the clock it ran at.
 // Each folds what it computed into one value per workgroup, written only
 // when it equals a value it never takes, so the work cannot be dropped.
 #include "mosaic_probe.h"
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* p, size_t 
   if (acc == 0x7f8badc0u) sink[blockIdx.x] = __uint_as_float(acc);
 }
 
-__global__ __launch_bounds__(256) void probe_mfma_kernel(float* sink, int iters) {
+__global__ __launch_bounds__(256) void probe_mfma_kernel(float* sink, int iters, unsigned long long* clocks) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   bf16x8 a, b;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -57,6 +60,10 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float* sink, int iters)
 #pragma unroll
   for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
   if (s == -1234.5f) sink[blockIdx.x] = s;
+  if (clocks && threadIdx.x == 0) {   // shader clocks and 100 MHz ticks of wave 0's run
+    clocks[2 * blockIdx.x] = __builtin_amdgcn_s_memtime() - t0;
+    clocks[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime() - r0;
+  }
 }
 
 }  // namespace
@@ -71,10 +78,10 @@ int mosaic_probe_read(const void* buf, size_t bytes, float* sink, int blocks, vo
   return (int)hipGetLastError();
 }
 
-int mosaic_probe_mfma(float* sink, int blocks, int iters, void* stream) {
+int mosaic_probe_mfma(float* sink, int blocks, int iters, unsigned long long* clocks, void* stream) {
   if (!sink || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     sink, iters);
+                     sink, iters, clocks);
   return (int)hipGetLastError();
 }
 

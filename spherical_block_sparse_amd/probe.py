@@ -25,7 +25,7 @@ def lib() -> ctypes.CDLL:
         L.mosaic_probe_read.restype = I
         L.mosaic_probe_read.argtypes = [P, S, P, I, P]
         L.mosaic_probe_mfma.restype = I
-        L.mosaic_probe_mfma.argtypes = [P, I, I, P]
+        L.mosaic_probe_mfma.argtypes = [P, I, I, P, P]
         _probe = L
     return _probe
 
@@ -44,9 +44,12 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
                                    torch.cuda.current_stream().cuda_stream), "mosaic_probe_read")
 
 
-def probe_mfma(sink: torch.Tensor, blocks: int, iters: int) -> float:
-    """Back-to-back bf16 MFMAs; returns the FLOPs the launch performs."""
+def probe_mfma(sink: torch.Tensor, blocks: int, iters: int, clocks: torch.Tensor | None = None) -> float:
+    """Back-to-back bf16 MFMAs; returns the FLOPs the launch performs.  clocks (int64 [blocks, 2]),
+    if given, receives each workgroup's shader clocks and 100 MHz ticks."""
     assert sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= blocks
-    _check(lib().mosaic_probe_mfma(sink.data_ptr(), blocks, iters, torch.cuda.current_stream().cuda_stream),
-           "mosaic_probe_mfma")
+    if clocks is not None:
+        assert clocks.is_cuda and clocks.dtype == torch.int64 and clocks.numel() >= 2 * blocks
+    _check(lib().mosaic_probe_mfma(sink.data_ptr(), blocks, iters, None if clocks is None else clocks.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream), "mosaic_probe_mfma")
     return float(blocks) * 4 * iters * 8 * 16384
