@@ -383,7 +383,7 @@ def main() -> int:
     ap.add_argument("--no-interp", action="store_true", help="skip the interpolation timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the BSA slices are independent and this build has no "
+        print("bench.py measures one GPU: the BSA slices are independent and the library has no "
               "multi-GPU path (batch/head slices would shard across GPUs with no communication). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2

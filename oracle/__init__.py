@@ -7,7 +7,7 @@ only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may call it.  It shares no code with the HIP library
 (``spherical_block_sparse_amd``) and imports nothing from it.
 
-What it follows (the pages this build is written from):
+What it follows (the pages the method is taken from):
 
 * papernotes.org ICML2026 notes on "(Sparse) Attention to the Details",
   section 关键设计 (key designs), items "HEALPix 球面镶嵌 + NESTED 索引" and
