@@ -607,3 +607,25 @@ def test_block_one_ns32_one_head():
     lane-list selection, the generic fine kernel on 16 single-token blocks
     plus the window."""
     _edge(CONFIGS["ns32"].with_(name="ns32-b1", block=1, heads=1, seed=321))
+
+
+# The smallest spheres: Nside 1 (the 12 base pixels, blocks of one token,
+# m = 12) and Nside 2 (48 tokens, blocks of 1 or 4), so that a row tile, a
+# key chunk and a window are each larger than the whole sphere.
+SMALLEST = [
+    BSAConfig("s1-b1-top1-w1", 1, 2, 2, 64, 1, 1, 1, "iid", 101),
+    BSAConfig("s1-b1-top12-w12-d32", 1, 2, 2, 32, 1, 12, 12, "iid", 102),
+    BSAConfig("s1-b1-top5-w7", 1, 2, 2, 64, 1, 5, 7, "iid", 103),
+    BSAConfig("s2-b4-top12-w48", 2, 2, 2, 64, 4, 12, 48, "iid", 104),
+    BSAConfig("s2-b4-top3-w5-d32", 2, 2, 2, 32, 4, 3, 5, "iid", 105),
+    BSAConfig("s2-b1-top48-w20", 2, 2, 2, 64, 1, 48, 20, "iid", 106),
+    BSAConfig("s2-b1-top20-w9", 2, 2, 2, 64, 1, 20, 9, "iid", 107),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALLEST, ids=lambda c: c.name)
+def test_edge_smallest_spheres(cfg):
+    _, *_, idx = _edge(cfg)
+    if cfg.topn == cfg.n_blocks:   # every row selects every block, in ascending order
+        want = torch.arange(cfg.n_blocks, dtype=torch.int32).expand(cfg.batch, cfg.heads, cfg.n_blocks, cfg.n_blocks)
+        assert torch.equal(idx.cpu(), want)
