@@ -508,8 +508,9 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
 //     are unchanged in structure (o_CG uses the approximate logits; its
 //     weights are rounded to bf16 anyway).
 //   * every key a lane's list lets go -- not inserted, evicted, or dropped by
-//     the final merges -- updates the row's largest dropped value R.  The
-//     merges keep the best 32 of the row.  A row is certified when
+//     the final merges -- updates the row's largest dropped value R.  Each
+//     lane lists its best K keys (K = 8 for n <= 8, else 16) and the merges
+//     keep the best 2K of the row.  A row is certified when
 //     R < s~_(n) - 2ε: every dropped key is then below the exact n-th logit.
 //     Keys above s~_(n) + 2ε are in the top n, keys below s~_(n) - 2ε are
 //     out, and the few in between are rescored in float64 (the same fused
@@ -817,10 +818,12 @@ __device__ __forceinline__ void issue_pieces(int c0, uint16_t* pb, float* vb, co
 }
 
 // Three waves per SIMD (at most 168 VGPRs, a few spilled in the epilogue)
-// run the stage about 15% faster than two.
-template <int D>
+// run the stage about 15% faster than two.  K list entries per lane while
+// streaming: 8 for top-n <= 8 (the merged 16 still leave 8 places past the
+// n-th for its band), 16 otherwise.
+template <int D, int K>
 __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
-  constexpr int K = 16;                  // list entries per lane while streaming
+  static_assert(K == 8 || K == 16, "list depth");
   constexpr int H = D / 32;              // 32-wide halves of d
   constexpr int PE = 2 * D;              // bf16 per row of pieces
   constexpr int kStage = kCols * D * 16;   // bytes: two chunks of pieces and of v̄
@@ -1466,8 +1469,13 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
   a.redo = 0;
   const dim3 grid((unsigned)(slices * a.row_tiles));
   if (topn <= 16 && kpieces && kbn2) {   // approximate logits, certified; crowded tiles redone in float64
-    if (head_dim == 64) hipLaunchKernelGGL(compress_select_apx_kernel<64>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(compress_select_apx_kernel<32>, grid, dim3(256), 0, stream, a);
+    if (head_dim == 64) {
+      if (topn <= 8) hipLaunchKernelGGL((compress_select_apx_kernel<64, 8>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((compress_select_apx_kernel<64, 16>), grid, dim3(256), 0, stream, a);
+    } else {
+      if (topn <= 8) hipLaunchKernelGGL((compress_select_apx_kernel<32, 8>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((compress_select_apx_kernel<32, 16>), grid, dim3(256), 0, stream, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.redo = 1;
