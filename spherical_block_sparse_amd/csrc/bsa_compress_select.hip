@@ -507,10 +507,9 @@ __global__ __launch_bounds__(256) void compress_select_list_kernel(CSArgs a) {
 //     the float64 kernel has it: the online softmax, ā·v̄ and the lane lists
 //     are unchanged in structure (o_CG uses the approximate logits; its
 //     weights are rounded to bf16 anyway).
-//   * every key a lane's list lets go -- not inserted, evicted, or dropped by
-//     the final merges -- updates the row's largest dropped value R.  Each
-//     lane lists its best K keys (K = 8 for n <= 8, else 16) and the merges
-//     keep the best 2K of the row.  A row is certified when
+//   * every key a lane's list lets go -- not inserted or evicted -- updates
+//     the row's largest dropped value R.  Each lane lists its best 8 keys and
+//     the merges keep all 32 of the row.  A row is certified when
 //     R < s~_(n) - 2ε: every dropped key is then below the exact n-th logit.
 //     Keys above s~_(n) + 2ε are in the top n, keys below s~_(n) - 2ε are
 //     out, and the few in between are rescored in float64 (the same fused
@@ -817,13 +816,15 @@ __device__ __forceinline__ void issue_pieces(int c0, uint16_t* pb, float* vb, co
   }
 }
 
-// Three waves per SIMD (at most 168 VGPRs, a few spilled in the epilogue)
-// run the stage about 15% faster than two.  K list entries per lane while
-// streaming: 8 for top-n <= 8 (the merged 16 still leave 8 places past the
-// n-th for its band), 16 otherwise.
-template <int D, int K>
+// Three waves per SIMD (at most 168 VGPRs) run the stage about 15% faster
+// than two.  Each lane lists its best eight keys while streaming, and the
+// final merges keep all 32 of the row's four lists.  A lane holds about a
+// quarter of its row's top n, so eight rarely drops one (and a row whose
+// lane did is not certified).  Sixteen per lane, the best 32 kept, ran
+// 6% slower at top-16 and 20% slower at top-8.
+template <int D>
 __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
-  static_assert(K == 8 || K == 16, "list depth");
+  constexpr int K = 8;                   // list entries per lane while streaming
   constexpr int H = D / 32;              // 32-wide halves of d
   constexpr int PE = 2 * D;              // bf16 per row of pieces
   constexpr int kStage = kCols * D * 16;   // bytes: two chunks of pieces and of v̄
@@ -985,7 +986,7 @@ __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
 
   store_ocg<D>(a.o_cg + ((size_t)slice * m + row) * D, oacc, l_run, lg, row < m);
 
-  // the row's best 2K: merge the lane groups pairwise (first without loss)
+  // the row's 4K keys: merge the lane groups pairwise, without loss
   constexpr int L = 2 * K;
   float lv[L];
   int li[L];
@@ -1000,6 +1001,10 @@ __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
     bitonic_merge_f<L>(lv, li);
   }
   rej = fmaxf(rej, __shfl_xor(rej, 16));
+  // the row's best 32 (kept in every lane of the row)
+  constexpr int LF = 32;
+  float fv[LF];
+  int fi[LF];
   {
     float pv[L];
     int pi[L];
@@ -1008,32 +1013,30 @@ __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
       pv[j] = __shfl_xor(lv[j], 32);
       pi[j] = __shfl_xor(li[j], 32);
     }
-    // the better of lv[j] and pv[L-1-j] is the best L as a bitonic sequence;
-    // the worse ones are dropped
+    static_assert(2 * L == LF, "the two halves fill the final list");
+    // the partner's list reversed makes one bitonic sequence, merged without loss
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-      const bool take = beats_f(pv[L - 1 - j], pi[L - 1 - j], lv[j], li[j]);
-      rej = fmaxf(rej, take ? lv[j] : pv[L - 1 - j]);
-      if (take) {
-        lv[j] = pv[L - 1 - j];
-        li[j] = pi[L - 1 - j];
-      }
+      fv[j] = lv[j];
+      fi[j] = li[j];
+      fv[LF - 1 - j] = pv[j];
+      fi[LF - 1 - j] = pi[j];
     }
-    bitonic_merge_f<L>(lv, li);
+    bitonic_merge_f<LF>(fv, fi);
   }
   rej = fmaxf(rej, __shfl_xor(rej, 32));
 
   // certification and the band around the n-th value
-  float vn = lv[0];
+  float vn = fv[0];
 #pragma unroll
   for (int j = 1; j < 16; ++j)
-    if (j == n - 1) vn = lv[j];
+    if (j == n - 1) vn = fv[j];
   const float band_lo = vn - 2.0f * eps, band_hi = vn + 2.0f * eps;
   int above = 0, inband = 0;
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    above += lv[j] > band_hi ? 1 : 0;
-    inband += (lv[j] >= band_lo && lv[j] <= band_hi) ? 1 : 0;
+  for (int j = 0; j < LF; ++j) {
+    above += fv[j] > band_hi ? 1 : 0;
+    inband += (fv[j] >= band_lo && fv[j] <= band_hi) ? 1 : 0;
   }
   static_assert(16 + kBandMax <= 32, "result slots");
   bool ok = rej < band_lo && inband <= kBandMax;
@@ -1048,8 +1051,8 @@ __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
     int v = 0x7fffffff;
     if (t < bmax) {
 #pragma unroll
-      for (int j = 0; j < L; ++j)
-        if (j == above + t) v = li[j];
+      for (int j = 0; j < LF; ++j)
+        if (j == above + t) v = fi[j];
     }
     bidx[t] = t < inband ? v : 0x7fffffff;
   }
@@ -1076,7 +1079,7 @@ __global__ __launch_bounds__(256, 3) void compress_select_apx_kernel(CSArgs a) {
   const int need = n - above;
   int ix[32];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) ix[j] = j < above ? li[j] : 0x7fffffff;
+  for (int j = 0; j < 16; ++j) ix[j] = j < above ? fi[j] : 0x7fffffff;
 #pragma unroll
   for (int t = 0; t < kBandMax; ++t) {
     int rank = 0;
@@ -1469,13 +1472,8 @@ hipError_t launch_compress_select(const double* qbar, const double* kbar, const 
   a.redo = 0;
   const dim3 grid((unsigned)(slices * a.row_tiles));
   if (topn <= 16 && kpieces && kbn2) {   // approximate logits, certified; crowded tiles redone in float64
-    if (head_dim == 64) {
-      if (topn <= 8) hipLaunchKernelGGL((compress_select_apx_kernel<64, 8>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((compress_select_apx_kernel<64, 16>), grid, dim3(256), 0, stream, a);
-    } else {
-      if (topn <= 8) hipLaunchKernelGGL((compress_select_apx_kernel<32, 8>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((compress_select_apx_kernel<32, 16>), grid, dim3(256), 0, stream, a);
-    }
+    if (head_dim == 64) hipLaunchKernelGGL(compress_select_apx_kernel<64>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(compress_select_apx_kernel<32>, grid, dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.redo = 1;
