@@ -17,7 +17,8 @@ import torch
 import oracle
 from spherical_block_sparse_amd import CONFIGS, BSAConfig, make_inputs
 from spherical_block_sparse_amd import _lib
-from spherical_block_sparse_amd.synth import to_f64
+from spherical_block_sparse_amd.locality_study import permute_tokens
+from spherical_block_sparse_amd.synth import nest_ring_order, to_f64
 
 import oracle_jobs
 from parity import MAX_ABS, NEAR_TIE, REL_L2, assert_close, check_indices, log, ocg_tolerance, selection_ref
@@ -307,13 +308,16 @@ def _bits(x):
     return x.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _full_size(cfg: BSAConfig, n_out_slices=None):
+def _full_size(cfg: BSAConfig, n_out_slices=None, ring=False):
     """The workload in the bench's launch configuration (whole batch, one
     forward call): every index row of every slice against the oracle's
     selection, and every output element of ``n_out_slices`` seeded slices
     (first and last included; all slices when None) against the oracle run
-    with the GPU's indices.  The oracle runs in a pool of host processes."""
+    with the GPU's indices.  The oracle runs in a pool of host processes.
+    ``ring`` lays the same field out in RING (iso-latitude) token order."""
     q, k, v, g = _gpu_inputs(cfg)
+    if ring:
+        q, k, v, g = permute_tokens([q, k, v, g], nest_ring_order(cfg.nside))
     need = _lib.mosaic_bsa_workspace_bytes(cfg.batch, cfg.heads, cfg.head_dim, cfg.nside, cfg.block, cfg.topn)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     out, idx = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window, workspace=ws)
@@ -368,6 +372,16 @@ def _full_size(cfg: BSAConfig, n_out_slices=None):
 def test_forward_ns64_every_slice():
     """ns64: every index row and every output element of all 32 slices."""
     _full_size(CONFIGS["ns64"])
+
+
+def test_forward_ns64_ring_order_every_row():
+    """The ns64 field in RING token order: a block is then a strip of one
+    iso-latitude ring, and the logits of neighbouring strips crowd within
+    the approximate selection's error bound on many rows, so the exact
+    in-workgroup fallback and the float64 redo of crowded tiles carry much
+    of the selection.  Every index row of all 32 slices, and 4 whole output
+    slices, against the oracle."""
+    _full_size(CONFIGS["ns64"], n_out_slices=4, ring=True)
 
 
 def test_forward_ns128_full_size():
