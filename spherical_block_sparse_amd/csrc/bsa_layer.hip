@@ -180,6 +180,23 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs p, const floatx4 
     return;
   }
   constexpr int RS = 64 + 4;   // floats per staged row
+  const int cl = lane % 16;             // 16-byte piece (4 features) of the row
+  const int fl = fw + 4 * cl;           // this lane's first feature
+  const bool f_ok = fl < p.F;
+  const int r0 = lane / 16;             // first row of this lane; rows r0, r0 + 4, ...
+  const long long mw = m0 + 64 * wm;    // the wave's first token
+  const long long rows_left = p.M - mw; // rows of the wave that exist
+  // OUT: the residual rows this lane adds, all loaded before anything is
+  // stored (x and y may alias as far as the compiler knows, so loads issued
+  // between the stores would each wait for the one before)
+  ushort4 xr[16];
+  if constexpr (OUT) {
+    const uint16_t* xp = p.x + (mw + r0) * p.F + fl;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      xr[i] = 4 * i + r0 < rows_left && f_ok ? *reinterpret_cast<const ushort4*>(xp + 4LL * i * p.F)
+                                             : make_ushort4(0, 0, 0, 0);
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -187,12 +204,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs p, const floatx4 
       *reinterpret_cast<floatx4*>(lds + (16 * mt + lr) * RS + 16 * ft + 4 * lg) = acc[ft][mt];
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own LDS writes are done
   __builtin_amdgcn_wave_barrier();
-  const int cl = lane % 16;             // 16-byte piece (4 features) of the row
-  const int fl = fw + 4 * cl;           // this lane's first feature
-  const bool f_ok = fl < p.F;
   // the wave's first token: batch element bw, position tw (a tile spans at
   // most two batch elements per wave: 64 rows, N >= 192)
-  const long long mw = m0 + 64 * wm;
   long long bw = bi0;
   int tw = t0 + 64 * wm;
   if (tw >= p.n_tok) {
@@ -200,12 +213,10 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs p, const floatx4 
     bw += 1;
   }
   // per-row global pointers: rows before the batch boundary, and after it
-  const uint16_t* xrow = nullptr;
   uint16_t* row0 = nullptr;
   uint16_t* row1 = nullptr;
   int step = 0;
   if constexpr (OUT) {
-    xrow = p.x + mw * p.F + fl;
     row0 = p.y + mw * p.F + fl;
     step = p.F;
   } else {
@@ -216,10 +227,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs p, const floatx4 
     step = p.head_dim;
   }
   const int split = p.n_tok - tw;       // rows from here on belong to batch element bw + 1
-  const int r0 = lane / 16;             // first row of this lane; rows r0, r0 + 4, ...
-  const long long rows_left = p.M - mw; // rows of the wave that exist
   if (OUT || split >= 64) {             // one batch element: pointers advance by 4 rows
-    const uint16_t* xp = xrow + (long long)r0 * step;
     uint16_t* yp = row0 + (long long)r0 * step;
     const long long adv = 4LL * step;
 #pragma unroll
@@ -229,17 +237,15 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs p, const floatx4 
         const floatx4 r = *reinterpret_cast<const floatx4*>(lds + row * RS + 4 * cl);
         ushort4 o;
         if constexpr (OUT) {
-          const ushort4 xr = *reinterpret_cast<const ushort4*>(xp);
-          o.x = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.x << 16) + r[0]);
-          o.y = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.y << 16) + r[1]);
-          o.z = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.z << 16) + r[2]);
-          o.w = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr.w << 16) + r[3]);
+          o.x = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr[i].x << 16) + r[0]);
+          o.y = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr[i].y << 16) + r[1]);
+          o.z = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr[i].z << 16) + r[2]);
+          o.w = bf16_rne(__builtin_bit_cast(float, (uint32_t)xr[i].w << 16) + r[3]);
         } else {
           o.x = bf16_rne(r[0]); o.y = bf16_rne(r[1]); o.z = bf16_rne(r[2]); o.w = bf16_rne(r[3]);
         }
         *reinterpret_cast<ushort4*>(yp) = o;
       }
-      if constexpr (OUT) xp += adv;
       yp += adv;
     }
     return;
