@@ -139,6 +139,31 @@ def time_stream(fn, steps: int) -> float:
     return start.elapsed_time(stop) / steps
 
 
+def time_steps(fn, steps: int) -> tuple:
+    """Mean milliseconds of fn() over `steps` calls, as time_stream, plus each
+    call's own duration: an event is recorded between consecutive calls on the
+    same stream (no synchronisation inside the timed region)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, per
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> dict:
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     q, k, v, g = make_inputs(cfg, device="cuda", dtype=torch.bfloat16)
@@ -156,7 +181,7 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
         fwd()
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
-    ms = time_stream(fwd, steps)
+    ms, per_step = time_steps(fwd, steps)
 
     # per-kernel durations through the stage entry points (same kernels)
     qbar = torch.empty((b, h, m, d), dtype=torch.float64, device=dev)
@@ -219,6 +244,7 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
         del dout, grads, dgates, bws, saved, out_t, sel_t
     res = dict(backward=bwd,
         cfg=cfg, ms=ms, tokens_per_s=cfg.tokens / (ms * 1e-3),
+        step_ms={"median": float(np.median(per_step)), "min": min(per_step), "max": max(per_step)},
         pool_ms=pool_ms, cs_ms=cs_ms, fine_ms=fine_ms, stages_match_forward=same,
         fine_tflops=ff / (fine_ms * 1e-3) / 1e12, fine_flops=ff,
         pool_gbs=pool_bytes(cfg) / (pool_ms * 1e-3) / 1e9, pool_bytes=pool_bytes(cfg),
@@ -365,7 +391,7 @@ def cpu_baseline(cfg: BSAConfig, inputs, budget_s: float) -> dict:
     return {"value": tok_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {cfg.slices} (batch, head) slices of the {cfg.name} inputs, "
                       f"{t_total:.1f} s, scaled by 1/heads to whole tokens",
-            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": host_cpu_model()}
 
 
 def main() -> int:
@@ -419,6 +445,7 @@ def main() -> int:
         del s["inputs"]
         secondary = {
             "workload": s["cfg"].name, "value": s["tokens_per_s"], "unit": "tokens/s", "ms_per_step": s["ms"],
+            "step_ms": s["step_ms"],
             "kernels_ms": {"pool": s["pool_ms"], "compress_select": s["cs_ms"], "fine": s["fine_ms"]},
             "fine_mfma_frac": s["fine_tflops"] / PEAK_BF16_TFLOPS,
             "compress_select_frac": compress_bound_ms(s["cfg"]) / s["cs_ms"],
@@ -436,6 +463,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": r["ms"],
+        # each timed call's own duration (events between consecutive calls)
+        "step_ms": r["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
