@@ -178,3 +178,23 @@ def test_counters_sum_rows_of_a_dispatch(tmp_path):
     assert len(lines) == 4   # header, two dispatches, mean
     assert lines[1].split()[-1] == "15" and lines[2].split()[-1] == "25"
     assert lines[3].split()[-1] == "20"
+
+
+def test_random_shape_draw_is_valid_and_varied():
+    """The seeded shapes of the random-shape GPU test are valid forward
+    arguments and reach every kernel path: blocks below 16 (one-wave fine
+    kernel), top-n above 16 and above 64 (list, buffered and radix
+    selection), both head dims, windows of one token and past the sphere."""
+    from test_random_shapes_gpu import CASES
+    assert len({c.name for c in CASES}) == len(CASES)
+    for c in CASES:
+        n_tok = 12 * c.nside ** 2
+        assert c.block & (c.block - 1) == 0 and (c.block.bit_length() - 1) % 2 == 0
+        assert 1 <= c.block <= c.nside ** 2
+        assert 1 <= c.topn <= n_tok // c.block
+        assert c.window >= 1 and c.head_dim in (32, 64)
+    assert any(c.block < 16 for c in CASES) and any(c.block >= 16 for c in CASES)
+    assert any(c.topn > 16 for c in CASES) and any(c.topn <= 16 for c in CASES)
+    assert any(c.topn > 64 for c in CASES)
+    assert {c.head_dim for c in CASES} == {32, 64}
+    assert any(c.window == 1 for c in CASES) and any(c.window > 2 * 12 * c.nside ** 2 for c in CASES)
