@@ -442,19 +442,30 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
     branch(1, nc, [&](int ci) { return wlo + ci * 64; }, [&](int ci) { return min(64, whi - wlo - ci * 64); });
   }
 
-  // epilogue: dq = dQ^T / sqrt(d) (+ the pooled gradient / block)
+  // epilogue: dq = dQ^T / sqrt(d) (+ the pooled gradient / block).  The
+  // pooled rows are all loaded before the first store: the compiler cannot
+  // rule out that they alias dq, so a load written after a store stays
+  // behind it, latency exposed.
+  float4 addp[2][DT];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int t = tw + 16 * s + lr;
+    const float* add = a.addq ? a.addq + ((size_t)slice * m + t / B) * D : nullptr;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      addp[s][dt] = add ? *reinterpret_cast<const float4*>(add + dt * 16 + 4 * lg) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int t = tw + 16 * s + lr;
     float* dst = a.dq + sb + (size_t)t * D;
-    const float* add = a.addq ? a.addq + ((size_t)slice * m + t / B) * D : nullptr;
     const float ab = 1.f / B;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       float4 r = make_float4(dqa[s][dt][0] * a.inv_sqrt_d, dqa[s][dt][1] * a.inv_sqrt_d,
                              dqa[s][dt][2] * a.inv_sqrt_d, dqa[s][dt][3] * a.inv_sqrt_d);
-      if (add) {
-        const float4 p = *reinterpret_cast<const float4*>(add + dt * 16 + 4 * lg);
+      if (a.addq) {
+        const float4 p = addp[s][dt];
         r.x += p.x * ab; r.y += p.y * ab; r.z += p.z * ab; r.w += p.w * ab;
       }
       *reinterpret_cast<float4*>(dst + dt * 16 + 4 * lg) = r;
@@ -615,25 +626,36 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
           [&](int ci) { return min(64, thi - tlo - ci * 64); }, std::integral_constant<bool, true>{});
   }
 
-  // epilogue: dk = dK^T / sqrt(d), dv = dV^T (+ pooled gradients / block)
+  // epilogue: dk = dK^T / sqrt(d), dv = dV^T (+ pooled gradients / block),
+  // every pooled row loaded before the first store (as in the dq kernel)
   const int m = a.m;
+  float4 addkp[2][DT], addvp[2][DT];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int u = uw + 16 * s + lr;
+    const float* addk = a.addk ? a.addk + ((size_t)slice * m + u / B) * D : nullptr;
+    const float* addv = a.addv ? a.addv + ((size_t)slice * m + u / B) * D : nullptr;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      addkp[s][dt] = addk ? *reinterpret_cast<const float4*>(addk + dt * 16 + 4 * lg) : make_float4(0.f, 0.f, 0.f, 0.f);
+      addvp[s][dt] = addv ? *reinterpret_cast<const float4*>(addv + dt * 16 + 4 * lg) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int u = uw + 16 * s + lr;
     const float ab = 1.f / B;
-    const float* addk = a.addk ? a.addk + ((size_t)slice * m + u / B) * D : nullptr;
-    const float* addv = a.addv ? a.addv + ((size_t)slice * m + u / B) * D : nullptr;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       float4 rk = make_float4(dka[s][dt][0] * a.inv_sqrt_d, dka[s][dt][1] * a.inv_sqrt_d,
                               dka[s][dt][2] * a.inv_sqrt_d, dka[s][dt][3] * a.inv_sqrt_d);
       float4 rv = make_float4(dva[s][dt][0], dva[s][dt][1], dva[s][dt][2], dva[s][dt][3]);
-      if (addk) {
-        const float4 p = *reinterpret_cast<const float4*>(addk + dt * 16 + 4 * lg);
+      if (a.addk) {
+        const float4 p = addkp[s][dt];
         rk.x += p.x * ab; rk.y += p.y * ab; rk.z += p.z * ab; rk.w += p.w * ab;
       }
-      if (addv) {
-        const float4 p = *reinterpret_cast<const float4*>(addv + dt * 16 + 4 * lg);
+      if (a.addv) {
+        const float4 p = addvp[s][dt];
         rv.x += p.x * ab; rv.y += p.y * ab; rv.z += p.z * ab; rv.w += p.w * ab;
       }
       *reinterpret_cast<float4*>(a.dk + sb + (size_t)u * D + dt * 16 + 4 * lg) = rk;
