@@ -703,40 +703,68 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
   const int x = threadIdx.x, c4 = x % C4, r0 = x / C4;
   const float4 ocg = *reinterpret_cast<const float4*>(a.o_cg + gb * D + 4 * c4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int r = r0; r < a.block; r += RS) {
-    const long long t = (long long)blk * a.block + r;
-    const long long row = slice * a.n_tok + t;
-    const float4 d4 = *reinterpret_cast<const float4*>(a.dout + row * D + 4 * c4);
-    const float g0 = a.gates[row * 3];
-    acc.x += g0 * d4.x; acc.y += g0 * d4.y; acc.z += g0 * d4.z; acc.w += g0 * d4.w;
-    ushort4 b;
-    b.x = bf16_bits(d4.x); b.y = bf16_bits(d4.y); b.z = bf16_bits(d4.z); b.w = bf16_bits(d4.w);
-    *reinterpret_cast<ushort4*>(a.dob + row * D + 4 * c4) = b;
-    float dg = d4.x * ocg.x + d4.y * ocg.y + d4.z * ocg.z + d4.w * ocg.w;
+  // Rows are taken kBatch sweeps at a time, every load of a batch issued
+  // before its first store: the compiler cannot rule out that the outputs
+  // alias the inputs, so a load written after a store stays behind it.
+  constexpr int kBatch = 4;
+  const bool sv = a.save_o != nullptr;
+  for (int rb = r0; rb < a.block; rb += kBatch * RS) {
+    float4 d4[kBatch], ob[kBatch][2];
+    float g[kBatch][3], lse[kBatch][2];
 #pragma unroll
-    for (int sh = 1; sh < C4; sh <<= 1) dg += __shfl_xor(dg, sh);
-    if (c4 == 0 && a.dgates) a.dgates[row * 3] = dg;
-    if (a.save_o) {   // dg_br = dO·o_br for the selected (0) and local (1) branches
+    for (int i = 0; i < kBatch; ++i) {
+      const int r = rb + i * RS;
+      if (r >= a.block) continue;
+      const long long row = slice * a.n_tok + (long long)blk * a.block + r;
+      d4[i] = *reinterpret_cast<const float4*>(a.dout + row * D + 4 * c4);
+      g[i][0] = a.gates[row * 3];
+      if (sv) {
 #pragma unroll
-      for (int br = 0; br < 2; ++br) {
-        // e = dO·o_br for the gate gradient; eb = dO_b·o_br (bf16 dO, as dP
-        // uses it) for D, so that the logit gradients of a row sum to zero
-        const float4 ob = *reinterpret_cast<const float4*>(a.save_o + (row * 2 + br) * D + 4 * c4);
-        float e = d4.x * ob.x + d4.y * ob.y + d4.z * ob.z + d4.w * ob.w;
-        float eb = bf16_round(d4.x) * ob.x + bf16_round(d4.y) * ob.y + bf16_round(d4.z) * ob.z +
-                   bf16_round(d4.w) * ob.w;
-#pragma unroll
-        for (int sh = 1; sh < C4; sh <<= 1) {
-          e += __shfl_xor(e, sh);
-          eb += __shfl_xor(eb, sh);
+        for (int br = 0; br < 2; ++br) {
+          ob[i][br] = *reinterpret_cast<const float4*>(a.save_o + (row * 2 + br) * D + 4 * c4);
+          g[i][1 + br] = a.gates[row * 3 + 1 + br];
+          lse[i][br] = a.save_lse[row * 2 + br];
         }
-        if (c4 == 0) {
-          const float gb = a.gates[row * 3 + 1 + br];
-          float* sp = a.stats + ((size_t)br * a.slices + slice) * 3 * a.n_tok + t;
-          sp[0] = a.save_lse[row * 2 + br];
-          sp[a.n_tok] = gb * eb;
-          sp[2 * (size_t)a.n_tok] = gb;
-          a.dgates[row * 3 + 1 + br] = e;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int r = rb + i * RS;
+      if (r >= a.block) continue;
+      const long long t = (long long)blk * a.block + r;
+      const long long row = slice * a.n_tok + t;
+      const float4 dv = d4[i];
+      const float g0 = g[i][0];
+      acc.x += g0 * dv.x; acc.y += g0 * dv.y; acc.z += g0 * dv.z; acc.w += g0 * dv.w;
+      ushort4 b;
+      b.x = bf16_bits(dv.x); b.y = bf16_bits(dv.y); b.z = bf16_bits(dv.z); b.w = bf16_bits(dv.w);
+      *reinterpret_cast<ushort4*>(a.dob + row * D + 4 * c4) = b;
+      float dg = dv.x * ocg.x + dv.y * ocg.y + dv.z * ocg.z + dv.w * ocg.w;
+#pragma unroll
+      for (int sh = 1; sh < C4; sh <<= 1) dg += __shfl_xor(dg, sh);
+      if (c4 == 0 && a.dgates) a.dgates[row * 3] = dg;
+      if (sv) {   // dg_br = dO·o_br for the selected (0) and local (1) branches
+#pragma unroll
+        for (int br = 0; br < 2; ++br) {
+          // e = dO·o_br for the gate gradient; eb = dO_b·o_br (bf16 dO, as dP
+          // uses it) for D, so that the logit gradients of a row sum to zero
+          const float4 o4 = ob[i][br];
+          float e = dv.x * o4.x + dv.y * o4.y + dv.z * o4.z + dv.w * o4.w;
+          float eb = bf16_round(dv.x) * o4.x + bf16_round(dv.y) * o4.y + bf16_round(dv.z) * o4.z +
+                     bf16_round(dv.w) * o4.w;
+#pragma unroll
+          for (int sh = 1; sh < C4; sh <<= 1) {
+            e += __shfl_xor(e, sh);
+            eb += __shfl_xor(eb, sh);
+          }
+          if (c4 == 0) {
+            const float gb = g[i][1 + br];
+            float* sp = a.stats + ((size_t)br * a.slices + slice) * 3 * a.n_tok + t;
+            sp[0] = lse[i][br];
+            sp[a.n_tok] = gb * eb;
+            sp[2 * (size_t)a.n_tok] = gb;
+            a.dgates[row * 3 + 1 + br] = e;
+          }
         }
       }
     }
