@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 9
+#define MOSAIC_BSA_ABI_VERSION 10
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -240,6 +240,16 @@ mosaic_status mosaic_bsa_layer_in(const void* x, const void* w_in, int batch, in
  * before the product). */
 mosaic_status mosaic_bsa_layer_out(const float* attn, const void* w_out, const void* x, int batch, int heads,
                                    int head_dim, int channels, int nside, void* y, void* stream);
+
+/* The same output projection from the attention output in the layout the
+ * layer's own fine kernel writes: attn bf16 [batch][N][heads*head_dim], the
+ * heads side by side (feature h*d + j), already rounded.  This is the GEMM
+ * that mosaic_bsa_layer_forward runs.  y = x + attn w_outᵀ, rounded to bf16;
+ * y may be x itself (each element's residual is read before it is written).
+ * Sizes, alignment and errors as for mosaic_bsa_layer_out. */
+mosaic_status mosaic_bsa_layer_out_merged(const void* attn, const void* w_out, const void* x, int batch,
+                                          int heads, int head_dim, int channels, int nside, void* y,
+                                          void* stream);
 
 /* Bytes of the state mosaic_bsa_forward_train leaves for mosaic_bsa_backward,
  * or 0 when the sizes are invalid or unsupported.  Layout (256-byte aligned

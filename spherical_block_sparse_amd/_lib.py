@@ -30,6 +30,7 @@ EXPORTED = (
     "mosaic_bsa_compress_select", "mosaic_bsa_fine",
     "mosaic_bsa_saved_bytes", "mosaic_bsa_forward_train",
     "mosaic_bsa_layer_workspace_bytes", "mosaic_bsa_layer_forward", "mosaic_bsa_layer_in", "mosaic_bsa_layer_out",
+    "mosaic_bsa_layer_out_merged",
     "mosaic_healpix_coarsen", "mosaic_interp_workspace_bytes", "mosaic_interp_attention",
     "mosaic_bsa_backward_workspace_bytes", "mosaic_bsa_backward",
 )
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_layer_in.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P]
         L.mosaic_bsa_layer_out.restype = I
         L.mosaic_bsa_layer_out.argtypes = [P, P, P, I, I, I, I, I, P, P]
+        L.mosaic_bsa_layer_out_merged.restype = I
+        L.mosaic_bsa_layer_out_merged.argtypes = [P, P, P, I, I, I, I, I, P, P]
         L.mosaic_bsa_saved_bytes.restype = S
         L.mosaic_bsa_saved_bytes.argtypes = [I, I, I, I, I]
         L.mosaic_bsa_forward_train.restype = I
@@ -367,6 +370,21 @@ def mosaic_bsa_layer_out(attn, w_out, x, nside, y=None, stream=None):
     _check(lib().mosaic_bsa_layer_out(
         _ptr(attn, torch.float32, (b, heads, n, head_dim), "attn"),
         _ptr(w_out, torch.bfloat16, (c, heads * head_dim), "w_out"), _ptr(x, torch.bfloat16, (b, n, c), "x"),
+        b, heads, head_dim, c, nside, _ptr(y, torch.bfloat16, (b, n, c), "y"), _stream(stream)))
+    return y
+
+
+def mosaic_bsa_layer_out_merged(attn, w_out, x, nside, heads, y=None, stream=None):
+    """y [b,N,C] bf16 = x + attn w_outᵀ, attn [b,N,H*d] bf16 (the heads side by side)."""
+    b, n, c = _layer_dims(x, nside)
+    hd = attn.shape[-1]
+    if hd % heads:
+        raise ValueError(f"attn's last dimension {hd} is not a multiple of heads={heads}")
+    head_dim = hd // heads
+    y = torch.empty((b, n, c), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _check(lib().mosaic_bsa_layer_out_merged(
+        _ptr(attn, torch.bfloat16, (b, n, hd), "attn"),
+        _ptr(w_out, torch.bfloat16, (c, hd), "w_out"), _ptr(x, torch.bfloat16, (b, n, c), "x"),
         b, heads, head_dim, c, nside, _ptr(y, torch.bfloat16, (b, n, c), "y"), _stream(stream)))
     return y
 

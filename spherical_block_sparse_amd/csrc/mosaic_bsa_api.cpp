@@ -449,6 +449,23 @@ mosaic_status mosaic_bsa_layer_out(const float* attn, const void* w_out, const v
                     "layer output projection launch");
 }
 
+mosaic_status mosaic_bsa_layer_out_merged(const void* attn, const void* w_out, const void* x, int batch,
+                                          int heads, int head_dim, int channels, int nside, void* y,
+                                          void* stream) {
+  REQUIRE_PTR(attn); REQUIRE_PTR(w_out); REQUIRE_PTR(x); REQUIRE_PTR(y);
+  REQUIRE_ALIGN(attn, 16); REQUIRE_ALIGN(w_out, 16); REQUIRE_ALIGN(x, 16); REQUIRE_ALIGN(y, 16);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, 16, 0, 0, 0, &s);
+  if (st != MOSAIC_OK) return st;
+  if ((st = check_layer(s, heads, channels)) != MOSAIC_OK) return st;
+  return hip_status(mosaic::launch_layer_out_merged(static_cast<const uint16_t*>(attn),
+                                                    static_cast<const uint16_t*>(w_out),
+                                                    static_cast<const uint16_t*>(x), batch, s.n_tok, channels,
+                                                    heads, s.d, static_cast<uint16_t*>(y),
+                                                    static_cast<hipStream_t>(stream)),
+                    "layer output projection launch");
+}
+
 mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const void* w_out, int batch, int heads,
                                        int head_dim, int channels, int nside, int block, int topn, int window,
                                        void* y, int32_t* sel_idx, void* workspace, size_t workspace_bytes,

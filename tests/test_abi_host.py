@@ -266,6 +266,10 @@ def test_layer_stage_validation():
     assert L.mosaic_bsa_layer_out(FAKE, FAKE, None, 1, 2, 64, 128, 32, FAKE, None) == NULL
     assert L.mosaic_bsa_layer_out(FAKE, FAKE, FAKE, 1, 2, 64, 128, 32, FAKE + 2, None) == MISAL
     assert L.mosaic_bsa_layer_out(FAKE, FAKE, FAKE, 1, 1, 32, 128, 32, FAKE, None) == UNSUP
+    assert L.mosaic_bsa_layer_out_merged(None, FAKE, FAKE, 1, 2, 64, 128, 32, FAKE, None) == NULL
+    assert L.mosaic_bsa_layer_out_merged(FAKE, FAKE, FAKE, 1, 2, 64, 128, 32, FAKE + 2, None) == MISAL
+    assert L.mosaic_bsa_layer_out_merged(FAKE, FAKE, FAKE, 1, 1, 32, 128, 32, FAKE, None) == UNSUP
+    assert L.mosaic_bsa_layer_out_merged(FAKE, FAKE, FAKE, 1, 2, 64, 128, 3, FAKE, None) == SHAPE
 
 
 def test_layer_workspace_bytes():

@@ -90,6 +90,30 @@ def test_layer_output_projection(cfg, channels):
 
 
 @pytest.mark.parametrize("cfg,channels", LAYER_CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_layer_output_projection_merged(cfg, channels):
+    """The merged-layout entry point (the layer's own GEMM) against the
+    oracle on the same bf16 attention values, and in place (y = x)."""
+    x, _, w_out = make_layer_inputs(cfg, channels, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed + 1)
+    b, h, n, d = cfg.batch, cfg.heads, cfg.n_tokens, cfg.head_dim
+    attn = torch.randn((b, h, n, d), generator=gen, device="cuda").to(torch.bfloat16)
+    merged = attn.permute(0, 2, 1, 3).contiguous().view(b, n, h * d)
+    y = _lib.mosaic_bsa_layer_out_merged(merged, w_out[0], x, cfg.nside, h)
+    y_in_place = x.clone()
+    _lib.mosaic_bsa_layer_out_merged(merged, w_out[0], y_in_place, cfg.nside, h, y=y_in_place)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_in_place)
+    a, wo, xf = to_f64(attn), to_f64(w_out[0]), to_f64(x)
+    want = oracle.layer_out_ref(a, wo, xf)
+    absum = np.abs(xf) + np.abs(a.transpose(0, 2, 1, 3).reshape(b, n, h * d)) @ np.abs(wo).T
+    _ulp_check(f"{cfg.name} y (merged)", to_f64(y), want, absum, h * d + 1)
+    # the float32 stage entry point on the same (bf16-valued) attention output agrees
+    y32 = _lib.mosaic_bsa_layer_out(attn.float(), w_out[0], x, cfg.nside)
+    torch.cuda.synchronize()
+    assert float((y.float() == y32.float()).float().mean()) >= 0.999
+
+
+@pytest.mark.parametrize("cfg,channels", LAYER_CASES, ids=lambda c: getattr(c, "name", str(c)))
 def test_layer_forward(cfg, channels):
     x, w_in, w_out = make_layer_inputs(cfg, channels, device="cuda")
     y, sel = _lib.mosaic_bsa_layer_forward(x, w_in[0], w_out[0], cfg.heads, cfg.head_dim, cfg.nside, cfg.block,
