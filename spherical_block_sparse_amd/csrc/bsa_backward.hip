@@ -9,7 +9,13 @@
 //
 // Every branch is softmax attention o = P V over its own key set, whose
 // gradient is dV = P^T dO, dS = P ⊙ (dO V^T - D) with D = rowsum(dO ⊙ o),
-// dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).  Launch order:
+// dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).  A gated branch (out += g o)
+// takes g·dO.  The kernels form P·g in one exponential: the per-query plane
+// holds lse - log2|g|, so exp2(S c - that) = P |g|; the gate's sign is folded
+// into the bf16 dO of the branch (an exact sign flip, one copy per branch),
+// and the score-MFMA for dP starts from -sign(g)·(dO_b·o) instead of zero, so
+// that dS = P|g| (sign(g) dO_b V^T - sign(g) dO_b·o) takes one multiply.
+// Launch order:
 //   1. pool and compressed forward (the forward's kernels) recompute q̄, k̄,
 //      v̄ and o_CG;
 //   2. prep: dO to bf16, do_CG_i = sum over block i of g_CG·dO, the g_CG
@@ -149,13 +155,14 @@ struct BwdArgs {
   const uint16_t* q;      // bf16 [S][N][D]
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* dob;    // bf16 upstream gradient [S][N][D]
+  const uint16_t* dob;    // bf16 upstream gradient of the selected branch [S][N][D], sign of its gate applied
+  const uint16_t* dob_loc;// the same for the local branch (the compressed pass: its pooled dO for both)
   const float* dof;       // the same in fp32 (for D = dO·o)
   const float* gates;     // [S][N][3] (g_CG, g_FG, g_L), or null: unit gates
   const int32_t* sel;     // [S][m][n] selection, or null: no selected branch
   const int32_t* inv_off; // [S][m+1] inverted selection offsets
   const int32_t* inv_list;// [S][m*n] query blocks per key block
-  float* stats;           // [2][S][3][N] per branch planes lse, D, g; branch 0 selected, 1 local
+  float* stats;           // [2][S][3][N] per branch planes lse - log2|g|, -sign(g) dO_b·o, g; branch 0 selected, 1 local
   float* dq;              // [S][N][D] fp32 out
   float* dk;
   float* dv;
@@ -198,18 +205,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int tw = t0 + 32 * w;
   const size_t sb = (size_t)slice * N * D;
-  const uint16_t *qs = a.q + sb, *ks = a.k + sb, *vs = a.v + sb, *dos = a.dob + sb;
+  const uint16_t *qs = a.q + sb, *ks = a.k + sb, *vs = a.v + sb;
   const float* dofs = a.dof + sb;
   const float c = a.scale_log2;
 
+  // q operands; dO operands per branch (each branch's dO carries the sign of its gate)
   bf16x8 qf[2][KK], df[2][KK];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qf[s][kk] = global_operand<D>(qs, tw + 16 * s + lr, kk);
-      df[s][kk] = global_operand<D>(dos, tw + 16 * s + lr, kk);
-    }
+    for (int kk = 0; kk < KK; ++kk) qf[s][kk] = global_operand<D>(qs, tw + 16 * s + lr, kk);
   floatx4 dqa[2][DT];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -235,10 +240,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   // whether its scores need the per-lane key range, and that range
   auto branch = [&](int br_id, int nc, auto chunk_tok, auto chunk_valid) __attribute__((always_inline)) {
     float g[2];
+    const uint16_t* dos = (br_id == 0 ? a.dob : a.dob_loc) + sb;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int t = tw + 16 * s + lr;
       g[s] = a.gates ? a.gates[((size_t)slice * N + t) * 3 + 1 + br_id] : 1.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) df[s][kk] = global_operand<D>(dos, t, kk);
     }
     // key range of this lane's query in chunk ci (all keys for the selected branch)
     auto range = [&](int ci, int s, int& lo, int& span) __attribute__((always_inline)) -> bool {
@@ -353,10 +361,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
       for (int s = 0; s < 2; ++s) {
         const int t = tw + 16 * s + lr;
         const float inv_l = 1.f / st[s].l[0];
-        // dg = dO·o (the gate gradient) with dO in float32; D = g (dO_b·o)
-        // with the bf16 dO_b that dP = dO_b V^T uses, so that sum_u dS_u
-        // stays zero up to rounding (otherwise dO's rounding error, times
-        // the mean key, lands in every dQ)
+        // dg = dO·o (the gate gradient) with dO in float32; dO_b·o with the
+        // bf16 dO_b that dP = dO_b V^T uses, so that sum_u dS_u stays zero up
+        // to rounding (otherwise dO's rounding error, times the mean key,
+        // lands in every dQ)
         float dg = 0.f, dgb = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -371,8 +379,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
         dgb *= inv_l;
         dgb += __shfl_xor(dgb, 16);
         dgb += __shfl_xor(dgb, 32);
-        lse[s] = st[s].m * c + log2f(st[s].l[0]);
-        dsub[s] = g[s] * dgb;
+        // the planes of the kernels' product form: P|g| = exp2(S c - lse + log2|g|),
+        // dS = P|g| (sign(g) dP - sign(g) dO_b·o); |g| = 0 gives an exponent of -inf
+        lse[s] = st[s].m * c + log2f(st[s].l[0]) - log2f(fabsf(g[s]));
+        dsub[s] = signbit(g[s]) ? dgb : -dgb;
         if (lg == 0) {
           float* sp = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N + t;
           sp[0] = lse[s];
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
           if (a.dgates) a.dgates[((size_t)slice * N + t) * 3 + 1 + br_id] = dg;
         }
       }
-    } else {   // the training forward saved lse; the prep kernel formed D and dgates
+    } else {   // the training forward saved lse; the prep kernel formed the planes and dgates
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const float* sp = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N + tw + 16 * s + lr;
@@ -395,10 +405,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
       floatx4 acc[2][4], dpa[2][4];
       scores(kb, acc);
       mask(ci, acc);
+      // dP starts from -sign(g) dO_b·o, so the MFMAs leave sign(g) dP - sign(g) dO_b·o
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) dpa[s][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 4; ++kt) dpa[s][kt] = floatx4{dsub[s], dsub[s], dsub[s], dsub[s]};
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -415,8 +426,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(acc[s][kt][i], c, -lse[s]));
-            ds[s][kt >> 1][4 * (kt & 1) + i] = static_cast<__bf16>(p * (g[s] * dpa[s][kt][i] - dsub[s]));
+            const float pg = __builtin_amdgcn_exp2f(fmaf(acc[s][kt][i], c, -lse[s]));   // P |g|
+            ds[s][kt >> 1][4 * (kt & 1) + i] = static_cast<__bf16>(pg * dpa[s][kt][i]);
           }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -492,7 +503,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int uw = u0 + 32 * w;
   const size_t sb = (size_t)slice * N * D;
-  const uint16_t *qs = a.q + sb, *ks = a.k + sb, *vs = a.v + sb, *dos = a.dob + sb;
+  const uint16_t *qs = a.q + sb, *ks = a.k + sb, *vs = a.v + sb;
   const float c = a.scale_log2;
 
   bf16x8 kf[2][KK], vf[2][KK];
@@ -521,6 +532,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   auto phase = [&](int br_id, int nc, auto chunk_row, auto chunk_valid, auto local) __attribute__((always_inline)) {
     constexpr bool LOCAL = decltype(local)::value;
     const float* stats = a.stats + ((size_t)br_id * a.slices + slice) * 3 * N;
+    const uint16_t* dos = (br_id == 0 ? a.dob : a.dob_loc) + sb;   // the branch's signed dO
     auto stage = [&](int ci, int p) __attribute__((always_inline)) {
       stage_rows<D>(Qb(p), qs, chunk_row(ci), chunk_valid(ci), w);
       stage_rows<D>(Ob(p), dos, chunk_row(ci), chunk_valid(ci), w);
@@ -539,17 +551,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
       const int r0 = chunk_row(ci), nv = chunk_valid(ci);
       // in halves of 32 queries (j): S = Q K^T and dP = dO V^T, where the
       // lane holds key lr of sub-tile s and queries 32*j + 16*h + 4*lg + i;
-      // then dV^T += dO^T (P g) and dK^T += Q^T dS over those queries
+      // then dV^T += dO^T (P g) and dK^T += Q^T dS over those queries.  dO
+      // is the branch's signed copy, and dP starts from the plane
+      // -sign(g) dO_b·o, so the MFMAs leave sign(g) dP - sign(g) dO_b·o.
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         floatx4 sa[2][2], dpa[2][2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int h = 0; h < 2; ++h) {
+          const float4 d4 = *reinterpret_cast<const float4*>(stt + 64 + 32 * j + 16 * h + 4 * lg);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+          for (int s = 0; s < 2; ++s) {
             sa[s][h] = floatx4{0.f, 0.f, 0.f, 0.f};
-            dpa[s][h] = floatx4{0.f, 0.f, 0.f, 0.f};
+            dpa[s][h] = floatx4{d4.x, d4.y, d4.z, d4.w};
           }
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -563,23 +579,20 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
             }
           }
         bf16x8 pg[2], ds[2];
-        // P = exp2(S c - lse); P g and dS = P (g dP - D).  Padded rows and
-        // (local phase) keys outside the query's window get exponent -inf;
-        // key u is inside the window of query t iff u - t + lo_off < window
-        // (unsigned), and u - t is a per-lane base plus a constant.
+        // P|g| = exp2(S c - (lse - log2|g|)) and dS = P|g| (dP - D) from the
+        // signed accumulators.  Padded rows and (local phase) keys outside
+        // the query's window get exponent -inf; key u is inside the window
+        // of query t iff u - t + lo_off < window (unsigned), and u - t is a
+        // per-lane base plus a constant.
         const int dbase = uw + lr - r0 - 32 * j - 4 * lg + lo_off;
         const int vbase = nv - 32 * j - 4 * lg;   // row qi valid iff qi - 32j - 4lg < vbase
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int q0 = 32 * j + 16 * h + 4 * lg;   // the lane's first query row of the chunk
           const float4 lse4 = *reinterpret_cast<const float4*>(stt + q0);
-          const float4 d4 = *reinterpret_cast<const float4*>(stt + 64 + q0);
-          const float4 g4 = *reinterpret_cast<const float4*>(stt + 128 + q0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float lse = i == 0 ? lse4.x : i == 1 ? lse4.y : i == 2 ? lse4.z : lse4.w;
-            const float dd = i == 0 ? d4.x : i == 1 ? d4.y : i == 2 ? d4.z : d4.w;
-            const float gg = i == 0 ? g4.x : i == 1 ? g4.y : i == 2 ? g4.z : g4.w;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
               float x = fmaf(sa[s][h][i], c, -lse);
@@ -587,9 +600,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
                 const bool ok = 16 * h + i < vbase && (unsigned)(dbase + 16 * s - 16 * h - i) < (unsigned)a.window;
                 x = ok ? x : -INFINITY;
               }
-              const float p = __builtin_amdgcn_exp2f(x);
-              pg[s][4 * h + i] = static_cast<__bf16>(p * gg);
-              ds[s][4 * h + i] = static_cast<__bf16>(p * (gg * dpa[s][h][i] - dd));
+              const float p = __builtin_amdgcn_exp2f(x);   // P |g|
+              pg[s][4 * h + i] = static_cast<__bf16>(p);
+              ds[s][4 * h + i] = static_cast<__bf16>(p * dpa[s][h][i]);
             }
           }
         }
@@ -674,7 +687,8 @@ struct PrepArgs {
   const double* qbar;      // [S][m][D]
   const double* kbar;
   const float* vbar;
-  uint16_t* dob;           // out bf16 [S][N][D]
+  uint16_t* dob;           // out bf16 [S][N][D]: sign(g_FG) dO (the selected branch's)
+  uint16_t* dob_loc;       // out bf16 [S][N][D]: sign(g_L) dO (the local branch's)
   float* docg;             // out [S][m][D]
   uint16_t* docg_b;        // out bf16 [S][m][D]
   uint16_t* qbar_b;        // out bf16 [S][m][D]
@@ -683,7 +697,7 @@ struct PrepArgs {
   float* dgates;           // out column 0 (or null); with save_o also columns 1, 2
   const float* save_o;     // [S][N][2][D] o_FG, o_L of the training forward, or null
   const float* save_lse;   // [S][N][2]
-  float* stats;            // with save_o: out [2][S][3][N] planes lse, D = g dg, g
+  float* stats;            // with save_o: out [2][S][3][N] planes lse - log2|g|, -sign(g) dO_b·o, g
   long long slices;
   int n_tok, block, m;
 };
@@ -717,12 +731,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
       if (r >= a.block) continue;
       const long long row = slice * a.n_tok + (long long)blk * a.block + r;
       d4[i] = *reinterpret_cast<const float4*>(a.dout + row * D + 4 * c4);
-      g[i][0] = a.gates[row * 3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) g[i][r] = a.gates[row * 3 + r];
       if (sv) {
 #pragma unroll
         for (int br = 0; br < 2; ++br) {
           ob[i][br] = *reinterpret_cast<const float4*>(a.save_o + (row * 2 + br) * D + 4 * c4);
-          g[i][1 + br] = a.gates[row * 3 + 1 + br];
           lse[i][br] = a.save_lse[row * 2 + br];
         }
       }
@@ -736,9 +750,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
       const float4 dv = d4[i];
       const float g0 = g[i][0];
       acc.x += g0 * dv.x; acc.y += g0 * dv.y; acc.z += g0 * dv.z; acc.w += g0 * dv.w;
+      // each fine branch's bf16 dO carries the sign of the branch's gate
+      // (rounding commutes with the sign, so this is bf16(dO) or its negation)
       ushort4 b;
       b.x = bf16_bits(dv.x); b.y = bf16_bits(dv.y); b.z = bf16_bits(dv.z); b.w = bf16_bits(dv.w);
-      *reinterpret_cast<ushort4*>(a.dob + row * D + 4 * c4) = b;
+#pragma unroll
+      for (int br = 0; br < 2; ++br) {
+        const uint16_t sg = signbit(g[i][1 + br]) ? 0x8000 : 0;
+        ushort4 bs;
+        bs.x = b.x ^ sg; bs.y = b.y ^ sg; bs.z = b.z ^ sg; bs.w = b.w ^ sg;
+        *reinterpret_cast<ushort4*>((br == 0 ? a.dob : a.dob_loc) + row * D + 4 * c4) = bs;
+      }
       float dg = dv.x * ocg.x + dv.y * ocg.y + dv.z * ocg.z + dv.w * ocg.w;
 #pragma unroll
       for (int sh = 1; sh < C4; sh <<= 1) dg += __shfl_xor(dg, sh);
@@ -757,11 +779,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
             e += __shfl_xor(e, sh);
             eb += __shfl_xor(eb, sh);
           }
-          if (c4 == 0) {
+          if (c4 == 0) {   // the planes of the kernels' product form (see the header)
             const float gb = g[i][1 + br];
             float* sp = a.stats + ((size_t)br * a.slices + slice) * 3 * a.n_tok + t;
-            sp[0] = lse[i][br];
-            sp[a.n_tok] = gb * eb;
+            sp[0] = lse[i][br] - log2f(fabsf(gb));
+            sp[a.n_tok] = signbit(gb) ? eb : -eb;
             sp[2 * (size_t)a.n_tok] = gb;
             a.dgates[row * 3 + 1 + br] = e;
           }
@@ -878,7 +900,7 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
   // prep
   PrepArgs p;
   p.dout = L.dout; p.gates = L.gates; p.o_cg = L.o_cg; p.qbar = L.qbar; p.kbar = L.kbar; p.vbar = L.vbar;
-  p.dob = L.dob; p.docg = L.docg; p.docg_b = L.docg_b; p.qbar_b = L.qbar_b; p.kbar_b = L.kbar_b; p.vbar_b = L.vbar_b;
+  p.dob = L.dob; p.dob_loc = L.dob_loc; p.docg = L.docg; p.docg_b = L.docg_b; p.qbar_b = L.qbar_b; p.kbar_b = L.kbar_b; p.vbar_b = L.vbar_b;
   p.dgates = L.dgates; p.n_tok = N; p.block = L.block; p.m = m;
   p.save_o = L.save_o; p.save_lse = L.save_lse; p.stats = L.stats; p.slices = S;
   hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)(S * m)), dim3(256), 0, stream, p);
@@ -889,7 +911,7 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
   const float isd = (float)(1.0 / sqrt((double)D));
   // compressed branch: dense attention over the pooled rows (window covers all)
   BwdArgs cg = {};
-  cg.q = L.qbar_b; cg.k = L.kbar_b; cg.v = L.vbar_b; cg.dob = L.docg_b; cg.dof = L.docg;
+  cg.q = L.qbar_b; cg.k = L.kbar_b; cg.v = L.vbar_b; cg.dob = L.docg_b; cg.dob_loc = L.docg_b; cg.dof = L.docg;
   cg.gates = nullptr; cg.sel = nullptr; cg.stats = L.stats_cg;
   cg.dq = L.dqbar; cg.dk = L.dkbar; cg.dv = L.dvbar; cg.dgates = nullptr;
   cg.n_tok = m; cg.block = 1; cg.topn = 0; cg.window = 2 * m + 1; cg.m = m; cg.slices = S;
@@ -908,7 +930,7 @@ hipError_t launch_d(const BwdLaunch& L, hipStream_t stream) {
                      dim3(64 * kSortWaves), 0, stream, L.inv_off, L.inv_tmp, L.inv_list, S * m, m, m * L.topn);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   BwdArgs f = {};
-  f.q = L.q; f.k = L.k; f.v = L.v; f.dob = L.dob; f.dof = L.dout; f.gates = L.gates; f.sel = L.sel;
+  f.q = L.q; f.k = L.k; f.v = L.v; f.dob = L.dob; f.dob_loc = L.dob_loc; f.dof = L.dout; f.gates = L.gates; f.sel = L.sel;
   f.inv_off = L.inv_off; f.inv_list = L.inv_list; f.stats = L.stats;
   f.dq = L.dq; f.dk = L.dk; f.dv = L.dv; f.dgates = L.dgates;
   f.addq = L.dqbar; f.addk = L.dkbar; f.addv = L.dvbar;

@@ -63,7 +63,8 @@ struct BwdLaunch {
   const float* o_cg;        // compressed output [S][m][d] (likewise)
   const float* save_o;      // training forward's o_FG, o_L [S][N][2][d], or null: recompute
   const float* save_lse;    // their log2-sum-exp [S][N][2]
-  uint16_t* dob;            // workspace: bf16 dO [S][N][d]
+  uint16_t* dob;            // workspace: bf16 dO [S][N][d] with the sign of g_FG (selected branch)
+  uint16_t* dob_loc;        // the same with the sign of g_L (local branch)
   float* docg;              // [S][m][d] and its bf16 copy
   uint16_t* docg_b;
   uint16_t* qbar_b;         // bf16 pooled rows [S][m][d]

@@ -124,7 +124,7 @@ Saved saved_layout(const Shape& s) {
 // Backward workspace: recomputed forward pieces, bf16 copies, per-query
 // statistics, pooled gradients and the inverted selection.
 struct BwdWorkspace {
-  size_t qbar, kbar, vbar, ocg, sel, dob, docg, docg_b, qbar_b, kbar_b, vbar_b, stats, stats_cg, dqbar, dkbar,
+  size_t qbar, kbar, vbar, ocg, sel, dob, dob_loc, docg, docg_b, qbar_b, kbar_b, vbar_b, stats, stats_cg, dqbar, dkbar,
       dvbar, inv_off, inv_tmp, inv_list, total;
 };
 
@@ -139,6 +139,7 @@ BwdWorkspace bwd_layout(const Shape& s) {
   w.ocg = take(em * sizeof(float));
   w.sel = take((size_t)s.slices * s.m * s.topn * sizeof(int32_t));
   w.dob = take(en * sizeof(uint16_t));
+  w.dob_loc = take(en * sizeof(uint16_t));
   w.docg = take(em * sizeof(float));
   w.docg_b = take(em * sizeof(uint16_t));
   w.qbar_b = take(em * sizeof(uint16_t));
@@ -628,6 +629,7 @@ mosaic_status mosaic_bsa_backward(const void* q, const void* k, const void* v, c
   L.vbar = vbar;
   L.o_cg = ocg;
   L.dob = reinterpret_cast<uint16_t*>(ws + w.dob);
+  L.dob_loc = reinterpret_cast<uint16_t*>(ws + w.dob_loc);
   L.docg = reinterpret_cast<float*>(ws + w.docg);
   L.docg_b = reinterpret_cast<uint16_t*>(ws + w.docg_b);
   L.qbar_b = reinterpret_cast<uint16_t*>(ws + w.qbar_b);

@@ -7,7 +7,7 @@ which the backward holds fixed), so the comparison is element by element.
 
 Tolerance, from the arithmetic of the kernels: every product is bf16 x bf16
 with float32 accumulation; q, k, v are exact bf16 inputs, while dout, the
-probabilities and dS = P (g dP - D) are rounded to bf16 (relative error
+probabilities P|g| and dS = P g (dP - dO_b·o) are rounded to bf16 (relative error
 <= 2^-9 each) before they enter a product.  D is formed from the same
 bf16 dout as dP, so a row's dS still sums to zero up to rounding and no
 systematic error times the mean key enters dQ or dK.  A gradient element is
@@ -35,13 +35,20 @@ REL_L2 = 1e-2
 MAX_REL = 2e-2
 
 
-def _run(cfg: BSAConfig, seed: int = 0):
+def _run(cfg: BSAConfig, seed: int = 0, gates=None, use_saved: bool = False):
     dev = "cuda"
     q, k, v, g = make_inputs(cfg, device=dev)
+    if gates is not None:
+        g = gates(g)
     gen = torch.Generator(device=dev).manual_seed(1000 + cfg.seed + seed)
     dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32)
-    _, sel = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
-    dq, dk, dv, dg = _lib.mosaic_bsa_backward(q, k, v, g, sel, dout, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    saved = None
+    if use_saved:
+        _, sel, saved = _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    else:
+        _, sel = _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    dq, dk, dv, dg = _lib.mosaic_bsa_backward(q, k, v, g, sel, dout, cfg.nside, cfg.block, cfg.topn, cfg.window,
+                                              saved=saved)
     torch.cuda.synchronize()
     ref = oracle.bsa_backward_ref(to_f64(q), to_f64(k), to_f64(v), g.double().cpu().numpy(),
                                   dout.double().cpu().numpy(), cfg.block, cfg.topn, cfg.window,
@@ -69,6 +76,22 @@ def test_backward_ns32_two_heads():
 
 def test_backward_correlated_field_head_dim_32():
     _run(BSAConfig("ns32-d32", 32, 1, 1, 32, 64, 8, 100, "fourier", 33))
+
+
+def _signed_gates(g):
+    """Gates of either sign, with exact zeros and negative zeros: the interface
+    takes any float32 gates, while the kernels fold each fine gate's sign into
+    that branch's bf16 dO and its magnitude into the exponent of P|g|."""
+    gen = torch.Generator(device=g.device).manual_seed(77)
+    s = torch.randn(g.shape, generator=gen, device=g.device, dtype=torch.float32)
+    s[..., 0::7, :] = 0.0
+    s[..., 3::11, :] = -0.0
+    return s
+
+
+@pytest.mark.parametrize("use_saved", [False, True], ids=["recompute", "saved-state"])
+def test_backward_signed_and_zero_gates(use_saved):
+    _run(BSAConfig("ns32-signed", 32, 1, 2, 64, 64, 16, 256, "fourier", 38), gates=_signed_gates, use_saved=use_saved)
 
 
 def test_backward_block_256():
