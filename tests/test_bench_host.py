@@ -198,3 +198,20 @@ def test_random_shape_draw_is_valid_and_varied():
     assert any(c.topn > 64 for c in CASES)
     assert {c.head_dim for c in CASES} == {32, 64}
     assert any(c.window == 1 for c in CASES) and any(c.window > 2 * 12 * c.nside ** 2 for c in CASES)
+
+
+def test_random_backward_shape_draw_is_valid_and_varied():
+    """The seeded shapes of the random-shape backward GPU test lie inside the
+    backward's domain (block >= 64, top-n <= 64, m a multiple of 64) and
+    reach both head dims, both block sizes, signed and unsigned gates,
+    windows of one token and past the sphere, and the largest top-n."""
+    from test_random_shapes_backward_gpu import CASES
+    assert len({c.name for c, _ in CASES}) == len(CASES)
+    for c, _ in CASES:
+        m = 12 * c.nside ** 2 // c.block
+        assert c.block >= 64 and c.block <= c.nside ** 2 and m % 64 == 0
+        assert 1 <= c.topn <= min(m, 64) and c.window >= 1 and c.head_dim in (32, 64)
+    assert {c.head_dim for c, _ in CASES} == {32, 64} and {c.block for c, _ in CASES} == {64, 256}
+    assert {sg for _, sg in CASES} == {True, False}
+    assert any(c.window == 1 for c, _ in CASES)
+    assert any(c.window > 2 * 12 * c.nside ** 2 for c, _ in CASES) and any(c.topn == 64 for c, _ in CASES)
