@@ -34,6 +34,21 @@ int mosaic_probe_read(const void* buf, size_t bytes, float* sink, int blocks, vo
  * shader clock it ran at. */
 int mosaic_probe_mfma(float* sink, int blocks, int iters, unsigned long long* clocks, void* stream);
 
+/* Whether MFMAs and vector-ALU instructions overlap.  `blocks` workgroups of
+ * eight waves, one per compute unit at a time (each holds 96 KB of LDS), so
+ * each SIMD holds two of a workgroup's waves.  Per iteration, "MFMA work" is
+ * 32 independent v_mfma_f32_16x16x32_bf16 and "vector work" 32 FMAs, 32
+ * exp2, 16 bf16 packs and 16 XORs (the fine kernel's vector mix per 64-key
+ * chunk and wave).  mode 0: every wave does `iters` iterations of MFMA work;
+ * 1: of vector work; 2: waves 0-3 MFMA work and waves 4-7 vector work;
+ * 3: every wave both, interleaved.  `clocks` (may be NULL): uint64
+ * [blocks][8], each wave's elapsed shader clocks; `simd` (may be NULL, used
+ * only with clocks): int32 [blocks][8], each wave's SIMD (HW_ID bits 5:4).
+ * `sink` (float32 [blocks]) as above.  hipErrorInvalidValue for a mode
+ * outside 0..3. */
+int mosaic_probe_overlap(float* sink, int blocks, int iters, int mode, unsigned long long* clocks, int* simd,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

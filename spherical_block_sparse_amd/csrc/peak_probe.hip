@@ -12,6 +12,8 @@
 //     operands, eight independent accumulators per wave (no loads at all);
 //     optionally each workgroup's shader clocks (s_memtime) and 100 MHz
 //     ticks (s_memrealtime) over its run, which give the clock it ran at.
+//   * mosaic_probe_overlap: whether MFMAs and vector instructions of two
+//     waves on one SIMD, or of one wave, run at the same time (below).
 // Each folds what it computed into one value per workgroup, written only
 // when it equals a value it never takes, so the work cannot be dropped.
 #include "mosaic_probe.h"
@@ -21,6 +23,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -66,6 +69,90 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float* sink, int iters,
   }
 }
 
+// MFMA / vector-ALU overlap.  A workgroup of eight waves holds a 96 KB LDS
+// array, so one workgroup runs per compute unit and each SIMD holds two of
+// its waves (the kernel records each wave's SIMD from HW_ID to confirm which
+// two).  An iteration of "MFMA work" is 32 independent
+// v_mfma_f32_16x16x32_bf16 (eight accumulators); an iteration of "vector
+// work" is the fine kernel's per-chunk vector mix: 32 FMAs and 32 exp2 in
+// eight independent chains, 16 bf16 packs of the exp2 results and 16 XORs
+// that fold the packs into a checksum.  MODE 0: every wave does MFMA work;
+// 1: every wave does vector work; 2: waves 0-3 MFMA work, waves 4-7 vector
+// work; 3: every wave does both, a round of 8 MFMAs then a quarter of the
+// vector work, four times per iteration.
+constexpr int kOverlapLds = 96 * 1024;
+
+template <int MODE>
+__global__ __launch_bounds__(512) void probe_overlap_kernel(float* sink, int iters, unsigned long long* clocks,
+                                                            int* simd) {
+  __shared__ float pad[kOverlapLds / 4];
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const bool mf = MODE == 0 || MODE == 3 || (MODE == 2 && w < 4);
+  const bool va = MODE == 1 || MODE == 3 || (MODE == 2 && w >= 4);
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>((float)((threadIdx.x + e) & 7) * 0.125f);
+    b[e] = static_cast<__bf16>((float)((threadIdx.x * 3 + e) & 7) * 0.0625f);
+  }
+  floatx4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = -0.25f - 0.001f * (float)((threadIdx.x + j) & 15);
+  uint32_t chk = 0;
+  // a quarter of the vector work: 8 FMAs, 8 exp2, 4 packs, 4 XORs
+  auto vround = [&]() __attribute__((always_inline)) {
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = fmaf(x[j], 0.5f, -0.25f);
+      p[j] = __builtin_amdgcn_exp2f(x[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      bf16x2 pk;
+      pk[0] = static_cast<__bf16>(p[j]);
+      pk[1] = static_cast<__bf16>(p[j + 1]);
+      chk ^= __builtin_bit_cast(uint32_t, pk);
+    }
+  };
+  auto mround = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  };
+  if constexpr (MODE == 3) {
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mround();
+        vround();
+      }
+  } else {
+    if (mf)
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mround();
+    if (va)
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vround();
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  pad[threadIdx.x] = s + (float)chk;
+  __syncthreads();
+  if (pad[(threadIdx.x + 64) % 512] == -1234.5f) sink[blockIdx.x] = s;
+  if (clocks && threadIdx.x % 64 == 0) {
+    clocks[(size_t)blockIdx.x * 8 + w] = __builtin_amdgcn_s_memtime() - t0;
+    // HW_ID bits 5:4 hold the wave's SIMD (s_getreg_b32 size 2, offset 4, register 4)
+    if (simd) simd[(size_t)blockIdx.x * 8 + w] = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +169,20 @@ int mosaic_probe_mfma(float* sink, int blocks, int iters, unsigned long long* cl
   if (!sink || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      sink, iters, clocks);
+  return (int)hipGetLastError();
+}
+
+int mosaic_probe_overlap(float* sink, int blocks, int iters, int mode, unsigned long long* clocks, int* simd,
+                         void* stream) {
+  if (!sink || blocks < 1 || iters < 1 || mode < 0 || mode > 3) return (int)hipErrorInvalidValue;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)blocks), block(512);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(probe_overlap_kernel<0>, grid, block, 0, hs, sink, iters, clocks, simd); break;
+    case 1: hipLaunchKernelGGL(probe_overlap_kernel<1>, grid, block, 0, hs, sink, iters, clocks, simd); break;
+    case 2: hipLaunchKernelGGL(probe_overlap_kernel<2>, grid, block, 0, hs, sink, iters, clocks, simd); break;
+    default: hipLaunchKernelGGL(probe_overlap_kernel<3>, grid, block, 0, hs, sink, iters, clocks, simd); break;
+  }
   return (int)hipGetLastError();
 }
 

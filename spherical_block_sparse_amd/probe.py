@@ -11,7 +11,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_PATH = os.path.join(_HERE, "libmosaic_probe.so")
-EXPORTED = ("mosaic_probe_read", "mosaic_probe_mfma")
+EXPORTED = ("mosaic_probe_read", "mosaic_probe_mfma", "mosaic_probe_overlap")
 _probe = None
 
 
@@ -26,6 +26,8 @@ def lib() -> ctypes.CDLL:
         L.mosaic_probe_read.argtypes = [P, S, P, I, P]
         L.mosaic_probe_mfma.restype = I
         L.mosaic_probe_mfma.argtypes = [P, I, I, P, P]
+        L.mosaic_probe_overlap.restype = I
+        L.mosaic_probe_overlap.argtypes = [P, I, I, I, P, P, P]
         _probe = L
     return _probe
 
@@ -53,3 +55,72 @@ def probe_mfma(sink: torch.Tensor, blocks: int, iters: int, clocks: torch.Tensor
     _check(lib().mosaic_probe_mfma(sink.data_ptr(), blocks, iters, None if clocks is None else clocks.data_ptr(),
                                    torch.cuda.current_stream().cuda_stream), "mosaic_probe_mfma")
     return float(blocks) * 4 * iters * 8 * 16384
+
+
+OVERLAP_MODES = ("MFMA work, every wave", "vector work, every wave",
+                 "MFMA work on waves 0-3, vector work on waves 4-7", "both, interleaved in every wave")
+
+
+def probe_overlap(sink: torch.Tensor, blocks: int, iters: int, mode: int, clocks: torch.Tensor | None = None,
+                  simd: torch.Tensor | None = None) -> None:
+    """One launch of the MFMA / vector overlap probe (include/mosaic_probe.h)."""
+    assert sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= blocks
+    if clocks is not None:
+        assert clocks.is_cuda and clocks.dtype == torch.int64 and clocks.numel() >= 8 * blocks
+    if simd is not None:
+        assert clocks is not None and simd.is_cuda and simd.dtype == torch.int32 and simd.numel() >= 8 * blocks
+    _check(lib().mosaic_probe_overlap(sink.data_ptr(), blocks, iters, mode,
+                                      None if clocks is None else clocks.data_ptr(),
+                                      None if simd is None else simd.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream), "mosaic_probe_overlap")
+
+
+def overlap_report(blocks: int = 1024, iters: int = 1024, reps: int = 5) -> str:
+    """Runs the four overlap modes and returns a text table: the mean launch
+    time (HIP events), each wave's shader clocks per iteration, and what the
+    split mode would take if one wave's MFMAs and the other's vector work ran
+    at the same time (the larger of the two halves) or one after the other
+    (their sum)."""
+    sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
+    simd = torch.zeros(blocks * 8, dtype=torch.int32, device="cuda")
+    ms, per_wave = [], []
+    for mode in range(4):
+        probe_overlap(sink, blocks, iters, mode)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            probe_overlap(sink, blocks, iters, mode)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / reps)
+        probe_overlap(sink, blocks, iters, mode, clocks, simd)
+        torch.cuda.synchronize()
+        c = clocks.view(blocks, 8).double().cpu() / iters
+        per_wave.append((float(c[:, :4].median()), float(c[:, 4:].median())))
+    sid = (simd.view(blocks, 8).cpu() >> 4) & 3
+    paired = float((sid[:, :4] == sid[:, 4:]).all(dim=1).double().mean())
+    t0, t1, t2, t3 = ms
+    lines = [f"blocks {blocks} x 8 waves (one workgroup per compute unit at a time), {iters} iterations per wave",
+             f"waves w and w+4 on one SIMD in {100 * paired:.1f}% of the workgroups (HW_ID)", "",
+             f"{'mode':<58} {'ms':>8} {'clk/iter w0-3':>14} {'clk/iter w4-7':>14}"]
+    for mode in range(4):
+        lines.append(f"{mode} {OVERLAP_MODES[mode]:<56} {ms[mode]:>8.3f} {per_wave[mode][0]:>14.1f} {per_wave[mode][1]:>14.1f}")
+    lines += ["",
+              "mode 2 puts half of mode 0's work and half of mode 1's on every SIMD, one wave of each:",
+              f"  if they ran at the same time it would take max(t0, t1)/2 = {max(t0, t1) / 2:.3f} ms;",
+              f"  one after the other, (t0 + t1)/2 = {(t0 + t1) / 2:.3f} ms; measured {t2:.3f} ms",
+              "mode 3 puts all of both on every wave:",
+              f"  one after the other, t0 + t1 = {t0 + t1:.3f} ms; measured {t3:.3f} ms "
+              f"({100 * (1 - t3 / (t0 + t1)):.1f}% of the sum hidden)"]
+    return "\n".join(lines)
+
+
+if __name__ == "__main__":
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "overlap":
+        print(overlap_report(), flush=True)
+    else:
+        print("usage: python -m spherical_block_sparse_amd.probe overlap", file=sys.stderr)
+        sys.exit(2)
