@@ -18,7 +18,8 @@
 // Launch order:
 //   1. pool and compressed forward (the forward's kernels) recompute q̄, k̄,
 //      v̄ and o_CG;
-//   2. prep: dO to bf16, do_CG_i = sum over block i of g_CG·dO, the g_CG
+//   2. prep: dO to bf16 (one copy per fine branch, signed by its gate),
+//      do_CG_i = sum over block i of g_CG·dO, the g_CG
 //      gradient dO·o_CG, bf16 copies of q̄, k̄, v̄ and do_CG;
 //   3. the compressed branch is dense attention over the m pooled rows, so it
 //      runs through the same two kernels as the local branch with a window
@@ -26,7 +27,7 @@
 //      dq̄, dk̄, dv̄;
 //   4. dq kernel (query-major, tiles of 64 queries as in the forward): per
 //      branch a forward pass over the branch's key chunks (o, log-sum-exp,
-//      D = g·dO·o, the gate gradient) and a backward pass (P from the
+//      dO_b·o, the gate gradient) and a backward pass (P from the
 //      log-sum-exp, dP = dO V^T, dS, dQ^T += K^T dS^T); dq̄/B is added in
 //      the epilogue;
 //   5. the inverted selection (key block -> query blocks that chose it),
