@@ -41,11 +41,16 @@ int mosaic_probe_mfma(float* sink, int blocks, int iters, unsigned long long* cl
  * exp2, 16 bf16 packs and 16 XORs (the fine kernel's vector mix per 64-key
  * chunk and wave).  mode 0: every wave does `iters` iterations of MFMA work;
  * 1: of vector work; 2: waves 0-3 MFMA work and waves 4-7 vector work;
- * 3: every wave both, interleaved.  `clocks` (may be NULL): uint64
+ * 3: every wave both, interleaved; 4: every wave the arithmetic of one
+ * 64-key chunk of the fine kernel per iteration (S^T = K Q^T for two 16-query
+ * sub-tiles, the bf16 weights, the all-ones denominators, O^T += V^T P^T:
+ * 36 MFMAs, 32 FMAs, 32 exp2, 16 packs) with its K and V^T operands read
+ * from LDS as the fine kernel reads them; 5: the same with the operands in
+ * registers.  `clocks` (may be NULL): uint64
  * [blocks][8], each wave's elapsed shader clocks; `simd` (may be NULL, used
  * only with clocks): int32 [blocks][8], each wave's SIMD (HW_ID bits 5:4).
  * `sink` (float32 [blocks]) as above.  hipErrorInvalidValue for a mode
- * outside 0..3. */
+ * outside 0..5. */
 int mosaic_probe_overlap(float* sink, int blocks, int iters, int mode, unsigned long long* clocks, int* simd,
                          void* stream);
 

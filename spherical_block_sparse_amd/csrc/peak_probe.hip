@@ -26,6 +26,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* p, size_t n16, float* sink) {
   const size_t stride = (size_t)gridDim.x * 256;
@@ -153,6 +155,118 @@ __global__ __launch_bounds__(512) void probe_overlap_kernel(float* sink, int ite
   }
 }
 
+// The attention chunk's arithmetic without its loads and barrier: per
+// iteration a wave forms S^T = K Q^T for 64 keys and two 16-query sub-tiles
+// (16 MFMAs), the weights exp2(S c - m) in bf16 (32 FMAs, 32 exp2, 16
+// packs), the denominators with an all-ones operand (4 MFMAs) and
+// O^T += V^T P^T (16 MFMAs), the dependency chain of a 64-key chunk of the
+// fine kernel.  LDS: the K operands are read from a 64 x 64 bf16 tile in LDS
+// (two such K/V tile pairs, alternating between iterations so that the reads
+// stay inside the loop)
+// (8 reads of 16 bytes per lane, rows XOR-swizzled in 16-byte pieces so that
+// 16 consecutive rows hit distinct banks) and the V^T operands with the
+// transposing 8-byte read (16 per lane), as the fine kernel reads them;
+// otherwise the same operands come from registers.
+template <bool LDS>
+__global__ __launch_bounds__(512) void probe_chunk_kernel(float* sink, int iters, unsigned long long* clocks,
+                                                          int* simd) {
+  __shared__ __attribute__((aligned(16))) uint16_t kv[kOverlapLds / 2];   // K tile, V tile, the rest padding
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+  for (int e = threadIdx.x; e < 4 * 64 * 64; e += 512)
+    kv[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>((float)((e * 7) & 15) * 0.0625f - 0.5f));
+  __syncthreads();
+  auto swz = [](int row) { return 2 * ((row >> 1) & 3) + ((row >> 3) & 1); };
+  bf16x8 qf[2][2], kr[4][2], vr[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][kk][e] = static_cast<__bf16>((float)((lane + e + s + kk) & 7) * 0.03125f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kr[i][j][e] = static_cast<__bf16>((float)((lane * 3 + e + i) & 7) * 0.0625f);
+        vr[j][i][e] = static_cast<__bf16>((float)((lane + 5 * e + j) & 7) * 0.0625f);
+      }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
+  floatx4 o[2][4], l[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    l[s] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[s][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c = 0.18033688f, mref = 4.0f;
+  for (int it = 0; it < iters; ++it) {
+    const uint16_t* K = kv + (it & 1) * (2 * 64 * 64);   // this iteration's K tile, its V tile after it
+    const uint16_t* V = K + 64 * 64;
+    floatx4 acc[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) acc[s][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int row = kt * 16 + lr;
+        const bf16x8 ka = LDS ? *reinterpret_cast<const bf16x8*>(K + row * 64 + 8 * ((4 * kk + lg) ^ swz(row)))
+                              : kr[kt][kk];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) acc[s][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[s][kk], acc[s][kt], 0, 0, 0);
+      }
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pb[s][kt >> 1][4 * (kt & 1) + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(acc[s][kt][i], c, -mref)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) l[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[s][j], l[s], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        bf16x8 va;
+        if constexpr (LDS) {
+          const int row = 32 * j + 4 * lg + (lr >> 2);
+          const int col = dt * 16 + 4 * (lr & 3);
+          const uint16_t* src = V + row * 64 + 8 * ((col >> 3) ^ swz(row)) + (col & 7);
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(src));
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(src + 16 * 64));
+          va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          va = vr[j][dt];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) o[s][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[s][j], o[s][dt], 0, 0, 0);
+      }
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    sum += l[s][0];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) sum += o[s][dt][0] + o[s][dt][1] + o[s][dt][2] + o[s][dt][3];
+  }
+  if (sum == -1234.5f || kv[(threadIdx.x * 97) % (kOverlapLds / 2)] == 0x7fc1) sink[blockIdx.x] = sum;
+  if (clocks && lane == 0) {
+    clocks[(size_t)blockIdx.x * 8 + w] = __builtin_amdgcn_s_memtime() - t0;
+    if (simd) simd[(size_t)blockIdx.x * 8 + w] = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,14 +288,16 @@ int mosaic_probe_mfma(float* sink, int blocks, int iters, unsigned long long* cl
 
 int mosaic_probe_overlap(float* sink, int blocks, int iters, int mode, unsigned long long* clocks, int* simd,
                          void* stream) {
-  if (!sink || blocks < 1 || iters < 1 || mode < 0 || mode > 3) return (int)hipErrorInvalidValue;
+  if (!sink || blocks < 1 || iters < 1 || mode < 0 || mode > 5) return (int)hipErrorInvalidValue;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)blocks), block(512);
   switch (mode) {
     case 0: hipLaunchKernelGGL(probe_overlap_kernel<0>, grid, block, 0, hs, sink, iters, clocks, simd); break;
     case 1: hipLaunchKernelGGL(probe_overlap_kernel<1>, grid, block, 0, hs, sink, iters, clocks, simd); break;
     case 2: hipLaunchKernelGGL(probe_overlap_kernel<2>, grid, block, 0, hs, sink, iters, clocks, simd); break;
-    default: hipLaunchKernelGGL(probe_overlap_kernel<3>, grid, block, 0, hs, sink, iters, clocks, simd); break;
+    case 3: hipLaunchKernelGGL(probe_overlap_kernel<3>, grid, block, 0, hs, sink, iters, clocks, simd); break;
+    case 4: hipLaunchKernelGGL(probe_chunk_kernel<true>, grid, block, 0, hs, sink, iters, clocks, simd); break;
+    default: hipLaunchKernelGGL(probe_chunk_kernel<false>, grid, block, 0, hs, sink, iters, clocks, simd); break;
   }
   return (int)hipGetLastError();
 }

@@ -58,7 +58,8 @@ def probe_mfma(sink: torch.Tensor, blocks: int, iters: int, clocks: torch.Tensor
 
 
 OVERLAP_MODES = ("MFMA work, every wave", "vector work, every wave",
-                 "MFMA work on waves 0-3, vector work on waves 4-7", "both, interleaved in every wave")
+                 "MFMA work on waves 0-3, vector work on waves 4-7", "both, interleaved in every wave",
+                 "attention chunk, K and V^T operands from LDS", "attention chunk, operands in registers")
 
 
 def probe_overlap(sink: torch.Tensor, blocks: int, iters: int, mode: int, clocks: torch.Tensor | None = None,
@@ -85,7 +86,7 @@ def overlap_report(blocks: int = 1024, iters: int = 1024, reps: int = 5) -> str:
     clocks = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
     simd = torch.zeros(blocks * 8, dtype=torch.int32, device="cuda")
     ms, per_wave = [], []
-    for mode in range(4):
+    for mode in range(6):
         probe_overlap(sink, blocks, iters, mode)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -101,11 +102,11 @@ def overlap_report(blocks: int = 1024, iters: int = 1024, reps: int = 5) -> str:
         per_wave.append((float(c[:, :4].median()), float(c[:, 4:].median())))
     sid = (simd.view(blocks, 8).cpu() >> 4) & 3
     paired = float((sid[:, :4] == sid[:, 4:]).all(dim=1).double().mean())
-    t0, t1, t2, t3 = ms
+    t0, t1, t2, t3 = ms[:4]
     lines = [f"blocks {blocks} x 8 waves (one workgroup per compute unit at a time), {iters} iterations per wave",
              f"waves w and w+4 on one SIMD in {100 * paired:.1f}% of the workgroups (HW_ID)", "",
              f"{'mode':<58} {'ms':>8} {'clk/iter w0-3':>14} {'clk/iter w4-7':>14}"]
-    for mode in range(4):
+    for mode in range(6):
         lines.append(f"{mode} {OVERLAP_MODES[mode]:<56} {ms[mode]:>8.3f} {per_wave[mode][0]:>14.1f} {per_wave[mode][1]:>14.1f}")
     lines += ["",
               "mode 2 puts half of mode 0's work and half of mode 1's on every SIMD, one wave of each:",
@@ -113,7 +114,11 @@ def overlap_report(blocks: int = 1024, iters: int = 1024, reps: int = 5) -> str:
               f"  one after the other, (t0 + t1)/2 = {(t0 + t1) / 2:.3f} ms; measured {t2:.3f} ms",
               "mode 3 puts all of both on every wave:",
               f"  one after the other, t0 + t1 = {t0 + t1:.3f} ms; measured {t3:.3f} ms "
-              f"({100 * (1 - t3 / (t0 + t1)):.1f}% of the sum hidden)"]
+              f"({100 * (1 - t3 / (t0 + t1)):.1f}% of the sum hidden)",
+              "modes 4 and 5, one 64-key attention chunk per iteration, two waves per SIMD (the older",
+              "wave of a SIMD finishes first; the SIMD is busy until the later one is done):",
+              f"  SIMD clocks per chunk and wave (half the later wave's clocks per iteration): operands from "
+              f"LDS {max(per_wave[4]) / 2:.0f}, from registers {max(per_wave[5]) / 2:.0f}"]
     return "\n".join(lines)
 
 

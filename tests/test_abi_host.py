@@ -76,7 +76,7 @@ def test_probe_header_declares_and_library_exports_the_same_symbols():
     assert L.mosaic_probe_mfma(None, 4, 4, None, None) == INVALID
     assert L.mosaic_probe_mfma(FAKE, 4, 0, None, None) == INVALID
     assert L.mosaic_probe_overlap(None, 4, 4, 0, None, None, None) == INVALID
-    assert L.mosaic_probe_overlap(FAKE, 4, 4, 4, None, None, None) == INVALID
+    assert L.mosaic_probe_overlap(FAKE, 4, 4, 6, None, None, None) == INVALID
     assert L.mosaic_probe_overlap(FAKE, 4, 4, -1, None, None, None) == INVALID
     assert L.mosaic_probe_overlap(FAKE, 0, 4, 0, None, None, None) == INVALID
 
