@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 10
+#define MOSAIC_BSA_ABI_VERSION 11
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -79,9 +79,10 @@ const char* mosaic_last_error(void);
 /* Bytes of device workspace mosaic_bsa_forward needs: pooled q̄, k̄ (float64),
  * pooled v̄ and o_CG (float32), each [batch][heads][m][head_dim], then the
  * largest key norm of each block (float32 [batch][heads][m]), the bf16
- * pieces of k̄ ([batch][heads][m][2][head_dim]) and |k̄_j|^2 (float32
- * [batch][heads][m]), 256-byte aligned sections.  Returns 0 if the shape is
- * invalid or unsupported. */
+ * pieces of k̄ ([batch][heads][m][2][head_dim]), |k̄_j|^2 (float32
+ * [batch][heads][m]) and, per query block, the largest key norm over its
+ * selected blocks (float32 [batch][heads][m]), 256-byte aligned sections.
+ * Returns 0 if the shape is invalid or unsupported. */
 size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn);
 
 /* The whole BSA forward pass (pool -> compressed + selection -> selected and

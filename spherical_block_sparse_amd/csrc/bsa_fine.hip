@@ -73,6 +73,7 @@ struct FineArgs {
   const float* o_cg;
   const int32_t* sel;
   const float* knorm; // largest key norm of each key block [S][m], or null
+  const float* selmax;// per query block, the largest of knorm over its selected blocks [S][m], or null
   float* out;
   float* save_o;      // [S][N][2][D] o_FG, o_L (normalised), SAVE only
   float* save_lse;    // [S][N][2] their log2-sum-exp (log2 units of S*log2(e)/sqrt(d)), SAVE only
@@ -412,8 +413,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       const float qn = sqrtf(q2);
       const int ts = tw + 16 * s;   // the sub-tile's query range is uniform
       float ks = 0.f, kl = 0.f;
-      for (int gi = (ts >> lb) - blk0; gi <= ((ts + 15) >> lb) - blk0; ++gi)
-        for (int j = 0; j < n; ++j) ks = fmaxf(ks, kn[SelT[gi * n + j]]);
+      if (a.selmax) {   // formed by the selection-bound kernel (a sub-tile lies in one block)
+        ks = a.selmax[(size_t)slice * m + (ts >> lb)];
+      } else {
+        for (int gi = (ts >> lb) - blk0; gi <= ((ts + 15) >> lb) - blk0; ++gi)
+          for (int j = 0; j < n; ++j) ks = fmaxf(ks, kn[SelT[gi * n + j]]);
+      }
       const int ulo = max(0, ts - lo_off);
       const int uhi = (int)min((long long)N, (long long)ts + 15 + hi_off);
       for (int bl = ulo >> lb; bl <= (uhi - 1) >> lb; ++bl) kl = fmaxf(kl, kn[bl]);
@@ -807,6 +812,23 @@ hipError_t launch_generic(FineArgs a, long long slices, hipStream_t stream) {
 
 // One workgroup per tile of 32*WAVES queries of every slice: the tile size
 // fixes the tile count and the grid together.
+// For each query block, the largest key norm over its selected blocks (the
+// same clamped indices and the same maximum the fine kernel's prologue would
+// form from the selection table), one thread per row.
+__global__ __launch_bounds__(256) void sel_bound_kernel(const int32_t* sel, const float* knorm, float* selmax,
+                                                        long long rows, int m, int n) {
+  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const float* kn = knorm + (r / m) * m;
+  const int32_t* row = sel + r * n;
+  float mx = 0.f;
+  for (int j = 0; j < n; ++j) {
+    const int b = row[j];
+    mx = fmaxf(mx, kn[b < 0 ? 0 : (b >= m ? m - 1 : b)]);
+  }
+  selmax[r] = mx;
+}
+
 template <int D, int WAVES>
 hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
   a.tiles = a.n_tok / (32 * WAVES);
@@ -827,7 +849,7 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
                        hipStream_t stream, const float* knorm, float* save_o, float* save_lse,
-                       uint16_t* out_merged, int heads) {
+                       uint16_t* out_merged, int heads, float* selmax) {
   FineArgs a;
   a.q = q;
   a.k = k;
@@ -836,6 +858,7 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.o_cg = o_cg;
   a.sel = sel;
   a.knorm = knorm;
+  a.selmax = nullptr;
   a.out = out;
   a.save_o = save_o;
   a.save_lse = save_lse;
@@ -856,6 +879,14 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   const long long table = (long long)(block >= tile ? 1 : tile / block) * topn;
   if (block < 16 || table > kSelTable)
     return head_dim == 64 ? launch_generic<64>(a, slices, stream) : launch_generic<32>(a, slices, stream);
+  if (knorm && selmax) {   // the selected branch's score bounds, formed once per query block
+    const long long rows = slices * a.m;
+    hipLaunchKernelGGL(sel_bound_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, sel, knorm,
+                       selmax, rows, a.m, topn);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.selmax = selmax;
+  }
   if (head_dim == 64) return wide ? launch<64, 4>(a, slices, stream) : launch<64, 2>(a, slices, stream);
   return wide ? launch<32, 4>(a, slices, stream) : launch<32, 2>(a, slices, stream);
 }

@@ -39,7 +39,8 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
                        hipStream_t stream, const float* knorm = nullptr, float* save_o = nullptr,
-                       float* save_lse = nullptr, uint16_t* out_merged = nullptr, int heads = 1);
+                       float* save_lse = nullptr, uint16_t* out_merged = nullptr, int heads = 1,
+                       float* selmax = nullptr);
 
 // Everything the backward launches read and write (device pointers; the
 // workspace buffers are carved by the C-ABI entry point).

@@ -87,7 +87,7 @@ mosaic_status check_shape(int batch, int heads, int head_dim, int nside, int blo
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Workspace {
-  size_t qbar, kbar, vbar, ocg, knorm, kpieces, kbn2, total;
+  size_t qbar, kbar, vbar, ocg, knorm, kpieces, kbn2, selmax, total;
 };
 
 Workspace layout(const Shape& s) {
@@ -100,7 +100,8 @@ Workspace layout(const Shape& s) {
   w.knorm = w.ocg + align256(e * sizeof(float));
   w.kpieces = w.knorm + align256((size_t)s.slices * s.m * sizeof(float));
   w.kbn2 = w.kpieces + align256(e * 2 * sizeof(uint16_t));
-  w.total = w.kbn2 + align256((size_t)s.slices * s.m * sizeof(float));
+  w.selmax = w.kbn2 + align256((size_t)s.slices * s.m * sizeof(float));
+  w.total = w.selmax + align256((size_t)s.slices * s.m * sizeof(float));
   return w;
 }
 
@@ -224,7 +225,8 @@ mosaic_status run_forward(const Shape& s, const void* q, const void* k, const vo
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
-                          s.block, s.topn, s.window, hs, knorm);
+                          s.block, s.topn, s.window, hs, knorm, nullptr, nullptr, nullptr, 1,
+                          reinterpret_cast<float*>(ws + w.selmax));
   return hip_status(e, "bsa_fine launch");
 }
 
@@ -508,7 +510,7 @@ mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const vo
                                      kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
   e = mosaic::launch_fine(q, k, v, gates, ocg, sel_idx, nullptr, s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
-                          hs, knorm, nullptr, nullptr, attn, heads);
+                          hs, knorm, nullptr, nullptr, attn, heads, reinterpret_cast<float*>(bws + w.selmax));
   if (e != hipSuccess) return hip_status(e, "bsa_fine launch");
   return hip_status(mosaic::launch_layer_out_merged(attn, static_cast<const uint16_t*>(w_out),
                                                     static_cast<const uint16_t*>(x), batch, s.n_tok, channels, heads,
@@ -557,7 +559,8 @@ mosaic_status mosaic_bsa_forward_train(const void* q, const void* k, const void*
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
                           s.block, s.topn, s.window, hs, knorm, reinterpret_cast<float*>(base + sv.o),
-                          reinterpret_cast<float*>(base + sv.lse));
+                          reinterpret_cast<float*>(base + sv.lse), nullptr, 1,
+                          reinterpret_cast<float*>(ws + w.selmax));
   return hip_status(e, "bsa_fine launch");
 }
 

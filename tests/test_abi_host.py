@@ -95,14 +95,14 @@ def test_version_and_status_strings():
 def test_workspace_bytes_layout():
     L = _lib.lib()
     # ns128: S = 192, m = 3072, d = 64 -> two float64 and two float32 [S][m][d] sections, the
-    # float32 [S][m] largest key norm per block, the bf16 [S][m][2][d] pieces of k̄ and the
-    # float32 [S][m] |k̄_j|^2
+    # float32 [S][m] largest key norm per block, the bf16 [S][m][2][d] pieces of k̄, the
+    # float32 [S][m] |k̄_j|^2 and the float32 [S][m] selected-block bound per query block
     e = 192 * 3072 * 64
-    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) == e * (8 + 8 + 4 + 4 + 4) + 192 * 3072 * 4 * 2
+    assert L.mosaic_bsa_workspace_bytes(24, 8, 64, 128, 64, 16) == e * (8 + 8 + 4 + 4 + 4) + 192 * 3072 * 4 * 3
     # tiny: S = 2, m = 48, d = 32 -> sections rounded up to 256 bytes
     e = 2 * 48 * 32
     r = lambda x: (x + 255) // 256 * 256
-    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 4) == 2 * r(8 * e) + 3 * r(4 * e) + 2 * r(4 * 2 * 48)
+    assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 4) == 2 * r(8 * e) + 3 * r(4 * e) + 3 * r(4 * 2 * 48)
     assert L.mosaic_bsa_workspace_bytes(1, 2, 32, 8, 16, 0) == 0      # invalid -> 0
     assert L.mosaic_bsa_workspace_bytes(1, 2, 48, 8, 16, 4) == 0      # unsupported -> 0
 
