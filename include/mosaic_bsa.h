@@ -86,7 +86,9 @@ const char* mosaic_last_error(void);
 size_t mosaic_bsa_workspace_bytes(int batch, int heads, int head_dim, int nside, int block, int topn);
 
 /* The whole BSA forward pass (pool -> compressed + selection -> selected and
- * local fine attention with the gated sum), three kernels on `stream`.
+ * local fine attention with the gated sum), three kernels on `stream` (with
+ * a small fourth between the last two that forms each query block's
+ * selected-branch score bound, and the selection's float64 redo launch).
  *   q, k, v   in : bf16 bits [batch][heads][N][head_dim]
  *   gates     in : float32 [batch][heads][N][3]
  *   out       out: float32 [batch][heads][N][head_dim]
