@@ -197,12 +197,15 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
                                         kpieces=kpieces, kbn2=kbn2)
     cs = lambda: _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel2,
                                                  kpieces=kpieces, kbn2=kbn2)
+    sb = torch.empty((cfg.batch, cfg.heads, cfg.n_blocks), dtype=torch.float32, device=dev)
+    bound = lambda: _lib.mosaic_bsa_select_bound(sel2, knorm, cfg.nside, cfg.block, cfg.topn, cfg.head_dim, sb)
     fine = lambda: _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel2, cfg.nside, cfg.block, cfg.topn, cfg.window, out2,
-                                        knorm=knorm)
-    pool(); cs(); fine()
+                                        knorm=knorm, sel_bound=sb)
+    pool(); cs(); bound(); fine()
     kt = max(3, steps // 2)
     pool_ms = time_stream(pool, kt)
     cs_ms = time_stream(cs, kt)
+    bound_ms = time_stream(bound, kt)
     fine_ms = time_stream(fine, kt)
     torch.cuda.synchronize()
     same = bool(torch.equal(sel, sel2) and torch.equal(out, out2))
@@ -245,7 +248,7 @@ def measure(cfg: BSAConfig, steps: int, warmup: int, backward: bool = True) -> d
     res = dict(backward=bwd,
         cfg=cfg, ms=ms, tokens_per_s=cfg.tokens / (ms * 1e-3),
         step_ms={"median": float(np.median(per_step)), "min": min(per_step), "max": max(per_step)},
-        pool_ms=pool_ms, cs_ms=cs_ms, fine_ms=fine_ms, stages_match_forward=same,
+        pool_ms=pool_ms, cs_ms=cs_ms, bound_ms=bound_ms, fine_ms=fine_ms, stages_match_forward=same,
         fine_tflops=ff / (fine_ms * 1e-3) / 1e12, fine_flops=ff,
         pool_gbs=pool_bytes(cfg) / (pool_ms * 1e-3) / 1e9, pool_bytes=pool_bytes(cfg),
         cs_tflops=compress_flops(cfg) / (cs_ms * 1e-3) / 1e12,
@@ -451,7 +454,8 @@ def main() -> int:
         secondary = {
             "workload": s["cfg"].name, "value": s["tokens_per_s"], "unit": "tokens/s", "ms_per_step": s["ms"],
             "step_ms": s["step_ms"],
-            "kernels_ms": {"pool": s["pool_ms"], "compress_select": s["cs_ms"], "fine": s["fine_ms"]},
+            "kernels_ms": {"pool": s["pool_ms"], "compress_select": s["cs_ms"], "select_bound": s["bound_ms"],
+                           "fine": s["fine_ms"]},
             "fine_mfma_frac": s["fine_tflops"] / PEAK_BF16_TFLOPS,
             "compress_select_frac": compress_bound_ms(s["cfg"]) / s["cs_ms"],
             "pool_hbm_frac": s["pool_gbs"] / PEAK_HBM_GBS,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOSAIC_BSA_ABI_VERSION 11
+#define MOSAIC_BSA_ABI_VERSION 12
 
 typedef enum mosaic_status {
   MOSAIC_OK = 0,
@@ -164,11 +164,27 @@ mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar,
  * bound c·|q|·knorm as the fixed softmax reference in place of a running
  * maximum (the same softmax up to rounding).  A knorm that understates a
  * norm by a factor f lets weights grow to 2^((f-1)·bound): pass the pool's
- * own output. */
+ * own output.  sel_bound (may be NULL; not part of the method): with knorm,
+ * mosaic_bsa_select_bound's output for the same sel_idx and knorm, which
+ * the tiled kernel then reads in place of gathering knorm over each query
+ * block's selected blocks (the same results); given without knorm:
+ * MOSAIC_ERR_NULL_POINTER.  Alignment of sel_bound: 4 bytes. */
 mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const float* gates,
-                              const float* o_cg, const int32_t* sel_idx, const float* knorm, int batch,
-                              int heads, int head_dim, int nside, int block, int topn, int window,
-                              float* out, void* stream);
+                              const float* o_cg, const int32_t* sel_idx, const float* knorm,
+                              const float* sel_bound, int batch, int heads, int head_dim, int nside, int block,
+                              int topn, int window, float* out, void* stream);
+
+/* The selected branch's score bound per query block (not part of the
+ * method): sel_bound [batch][heads][m] float32 = the largest knorm over the
+ * topn blocks sel_idx [batch][heads][m][topn] lists for that query block
+ * (indices clamped into [0, m)), knorm [batch][heads][m] from
+ * mosaic_bsa_pool.  mosaic_bsa_forward, mosaic_bsa_forward_train and
+ * mosaic_bsa_layer_forward form it in their workspaces between the
+ * selection and the fine kernel; with this call a caller of the stages does
+ * the same for mosaic_bsa_fine.  Alignment: 4 bytes. */
+mosaic_status mosaic_bsa_select_bound(const int32_t* sel_idx, const float* knorm, int batch, int heads,
+                                      int head_dim, int nside, int block, int topn, float* sel_bound,
+                                      void* stream);
 
 /* ---- HEALPix coarsening ---------------------------------------------------
  * A field on the NESTED pixels at nside taken to nside / 2^levels

@@ -27,7 +27,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "mosaic_bsa_abi_version", "mosaic_status_string", "mosaic_last_error",
     "mosaic_bsa_workspace_bytes", "mosaic_bsa_forward", "mosaic_bsa_forward_noalloc", "mosaic_bsa_pool",
-    "mosaic_bsa_compress_select", "mosaic_bsa_fine",
+    "mosaic_bsa_compress_select", "mosaic_bsa_fine", "mosaic_bsa_select_bound",
     "mosaic_bsa_saved_bytes", "mosaic_bsa_forward_train",
     "mosaic_bsa_layer_workspace_bytes", "mosaic_bsa_layer_forward", "mosaic_bsa_layer_in", "mosaic_bsa_layer_out",
     "mosaic_bsa_layer_out_merged",
@@ -70,7 +70,9 @@ def lib() -> ctypes.CDLL:
         L.mosaic_bsa_compress_select.restype = I
         L.mosaic_bsa_compress_select.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P]
         L.mosaic_bsa_fine.restype = I
-        L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+        L.mosaic_bsa_fine.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+        L.mosaic_bsa_select_bound.restype = I
+        L.mosaic_bsa_select_bound.argtypes = [P, P, I, I, I, I, I, I, P, P]
         L.mosaic_bsa_backward_workspace_bytes.restype = S
         L.mosaic_bsa_backward_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.mosaic_interp_workspace_bytes.restype = S
@@ -233,9 +235,10 @@ def mosaic_bsa_compress_select(qbar, kbar, vbar, nside, block, topn, o_cg=None, 
 
 
 def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, out=None, knorm=None,
-                    stream=None):
+                    sel_bound=None, stream=None):
     """out [b,H,N,d] fp32: gated sum of o_cg with the selected and local fine branches.  knorm: the
-    pool's largest key norm per block (float32 [b,H,m]), or None for the running-maximum softmax."""
+    pool's largest key norm per block (float32 [b,H,m]), or None for the running-maximum softmax.
+    sel_bound: mosaic_bsa_select_bound's output for the same sel_idx and knorm, or None."""
     b, h, n, d = _dims(q, nside)
     m = n // block
     out = torch.empty((b, h, n, d), dtype=torch.float32, device=q.device) if out is None else out
@@ -244,8 +247,23 @@ def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, o
         _ptr(v, torch.bfloat16, (b, h, n, d), "v"), _ptr(gates, torch.float32, (b, h, n, 3), "gates"),
         _ptr(o_cg, torch.float32, (b, h, m, d), "o_cg"), _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"),
         None if knorm is None else _ptr(knorm, torch.float32, (b, h, m), "knorm"),
+        None if sel_bound is None else _ptr(sel_bound, torch.float32, (b, h, m), "sel_bound"),
         b, h, d, nside, block, topn, window, _ptr(out, torch.float32, (b, h, n, d), "out"), _stream(stream)))
     return out
+
+
+def mosaic_bsa_select_bound(sel_idx, knorm, nside, block, topn, head_dim, sel_bound=None, stream=None):
+    """sel_bound [b,H,m] fp32: the largest knorm over each query block's topn selected blocks."""
+    b, h, m, t = sel_idx.shape
+    if t != topn:
+        raise ValueError(f"sel_idx has {t} entries per row, topn is {topn}")
+    sel_bound = torch.empty((b, h, m), dtype=torch.float32, device=sel_idx.device) if sel_bound is None \
+        else sel_bound
+    _check(lib().mosaic_bsa_select_bound(
+        _ptr(sel_idx, torch.int32, (b, h, m, topn), "sel_idx"), _ptr(knorm, torch.float32, (b, h, m), "knorm"),
+        b, h, head_dim, nside, block, topn, _ptr(sel_bound, torch.float32, (b, h, m), "sel_bound"),
+        _stream(stream)))
+    return sel_bound
 
 
 def mosaic_bsa_saved_bytes(batch, heads, head_dim, nside, block) -> int:

@@ -845,11 +845,19 @@ hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
 
 }  // namespace
 
+// Whether launch_fine takes the tiled kernel: blocks of at least 16 tokens and
+// the tile's selection rows within its table (T = 128 queries when a block
+// holds >= 128 tokens and N allows, else 64).
+bool fine_tiled(int n_tok, int block, int topn) {
+  const int tile = block >= 128 && n_tok % 128 == 0 ? 128 : 64;
+  return block >= 16 && (long long)(block >= tile ? 1 : tile / block) * topn <= kSelTable;
+}
+
 hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gates,
                        const float* o_cg, const int32_t* sel, float* out, long long slices,
                        int n_tok, int head_dim, int block, int topn, int window,
                        hipStream_t stream, const float* knorm, float* save_o, float* save_lse,
-                       uint16_t* out_merged, int heads, float* selmax) {
+                       uint16_t* out_merged, int heads, const float* selmax) {
   FineArgs a;
   a.q = q;
   a.k = k;
@@ -858,7 +866,7 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.o_cg = o_cg;
   a.sel = sel;
   a.knorm = knorm;
-  a.selmax = nullptr;
+  a.selmax = knorm ? selmax : nullptr;
   a.out = out;
   a.save_o = save_o;
   a.save_lse = save_lse;
@@ -872,23 +880,21 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
   // 128-query tiles when a block holds >= 128 tokens (N is then a multiple of
   // 128), else 64 (N = 12*nside^2 with nside^2 >= block >= 16 is a multiple of 64)
-  const bool wide = block >= 128 && n_tok % 128 == 0;
+  const bool wide = block >= 128 && n_tok % 128 == 0;   // as in fine_tiled
   // the tiled kernel's selection table holds kSelTable entries: the rows of
   // the tile's T/block query blocks (one row when block >= T)
-  const int tile = wide ? 128 : 64;
-  const long long table = (long long)(block >= tile ? 1 : tile / block) * topn;
-  if (block < 16 || table > kSelTable)
+  if (!fine_tiled(n_tok, block, topn))
     return head_dim == 64 ? launch_generic<64>(a, slices, stream) : launch_generic<32>(a, slices, stream);
-  if (knorm && selmax) {   // the selected branch's score bounds, formed once per query block
-    const long long rows = slices * a.m;
-    hipLaunchKernelGGL(sel_bound_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, sel, knorm,
-                       selmax, rows, a.m, topn);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    a.selmax = selmax;
-  }
   if (head_dim == 64) return wide ? launch<64, 4>(a, slices, stream) : launch<64, 2>(a, slices, stream);
   return wide ? launch<32, 4>(a, slices, stream) : launch<32, 2>(a, slices, stream);
+}
+
+hipError_t launch_sel_bound(const int32_t* sel, const float* knorm, float* sel_bound, long long slices, int m,
+                            int topn, hipStream_t stream) {
+  const long long rows = slices * m;
+  hipLaunchKernelGGL(sel_bound_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, sel, knorm,
+                     sel_bound, rows, m, topn);
+  return hipGetLastError();
 }
 
 }  // namespace mosaic

@@ -40,7 +40,15 @@ hipError_t launch_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        int n_tok, int head_dim, int block, int topn, int window,
                        hipStream_t stream, const float* knorm = nullptr, float* save_o = nullptr,
                        float* save_lse = nullptr, uint16_t* out_merged = nullptr, int heads = 1,
-                       float* selmax = nullptr);
+                       const float* selmax = nullptr);
+
+// whether launch_fine runs the tiled kernel (the one that reads selmax)
+bool fine_tiled(int n_tok, int block, int topn);
+
+// selmax[r] = max over row r's topn selected blocks of knorm (indices clamped
+// into [0, m)), r < slices * m: the selected branch's score bound per query block
+hipError_t launch_sel_bound(const int32_t* sel, const float* knorm, float* sel_bound, long long slices, int m,
+                            int topn, hipStream_t stream);
 
 // Everything the backward launches read and write (device pointers; the
 // workspace buffers are carved by the C-ABI entry point).

@@ -204,6 +204,13 @@ LayerWorkspace layer_layout(const Shape& s) {
 }
 
 
+// The selected branch's score bound per query block, for the tiled fine
+// kernel only (the one-wave kernels do not use it).
+hipError_t sel_bound(const Shape& s, const int32_t* sel_idx, const float* knorm, float* selmax, hipStream_t hs) {
+  if (!mosaic::fine_tiled(s.n_tok, s.block, s.topn)) return hipSuccess;
+  return mosaic::launch_sel_bound(sel_idx, knorm, selmax, s.slices, s.m, s.topn, hs);
+}
+
 // The forward's three launches on a validated shape, with the workspace at ws
 // (layout(s).total bytes, 256-byte aligned).
 mosaic_status run_forward(const Shape& s, const void* q, const void* k, const void* v, const float* gates,
@@ -223,10 +230,11 @@ mosaic_status run_forward(const Shape& s, const void* q, const void* k, const vo
   e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs, kpieces,
                                      kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  float* selmax = reinterpret_cast<float*>(ws + w.selmax);
+  if ((e = sel_bound(s, sel_idx, knorm, selmax, hs)) != hipSuccess) return hip_status(e, "selection bound launch");
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
-                          s.block, s.topn, s.window, hs, knorm, nullptr, nullptr, nullptr, 1,
-                          reinterpret_cast<float*>(ws + w.selmax));
+                          s.block, s.topn, s.window, hs, knorm, nullptr, nullptr, nullptr, 1, selmax);
   return hip_status(e, "bsa_fine launch");
 }
 
@@ -300,21 +308,37 @@ mosaic_status mosaic_bsa_compress_select(const double* qbar, const double* kbar,
 }
 
 mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const float* gates,
-                              const float* o_cg, const int32_t* sel_idx, const float* knorm, int batch,
-                              int heads, int head_dim, int nside, int block, int topn, int window,
-                              float* out, void* stream) {
+                              const float* o_cg, const int32_t* sel_idx, const float* knorm,
+                              const float* sel_bound, int batch, int heads, int head_dim, int nside, int block,
+                              int topn, int window, float* out, void* stream) {
   REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(gates); REQUIRE_PTR(o_cg);
   REQUIRE_PTR(sel_idx); REQUIRE_PTR(out);
   REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(gates, 4);
   REQUIRE_ALIGN(o_cg, 16); REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(knorm, 4);
+  REQUIRE_ALIGN(sel_bound, 4);
+  if (sel_bound && !knorm) return fail(MOSAIC_ERR_NULL_POINTER, "sel_bound is given without knorm");
   Shape s;
   mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, window, kUsesTopn | kUsesWindow, &s);
   if (st != MOSAIC_OK) return st;
   return hip_status(mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                         static_cast<const uint16_t*>(v), gates, o_cg, sel_idx, out,
                                         s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
-                                        static_cast<hipStream_t>(stream), knorm),
+                                        static_cast<hipStream_t>(stream), knorm, nullptr, nullptr, nullptr, 1,
+                                        sel_bound),
                     "bsa_fine launch");
+}
+
+mosaic_status mosaic_bsa_select_bound(const int32_t* sel_idx, const float* knorm, int batch, int heads,
+                                      int head_dim, int nside, int block, int topn, float* sel_bound,
+                                      void* stream) {
+  REQUIRE_PTR(sel_idx); REQUIRE_PTR(knorm); REQUIRE_PTR(sel_bound);
+  REQUIRE_ALIGN(sel_idx, 4); REQUIRE_ALIGN(knorm, 4); REQUIRE_ALIGN(sel_bound, 4);
+  Shape s;
+  mosaic_status st = check_shape(batch, heads, head_dim, nside, block, topn, 0, kUsesTopn, &s);
+  if (st != MOSAIC_OK) return st;
+  return hip_status(mosaic::launch_sel_bound(sel_idx, knorm, sel_bound, s.slices, s.m, s.topn,
+                                             static_cast<hipStream_t>(stream)),
+                    "selection bound launch");
 }
 
 mosaic_status mosaic_bsa_forward(const void* q, const void* k, const void* v, const float* gates,
@@ -509,8 +533,10 @@ mosaic_status mosaic_bsa_layer_forward(const void* x, const void* w_in, const vo
   e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs, kpieces,
                                      kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  float* selmax = reinterpret_cast<float*>(bws + w.selmax);
+  if ((e = sel_bound(s, sel_idx, knorm, selmax, hs)) != hipSuccess) return hip_status(e, "selection bound launch");
   e = mosaic::launch_fine(q, k, v, gates, ocg, sel_idx, nullptr, s.slices, s.n_tok, s.d, s.block, s.topn, s.window,
-                          hs, knorm, nullptr, nullptr, attn, heads, reinterpret_cast<float*>(bws + w.selmax));
+                          hs, knorm, nullptr, nullptr, attn, heads, selmax);
   if (e != hipSuccess) return hip_status(e, "bsa_fine launch");
   return hip_status(mosaic::launch_layer_out_merged(attn, static_cast<const uint16_t*>(w_out),
                                                     static_cast<const uint16_t*>(x), batch, s.n_tok, channels, heads,
@@ -556,11 +582,12 @@ mosaic_status mosaic_bsa_forward_train(const void* q, const void* k, const void*
   e = mosaic::launch_compress_select(qbar, kbar, vbar, ocg, sel_idx, s.slices, s.m, s.d, s.topn, hs, kpieces,
                                      kbn2);
   if (e != hipSuccess) return hip_status(e, "bsa_compress_select launch");
+  float* selmax = reinterpret_cast<float*>(ws + w.selmax);
+  if ((e = sel_bound(s, sel_idx, knorm, selmax, hs)) != hipSuccess) return hip_status(e, "selection bound launch");
   e = mosaic::launch_fine(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), gates, ocg, sel_idx, out, s.slices, s.n_tok, s.d,
                           s.block, s.topn, s.window, hs, knorm, reinterpret_cast<float*>(base + sv.o),
-                          reinterpret_cast<float*>(base + sv.lse), nullptr, 1,
-                          reinterpret_cast<float*>(ws + w.selmax));
+                          reinterpret_cast<float*>(base + sv.lse), nullptr, 1, selmax);
   return hip_status(e, "bsa_fine launch");
 }
 

@@ -95,8 +95,9 @@ def main() -> int:
         knorm = torch.empty((cfg.batch, cfg.heads, cfg.n_blocks), dtype=torch.float32, device=q.device)
         qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
         o_cg, sel2 = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
+        sb = _lib.mosaic_bsa_select_bound(sel2, knorm, cfg.nside, cfg.block, cfg.topn, cfg.head_dim)
         fine = lambda: _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel2, cfg.nside, cfg.block, cfg.topn, cfg.window,
-                                            out, knorm=knorm)
+                                            out, knorm=knorm, sel_bound=sb)
         fwd = lambda: _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window, out, sel)
         fine_ms, fwd_ms = time_ms(fine, args.steps), time_ms(fwd, args.steps)
         s = sel.view(-1, cfg.n_blocks, cfg.topn)[: args.stat_slices].cpu().numpy()

@@ -72,6 +72,7 @@ def main() -> int:
     qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm, kpieces=kp, kbn2=kb2)
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, kpieces=kp,
                                                 kbn2=kb2)
+    sb = _lib.mosaic_bsa_select_bound(sel, knorm, cfg.nside, cfg.block, cfg.topn, d)
     torch.cuda.synchronize()
     if args.stage == "backward":
         _, sel_t, saved = _lib.mosaic_bsa_forward_train(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
@@ -92,7 +93,8 @@ def main() -> int:
             _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, o_cg, sel, kpieces=kp,
                                             kbn2=kb2)
         elif args.stage == "fine":
-            _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
+            _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm,
+                                 sel_bound=sb)
         else:
             _lib.mosaic_bsa_forward(q, k, v, g, cfg.nside, cfg.block, cfg.topn, cfg.window)
     torch.cuda.synchronize()

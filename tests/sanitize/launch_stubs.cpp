@@ -29,7 +29,11 @@ hipError_t launch_compress_select(const double*, const double*, const float*, fl
 }
 hipError_t launch_fine(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*, const int32_t*,
                        float*, long long, int, int, int, int, int, hipStream_t, const float*, float*, float*,
-                       uint16_t*, int, float*) {
+                       uint16_t*, int, const float*) {
+  return reached();
+}
+bool fine_tiled(int, int, int) { return true; }
+hipError_t launch_sel_bound(const int32_t*, const float*, float*, long long, int, int, hipStream_t) {
   return reached();
 }
 hipError_t launch_layer_in(const uint16_t*, const uint16_t*, long long, int, int, int, int, uint16_t*, uint16_t*,

@@ -154,11 +154,21 @@ def test_stage_entry_points_validate():
     assert cs(1, 2, 32, 8, 16, 4, FAKE, None, FAKE, FAKE) == NULL
     assert cs(1, 2, 32, 8, 16, 4, None, FAKE, FAKE, FAKE) == NULL
     assert cs(1, 2, 32, 8, 16, 4, FAKE + 8, FAKE, FAKE, FAKE) == MISAL
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 32, 8, 16, 4, 0, FAKE, None) == SHAPE
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 32, 8, 16, 4, 32, FAKE, None) == NULL
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 48, 8, 16, 4, 32, FAKE, None) == UNSUP
-    assert L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 2, 32, 8, 16, 4, 32, FAKE,
-                             None) == MISAL
+    fine = lambda *a: L.mosaic_bsa_fine(FAKE, FAKE, FAKE, FAKE, FAKE, *a, None)
+    assert fine(FAKE, None, None, 1, 2, 32, 8, 16, 4, 0, FAKE) == SHAPE
+    assert fine(None, None, None, 1, 2, 32, 8, 16, 4, 32, FAKE) == NULL
+    assert fine(FAKE, None, None, 1, 2, 48, 8, 16, 4, 32, FAKE) == UNSUP
+    assert fine(FAKE, FAKE + 2, None, 1, 2, 32, 8, 16, 4, 32, FAKE) == MISAL
+    assert fine(FAKE, FAKE, FAKE + 2, 1, 2, 32, 8, 16, 4, 32, FAKE) == MISAL
+    assert fine(FAKE, None, FAKE, 1, 2, 32, 8, 16, 4, 32, FAKE) == NULL          # a bound without knorm
+    bound = lambda *a: L.mosaic_bsa_select_bound(*a, None)
+    assert bound(FAKE, FAKE, 1, 2, 32, 8, 16, 0, FAKE) == SHAPE                   # topn 0
+    assert bound(FAKE, FAKE, 1, 2, 32, 8, 16, 49, FAKE) == SHAPE                  # topn above m = 48
+    assert bound(None, FAKE, 1, 2, 32, 8, 16, 4, FAKE) == NULL
+    assert bound(FAKE, None, 1, 2, 32, 8, 16, 4, FAKE) == NULL
+    assert bound(FAKE, FAKE, 1, 2, 32, 8, 16, 4, None) == NULL
+    assert bound(FAKE, FAKE, 1, 2, 32, 8, 16, 4, FAKE + 2) == MISAL
+    assert bound(FAKE, FAKE, 1, 2, 32, 12, 16, 4, FAKE) == SHAPE                  # nside not a power of two
 
 
 def test_python_binding_rejects_bad_tensors_without_launch():

@@ -283,7 +283,11 @@ def test_fine_score_bound_paths(name, scale):
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
     out_b = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
     out_l = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window)
+    sb = _lib.mosaic_bsa_select_bound(sel, knorm, cfg.nside, cfg.block, cfg.topn, cfg.head_dim)
+    out_s = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm,
+                                 sel_bound=sb)
     torch.cuda.synchronize()
+    assert torch.equal(out_b, out_s)     # the precomputed bound is the one the kernel gathers
     for (b, h) in [(0, 0), (cfg.batch - 1, cfg.heads - 1)]:
         gi = sel[b, h].cpu().numpy()
         ref = oracle.bsa_slice_ref(_slice(q, b, h), _slice(k, b, h), _slice(v, b, h), _slice(g, b, h),
@@ -505,8 +509,14 @@ def test_forward_equals_stages():
     o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn, kpieces=kp,
                                                 kbn2=kb2)
     out2 = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
+    sb = _lib.mosaic_bsa_select_bound(sel, knorm, cfg.nside, cfg.block, cfg.topn, cfg.head_dim)
+    out3 = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm,
+                                sel_bound=sb)
     torch.cuda.synchronize()
-    assert torch.equal(idx, sel) and torch.equal(out, out2)
+    assert torch.equal(idx, sel) and torch.equal(out, out2) and torch.equal(out, out3)
+    # the bound is a maximum of stored values: exact
+    want = torch.gather(knorm.unsqueeze(2).expand(-1, -1, cfg.n_blocks, -1), 3, sel.long()).amax(dim=3)
+    assert torch.equal(sb, want)
 
 
 # ------------------------------- blocks of 1 and 4 tokens, top-n above 64 ---
