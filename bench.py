@@ -507,6 +507,7 @@ def main() -> int:
                                 "bound_ms": compress_bound_ms(c), "frac": compress_bound_ms(c) / r["cs_ms"],
                                 "achieved_TFLOPs": r["cs_tflops"],
                                 "traffic": measured_traffic(f"select_{c.name}")},
+            "select_bound": {"ms": r["bound_ms"]},
             "fine": {"ms": r["fine_ms"], "frac_bf16_peak": r["fine_tflops"] / PEAK_BF16_TFLOPS},
             "stages_match_forward": r["stages_match_forward"],
         },
