@@ -653,3 +653,27 @@ def test_edge_smallest_spheres(cfg):
     if cfg.topn == cfg.n_blocks:   # every row selects every block, in ascending order
         want = torch.arange(cfg.n_blocks, dtype=torch.int32).expand(cfg.batch, cfg.heads, cfg.n_blocks, cfg.n_blocks)
         assert torch.equal(idx.cpu(), want)
+
+
+@pytest.mark.parametrize("cfg", [B1, B4, CONFIGS["ns32"].with_(name="ns32-b16-top80", block=16, heads=2, topn=80,
+                                                                 seed=325),
+                                 CONFIGS["ns32"].with_(name="ns32-top80", heads=2, topn=80, seed=326)],
+                         ids=lambda c: c.name)
+def test_select_bound_beyond_the_forward_shapes(cfg):
+    """mosaic_bsa_select_bound where the fine attention runs the one-wave kernel (blocks of 1 or 4
+    tokens; 4 query blocks of 16 tokens x 80 selected overflow the tiled kernel's table), which
+    forms its references itself, and where the tiled kernel reads it with top-n above 64 (blocks of
+    64): the bound is the exact maximum of the selected blocks' norms, and the fine stage given it
+    is bit-identical to the stage without it."""
+    q, k, v, g = _gpu_inputs(cfg)
+    knorm = _knorm(cfg)
+    qbar, kbar, vbar = _lib.mosaic_bsa_pool(q, k, v, cfg.nside, cfg.block, knorm=knorm)
+    o_cg, sel = _lib.mosaic_bsa_compress_select(qbar, kbar, vbar, cfg.nside, cfg.block, cfg.topn)
+    sb = _lib.mosaic_bsa_select_bound(sel, knorm, cfg.nside, cfg.block, cfg.topn, cfg.head_dim)
+    out_a = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm)
+    out_b = _lib.mosaic_bsa_fine(q, k, v, g, o_cg, sel, cfg.nside, cfg.block, cfg.topn, cfg.window, knorm=knorm,
+                                 sel_bound=sb)
+    torch.cuda.synchronize()
+    want = torch.gather(knorm.unsqueeze(2).expand(-1, -1, cfg.n_blocks, -1), 3, sel.long()).amax(dim=3)
+    assert torch.equal(sb, want)
+    assert torch.equal(out_a, out_b)
