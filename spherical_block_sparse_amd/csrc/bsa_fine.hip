@@ -38,6 +38,9 @@
 //     branch's blocks are bounded by c*|q|*max|k|; when those bounds are small
 //     enough for every query of a wave, the bounds serve as fixed
 //     references and the running maximum is skipped altogether.  The
+//     selected branch's max|k| per query block can come precomputed
+//     (sel_bound_kernel, launched by the caller between the selection and
+//     this kernel); without it the prologue gathers it.  The
 //     denominator is the same MFMA with an all-ones A operand (sum of the
 //     rounded weights, so each output is an exact convex combination of the
 //     weights actually applied).
@@ -810,8 +813,6 @@ hipError_t launch_generic(FineArgs a, long long slices, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One workgroup per tile of 32*WAVES queries of every slice: the tile size
-// fixes the tile count and the grid together.
 // For each query block, the largest key norm over its selected blocks (the
 // same clamped indices and the same maximum the fine kernel's prologue would
 // form from the selection table), one thread per row.
@@ -829,6 +830,8 @@ __global__ __launch_bounds__(256) void sel_bound_kernel(const int32_t* sel, cons
   selmax[r] = mx;
 }
 
+// One workgroup per tile of 32*WAVES queries of every slice: the tile size
+// fixes the tile count and the grid together.
 template <int D, int WAVES>
 hipError_t launch(FineArgs a, long long slices, hipStream_t stream) {
   a.tiles = a.n_tok / (32 * WAVES);
