@@ -181,7 +181,9 @@ mosaic_status mosaic_bsa_fine(const void* q, const void* k, const void* v, const
  * mosaic_bsa_pool.  mosaic_bsa_forward, mosaic_bsa_forward_train and
  * mosaic_bsa_layer_forward form it in their workspaces between the
  * selection and the fine kernel; with this call a caller of the stages does
- * the same for mosaic_bsa_fine.  Alignment: 4 bytes. */
+ * the same for mosaic_bsa_fine.  head_dim, nside, block and topn are
+ * validated as for mosaic_bsa_fine (head_dim enters nothing else).
+ * Alignment: 4 bytes. */
 mosaic_status mosaic_bsa_select_bound(const int32_t* sel_idx, const float* knorm, int batch, int heads,
                                       int head_dim, int nside, int block, int topn, float* sel_bound,
                                       void* stream);

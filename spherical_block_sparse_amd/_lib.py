@@ -253,10 +253,14 @@ def mosaic_bsa_fine(q, k, v, gates, o_cg, sel_idx, nside, block, topn, window, o
 
 
 def mosaic_bsa_select_bound(sel_idx, knorm, nside, block, topn, head_dim, sel_bound=None, stream=None):
-    """sel_bound [b,H,m] fp32: the largest knorm over each query block's topn selected blocks."""
-    b, h, m, t = sel_idx.shape
-    if t != topn:
-        raise ValueError(f"sel_idx has {t} entries per row, topn is {topn}")
+    """sel_bound [b,H,m] fp32: the largest knorm over each query block's topn selected blocks
+    (m = 12*nside^2 / block; sel_idx and knorm are checked against it)."""
+    if not isinstance(sel_idx, torch.Tensor) or sel_idx.dim() != 4:
+        raise ValueError("sel_idx must be [batch, heads, m, topn]")
+    if block < 1 or (12 * nside * nside) % block:
+        raise ValueError(f"block {block} does not divide N = 12*{nside}^2")
+    b, h = sel_idx.shape[:2]
+    m = 12 * nside * nside // block
     sel_bound = torch.empty((b, h, m), dtype=torch.float32, device=sel_idx.device) if sel_bound is None \
         else sel_bound
     _check(lib().mosaic_bsa_select_bound(

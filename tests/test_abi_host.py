@@ -179,6 +179,16 @@ def test_python_binding_rejects_bad_tensors_without_launch():
                                 out=torch.zeros(1), sel_idx=torch.zeros(1), workspace=torch.zeros(1, dtype=torch.uint8))
     with pytest.raises(ValueError):
         _lib.mosaic_bsa_forward(q[:, :, :700], q, q, q, 8, 16, 4, 32)
+    # the selection bound's tensors are checked against m = 12*nside^2/block (48 here), not
+    # taken from their own shapes: a call that names nside 16 for nside-8 selections never launches
+    sel = torch.zeros(1, 2, 48, 4, dtype=torch.int32)
+    kn = torch.zeros(1, 2, 48)
+    with pytest.raises(ValueError, match="shape"):
+        _lib.mosaic_bsa_select_bound(sel, kn, 16, 16, 4, 32)
+    with pytest.raises(ValueError, match="shape"):
+        _lib.mosaic_bsa_select_bound(sel, kn, 8, 16, 8, 32)
+    with pytest.raises(ValueError, match="device"):
+        _lib.mosaic_bsa_select_bound(sel, kn, 8, 16, 4, 32)
 
 
 def bwd(q=FAKE, k=FAKE, v=FAKE, gates=FAKE, sel=FAKE, dout=FAKE, batch=1, heads=2, d=64, nside=32, block=64,
