@@ -378,6 +378,21 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   const int c_all = c_sel + (whi - wlo + 63) / 64;
   const int blk0 = t0 / B;
   const int lb = 31 - __builtin_clz(B);   // block = 2^lb
+  // The score bounds' loads that need no selection table (the precomputed
+  // selected-branch bound and the window's block norms) are issued before the
+  // table is filled, so their latency overlaps its loads and barrier.
+  float ks_pre[2] = {0.f, 0.f}, kl_pre[2] = {0.f, 0.f};
+  if (a.knorm) {
+    const float* kn = a.knorm + (size_t)slice * m;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int ts = tw + 16 * s;   // the sub-tile's query range is uniform
+      if (a.selmax) ks_pre[s] = a.selmax[(size_t)slice * m + (ts >> lb)];   // a sub-tile lies in one block
+      const int ulo = max(0, ts - lo_off);
+      const int uhi = (int)min((long long)N, (long long)ts + 15 + hi_off);
+      for (int bl = ulo >> lb; bl <= (uhi - 1) >> lb; ++bl) kl_pre[s] = fmaxf(kl_pre[s], kn[bl]);
+    }
+  }
   {
     // the selection rows of this tile's query blocks, clamped so that a bad
     // index can never address outside the slice
@@ -414,17 +429,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       q2 += __shfl_xor(q2, 16);
       q2 += __shfl_xor(q2, 32);
       const float qn = sqrtf(q2);
-      const int ts = tw + 16 * s;   // the sub-tile's query range is uniform
-      float ks = 0.f, kl = 0.f;
-      if (a.selmax) {   // formed by the selection-bound kernel (a sub-tile lies in one block)
-        ks = a.selmax[(size_t)slice * m + (ts >> lb)];
-      } else {
+      const int ts = tw + 16 * s;
+      float ks = ks_pre[s];
+      const float kl = kl_pre[s];
+      if (!a.selmax) {   // gathered from the selection table
         for (int gi = (ts >> lb) - blk0; gi <= ((ts + 15) >> lb) - blk0; ++gi)
           for (int j = 0; j < n; ++j) ks = fmaxf(ks, kn[SelT[gi * n + j]]);
       }
-      const int ulo = max(0, ts - lo_off);
-      const int uhi = (int)min((long long)N, (long long)ts + 15 + hi_off);
-      for (int bl = ulo >> lb; bl <= (uhi - 1) >> lb; ++bl) kl = fmaxf(kl, kn[bl]);
       m_sel[s] = c * qn * ks;
       m_loc[s] = c * qn * kl;
       ok = ok && m_sel[s] <= kBoundMax && m_loc[s] <= kBoundMax;
