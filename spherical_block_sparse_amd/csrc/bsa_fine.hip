@@ -530,6 +530,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     if (bounded) br[s].m = m_sel[s] / c;
   }
   float4 pre[2][DT];   // g_CG*o_CG + g_FG*o_FG, formed when the selected branch ends
+  // g_L: the 64-query kernel keeps it from the gate row read when the
+  // selected branch ends, so its epilogue issues no loads ahead of its
+  // stores; the 128-query kernel reads it again in the epilogue.  Each is the
+  // faster of the two choices for that kernel, as measured.
+  constexpr bool kKeepGL = WAVES == 2;
+  float gl[2] = {0.f, 0.f};
 
   // SAVE: the branch's normalised output and log2-sum-exp m*c + log2(l) of
   // this lane's query, for a backward pass that then skips recomputing them
@@ -554,6 +560,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
       const int tq = tw + 16 * s + lr;
       const float* g = a.gates + ((size_t)slice * N + tq) * 3;
       const float g0 = g[0], g1 = g[1] / br[s].l[0];
+      if constexpr (kKeepGL) gl[s] = g[2];
       const float* ocg = a.o_cg + ((size_t)slice * m + tq / B) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -657,7 +664,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int s = 0; s < 2; ++s) {
     if constexpr (MODE == kSave) save_branch(s, 1);
     const int tq = tw + 16 * s + lr;
-    const float g2 = a.gates[((size_t)slice * N + tq) * 3 + 2] / br[s].l[0];
+    const float g2 = (kKeepGL ? gl[s] : a.gates[((size_t)slice * N + tq) * 3 + 2]) / br[s].l[0];
     float* dst = a.out + ((size_t)slice * N + tq) * D;
     uint16_t* dstb = nullptr;
     if constexpr (MODE == kMerged) {
